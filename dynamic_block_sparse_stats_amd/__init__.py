@@ -1,0 +1,247 @@
+"""Prism dynamic block-sparse video self-attention on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libprism.so`` (the C ABI in ``include/prism.h``): it checks
+tensor shapes and dtypes and passes device pointers and the current HIP stream; every step
+of the method runs in the library's HIP kernels.  PyTorch only provides device memory and
+streams.  There is no fallback: if the library is missing or was built for another target,
+calls raise.
+
+Entry points (same names as the C ABI):
+  workspace_bytes(cfg), plan_layout(cfg), plan(cfg, q, k, v, a2v, ws),
+  attn_fwd(cfg, ws, o, lse), attn_bwd(cfg, ws, dout, dq, dk, dv)
+and ``PrismAttention``, which owns a workspace and chains them.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libprism.so")
+
+F32, BF16 = 0, 1
+_DTYPES = {F32: torch.float32, BF16: torch.bfloat16}
+
+
+class PrismConfig(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int), ("H", ctypes.c_int), ("W", ctypes.c_int),
+                ("num_heads", ctypes.c_int), ("head_dim", ctypes.c_int),
+                ("dtype", ctypes.c_int), ("min_edge_log2", ctypes.c_int),
+                ("top_k", ctypes.c_int), ("top_p", ctypes.c_float),
+                ("tau128", ctypes.c_float), ("tau256", ctypes.c_float),
+                ("eps", ctypes.c_double), ("score_scale", ctypes.c_float),
+                ("softmax_scale", ctypes.c_float)]
+
+    @property
+    def N(self) -> int:
+        return self.T * self.H * self.W
+
+    @property
+    def torch_dtype(self):
+        return _DTYPES[self.dtype]
+
+
+_LAYOUT_FIELDS = ["zone_stats", "audio_stats", "zone_diag", "zone_shape", "zone_block",
+                  "block_start", "block_size", "unit_block", "perm", "inv_perm", "qbar",
+                  "kbar", "sel_count", "csr_col", "csc_count", "csc_row", "scores", "total"]
+
+
+class PrismLayout(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_size_t) for f in _LAYOUT_FIELDS] + [
+        ("N", ctypes.c_int), ("Z", ctypes.c_int), ("nb_max", ctypes.c_int)]
+
+
+class PrismError(RuntimeError):
+    pass
+
+
+_lib = None
+EXPORTS = ["prism_workspace_bytes", "prism_plan_layout", "prism_plan", "prism_attn_fwd",
+           "prism_attn_bwd", "prism_status_string", "prism_last_error"]
+
+
+def lib():
+    """The loaded libprism.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise PrismError(f"{LIB_PATH} is missing: build it with "
+                             "`python -m dynamic_block_sparse_stats_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, cfgp = ctypes.c_void_p, ctypes.POINTER(PrismConfig)
+        L.prism_workspace_bytes.argtypes = [cfgp]
+        L.prism_workspace_bytes.restype = ctypes.c_size_t
+        L.prism_plan_layout.argtypes = [cfgp, ctypes.POINTER(PrismLayout)]
+        L.prism_plan_layout.restype = ctypes.c_int
+        L.prism_plan.argtypes = [cfgp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.prism_plan.restype = ctypes.c_int
+        L.prism_attn_fwd.argtypes = [cfgp, vp, ctypes.c_size_t, vp, vp, vp]
+        L.prism_attn_fwd.restype = ctypes.c_int
+        L.prism_attn_bwd.argtypes = [cfgp, vp, ctypes.c_size_t, vp, vp, vp, vp, vp]
+        L.prism_attn_bwd.restype = ctypes.c_int
+        L.prism_status_string.argtypes = [ctypes.c_int]
+        L.prism_status_string.restype = ctypes.c_char_p
+        L.prism_last_error.argtypes = []
+        L.prism_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def make_config(T, H, W, num_heads, head_dim, dtype="bf16", min_edge_log2=1, top_k=8,
+                top_p=0.9, tau128=0.5, tau256=0.25, eps=1e-6, score_scale=0.0,
+                softmax_scale=0.0) -> PrismConfig:
+    dt = {"f32": F32, "bf16": BF16, F32: F32, BF16: BF16, torch.float32: F32,
+          torch.bfloat16: BF16}[dtype]
+    return PrismConfig(T, H, W, num_heads, head_dim, dt, min_edge_log2, int(top_k),
+                       float(top_p), float(tau128), float(tau256), float(eps),
+                       float(score_scale), float(softmax_scale))
+
+
+def config_for(wl, **over) -> PrismConfig:
+    """Configuration of a synth.Workload."""
+    kw = dict(dtype=wl.dtype, min_edge_log2=wl.min_edge_log2, top_k=wl.top_k,
+              top_p=wl.top_p)
+    kw.update(over)
+    return make_config(wl.T, wl.H, wl.W, wl.heads, wl.head_dim, **kw)
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        L = lib()
+        raise PrismError(f"{what}: {L.prism_status_string(st).decode()} "
+                         f"({L.prism_last_error().decode()})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _tok(cfg, t, name, dtype=None):
+    dtype = dtype or cfg.torch_dtype
+    shape = (cfg.N, cfg.num_heads, cfg.head_dim)
+    if t.dtype != dtype or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous {dtype} {shape} on the GPU, got "
+                         f"{t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def workspace_bytes(cfg: PrismConfig) -> int:
+    n = lib().prism_workspace_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise PrismError("configuration rejected: " + lib().prism_last_error().decode())
+    return n
+
+
+def plan_layout(cfg: PrismConfig) -> PrismLayout:
+    out = PrismLayout()
+    _check(lib().prism_plan_layout(ctypes.byref(cfg), ctypes.byref(out)), "prism_plan_layout")
+    return out
+
+
+def plan(cfg, q, k, v, a2v, ws, stream=None):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _tok(cfg, t, name)
+    if a2v is not None and (a2v.dtype != torch.float32 or a2v.numel() != cfg.N
+                            or not a2v.is_contiguous() or not a2v.is_cuda):
+        raise ValueError("a2v: expected a contiguous float32 [N] GPU tensor")
+    _check(lib().prism_plan(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(a2v), _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(stream)), "prism_plan")
+
+
+def attn_fwd(cfg, ws, o, lse, stream=None):
+    _tok(cfg, o, "o")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (cfg.num_heads, cfg.N):
+        raise ValueError("lse: expected float32 [heads, N]")
+    _check(lib().prism_attn_fwd(ctypes.byref(cfg), _ptr(ws), ws.numel() * ws.element_size(),
+                                _ptr(o), _ptr(lse), _stream(stream)), "prism_attn_fwd")
+
+
+def attn_bwd(cfg, ws, dout, dq, dk, dv, stream=None):
+    """Needs prism_attn_fwd to have run on ws since the last plan (it keeps O and lse)."""
+    for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _tok(cfg, t, name)
+    _check(lib().prism_attn_bwd(ctypes.byref(cfg), _ptr(ws), ws.numel() * ws.element_size(),
+                                _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)),
+           "prism_attn_bwd")
+
+
+def plan_views(cfg, ws) -> dict:
+    """Typed views of the plan's arrays inside the workspace (see prism_layout)."""
+    L = plan_layout(cfg)
+    Hh, Z, nb, N, D = cfg.num_heads, L.Z, L.nb_max, L.N, cfg.head_dim
+
+    def view(off, dtype, shape):
+        n = int(math.prod(shape))
+        esz = torch.empty((), dtype=dtype).element_size()
+        return ws[off: off + n * esz].view(dtype).view(*shape)
+
+    return {
+        "zone_stats": view(L.zone_stats, torch.float64, (Hh, Z, 4)),
+        "audio_stats": view(L.audio_stats, torch.float64, (Z, 4)),
+        "zone_diag": view(L.zone_diag, torch.float64, (Hh, Z, 4)),
+        "zone_shape": view(L.zone_shape, torch.int32, (Hh, Z)),
+        "zone_block": view(L.zone_block, torch.int32, (Hh, Z + 1)),
+        "block_start": view(L.block_start, torch.int32, (Hh, nb)),
+        "block_size": view(L.block_size, torch.int32, (Hh, nb)),
+        "unit_block": view(L.unit_block, torch.int32, (Hh, N // 64)),
+        "perm": view(L.perm, torch.int32, (Hh, N)),
+        "inv_perm": view(L.inv_perm, torch.int32, (Hh, N)),
+        "qbar": view(L.qbar, torch.float32, (Hh, nb, D)),
+        "kbar": view(L.kbar, torch.float32, (Hh, nb, D)),
+        "sel_count": view(L.sel_count, torch.int32, (Hh, nb)),
+        "csr_col": view(L.csr_col, torch.int32, (Hh, nb, nb)),
+        "csc_count": view(L.csc_count, torch.int32, (Hh, nb)),
+        "csc_row": view(L.csc_row, torch.int32, (Hh, nb, nb)),
+        "scores": view(L.scores, torch.float32, (nb, nb)),
+    }
+
+
+@dataclass
+class PrismAttention:
+    """Owns a workspace for one configuration and chains plan -> forward -> backward."""
+    cfg: PrismConfig
+    device: str = "cuda"
+
+    def __post_init__(self):
+        self.ws_bytes = workspace_bytes(self.cfg)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.o = None
+        self.lse = None
+
+    def plan(self, q, k, v, a2v=None, stream=None):
+        plan(self.cfg, q, k, v, a2v, self.ws, stream)
+
+    def forward(self, o=None, lse=None, stream=None):
+        cfg = self.cfg
+        if o is None:
+            o = torch.empty(cfg.N, cfg.num_heads, cfg.head_dim, dtype=cfg.torch_dtype,
+                            device=self.device)
+        if lse is None:
+            lse = torch.empty(cfg.num_heads, cfg.N, dtype=torch.float32, device=self.device)
+        attn_fwd(cfg, self.ws, o, lse, stream)
+        self.o, self.lse = o, lse
+        return o, lse
+
+    def backward(self, dout, dq=None, dk=None, dv=None, stream=None):
+        cfg = self.cfg
+        mk = lambda: torch.empty(cfg.N, cfg.num_heads, cfg.head_dim, dtype=cfg.torch_dtype,
+                                 device=self.device)
+        dq = mk() if dq is None else dq
+        dk = mk() if dk is None else dk
+        dv = mk() if dv is None else dv
+        if self.o is None:
+            raise PrismError("backward needs a forward on this workspace first")
+        attn_bwd(cfg, self.ws, dout, dq, dk, dv, stream)
+        return dq, dk, dv
+
+    def views(self):
+        return plan_views(self.cfg, self.ws)

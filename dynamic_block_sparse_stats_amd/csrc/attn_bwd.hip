@@ -1,0 +1,547 @@
+// attn_bwd.hip -- gradients of the block-sparse attention with the plan held constant
+// (arXiv 2610.05416; nanless digest, training section: shape assignment and block
+// selection are constants that pass no gradient; gradients flow only through the sparse
+// attention over the selected blocks).
+//
+// With P_xy = exp(scale q_x.k_y - lse_x) over the key tokens y of the blocks selected for
+// x's block, delta_x = do_x.o_x and dS_xy = P_xy (do_x.v_y - delta_x):
+//   dv_y = sum_x P_xy do_x,  dk_y = scale sum_x dS_xy q_x,  dq_x = scale sum_y dS_xy k_y.
+// Three passes, none with atomics (results are bit-reproducible):
+//   prep  -- gathers dO into the permuted layout (row-major and per-unit transposed) and
+//            forms delta from the float32 output the forward kept;
+//   dK/dV -- one workgroup per key tile (32 keys per wave, K and V rows held in registers),
+//            streaming the 64-token query units of every query block that selected the
+//            key block (the transposed selection lists);
+//   dQ    -- one workgroup per query tile (32 queries per wave, Q and dO in registers),
+//            streaming the selected key units as in the forward pass.
+// Both MFMA passes recompute P from the stored lse; outputs go straight to the tokens'
+// original positions.
+#include "prism_internal.h"
+
+namespace prism {
+
+constexpr int kDB = 128;
+
+__device__ __forceinline__ int rm_off(int r, int c) {  // [64][128] bf16 tile, 16 chunks/row
+  return r * 256 + ((c ^ (r & 15)) << 4);
+}
+__device__ __forceinline__ int tr_off(int d, int c) {  // [128][64] bf16 tile, 8 chunks/row
+  return d * 128 + ((c ^ ((d >> 1) & 7)) << 4);
+}
+__device__ __forceinline__ int swap23b(int e) {
+  return (e & ~12) | ((e >> 1) & 4) | ((e << 1) & 8);
+}
+
+// ============================================================================ prep
+template <typename T, int D, bool TRANSPOSE>
+__global__ void __launch_bounds__(256)
+    bwd_prep_kernel(int N, int heads, const int *__restrict__ perm, const T *__restrict__ dout,
+                    const float *__restrict__ o32p, T *__restrict__ dop, T *__restrict__ dopt,
+                    float *__restrict__ delta) {
+  constexpr int VPC = 16 / (int)sizeof(T);
+  constexpr int CH = D / VPC;
+  constexpr int RG = 256 / CH;
+  constexpr int RPT = kUnit / RG;
+  const int u = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int c = tid % CH, rg = tid / CH;
+  __shared__ __align__(16) uint16_t tile[TRANSPOSE ? kUnit * D : 8];
+  const size_t tstride = (size_t)heads * D;
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) {
+    const int row = rg + RG * rr;
+    const size_t p = (size_t)u * kUnit + row;
+    const int token = perm[(size_t)h * N + p];
+    u32x4 a = *reinterpret_cast<const u32x4 *>(dout + token * tstride + (size_t)h * D + c * VPC);
+    *reinterpret_cast<u32x4 *>(dop + ((size_t)h * N + p) * D + c * VPC) = a;
+    const float *orow = o32p + ((size_t)h * N + p) * D + c * VPC;
+    float dot = 0.f;
+    if constexpr (sizeof(T) == 2) {
+      const f32x4 o0 = *reinterpret_cast<const f32x4 *>(orow);
+      const f32x4 o1 = *reinterpret_cast<const f32x4 *>(orow + 4);
+      const float ov[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dot += __uint_as_float(a[e] << 16) * ov[2 * e];
+        dot += __uint_as_float(a[e] & 0xffff0000u) * ov[2 * e + 1];
+      }
+    } else {
+      const f32x4 o0 = *reinterpret_cast<const f32x4 *>(orow);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot += __uint_as_float(a[e]) * o0[e];
+    }
+#pragma unroll
+    for (int off = 1; off < CH; off <<= 1) dot += __shfl_xor(dot, off, 64);
+    if (c == 0) delta[(size_t)h * N + p] = dot;
+    if constexpr (TRANSPOSE) *reinterpret_cast<u32x4 *>(&tile[row * D + c * VPC]) = a;
+  }
+  if constexpr (TRANSPOSE) {
+    __syncthreads();
+    const int dd = tid >> 1, half = tid & 1;
+    const size_t ubase = ((size_t)h * (N / kUnit) + u) * (size_t)(D * kUnit);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        int pos0 = 32 * half + 8 * cc + e;
+        int key0 = (pos0 & ~15) | swap23b(pos0 & 15);
+        int key1 = ((pos0 + 1) & ~15) | swap23b((pos0 + 1) & 15);
+        pk[e >> 1] = (uint32_t)tile[key0 * D + dd] | ((uint32_t)tile[key1 * D + dd] << 16);
+      }
+      *reinterpret_cast<u32x4 *>(dopt + ubase + (size_t)dd * kUnit + 32 * half + 8 * cc) =
+          u32x4{pk[0], pk[1], pk[2], pk[3]};
+    }
+  }
+}
+
+// ============================================================================ dK / dV (bf16)
+template <int NW>
+__global__ void __launch_bounds__(NW * 64)
+    attn_dkdv_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
+                          const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
+                          const uint16_t *__restrict__ qpt, const uint16_t *__restrict__ kp,
+                          const uint16_t *__restrict__ vp, const uint16_t *__restrict__ dop,
+                          const uint16_t *__restrict__ dopt, const float *__restrict__ lsep,
+                          const float *__restrict__ delta, const int *__restrict__ unit_blk,
+                          const int *__restrict__ blk_start, const int *__restrict__ blk_size,
+                          const int *__restrict__ csc_count, const int *__restrict__ csc_row,
+                          const int *__restrict__ perm, float scale, float scale_log2e,
+                          uint16_t *__restrict__ dk, uint16_t *__restrict__ dv) {
+  constexpr int NT = NW * 64;
+  constexpr int CPT = 1024 / NT;
+  __shared__ __align__(16) uint8_t lds[4][16384];  // Q, dO (row-major), Q^T, dO^T
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int ntiles = *tile_count;
+  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int2 tl = tiles[t];
+    const int h = tl.x, u0 = tl.y;
+    const int jblk = unit_blk[(size_t)h * U + u0];
+    const int nq = csc_count[(size_t)h * nb_max + jblk];
+    const int *qlist = csc_row + ((size_t)h * nb_max + jblk) * nb_max;
+    const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
+    // this wave's 32 keys: K^T and V^T as B operands (lane = key, 8 dims per k-step)
+    const int key0 = u0 * kUnit + wave * 32;
+    bf16x8 kreg[8], vreg[8];
+    {
+      const uint16_t *kr = kp + ((size_t)h * N + key0 + l32) * kDB + 8 * hh;
+      const uint16_t *vr = vp + ((size_t)h * N + key0 + l32) * kDB + 8 * hh;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        kreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kr + 16 * kk));
+        vreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(vr + 16 * kk));
+      }
+    }
+    f32x16 dkt[4], dvt[4];  // [d][key] accumulators, 4 tiles of 32 dims
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) dkt[dt] = dvt[dt] = f32x16{};
+
+    for (int qi = 0; qi < nq; ++qi) {
+      const int iblk = qlist[qi];
+      const int us = bs[iblk] / kUnit, nu = bz[iblk] / kUnit;
+      for (int u = us; u < us + nu; ++u) {
+        __syncthreads();
+        const size_t ub = ((size_t)h * N + (size_t)u * kUnit) * kDB * 2;  // bytes
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+          const int q = tid + NT * e;
+          const uint8_t *g0 = reinterpret_cast<const uint8_t *>(qp) + ub + 16 * q;
+          const uint8_t *g1 = reinterpret_cast<const uint8_t *>(dop) + ub + 16 * q;
+          const uint8_t *g2 = reinterpret_cast<const uint8_t *>(qpt) + ub + 16 * q;
+          const uint8_t *g3 = reinterpret_cast<const uint8_t *>(dopt) + ub + 16 * q;
+          *reinterpret_cast<u32x4 *>(&lds[0][rm_off(q >> 4, q & 15)]) =
+              *reinterpret_cast<const u32x4 *>(g0);
+          *reinterpret_cast<u32x4 *>(&lds[1][rm_off(q >> 4, q & 15)]) =
+              *reinterpret_cast<const u32x4 *>(g1);
+          *reinterpret_cast<u32x4 *>(&lds[2][tr_off(q >> 3, q & 7)]) =
+              *reinterpret_cast<const u32x4 *>(g2);
+          *reinterpret_cast<u32x4 *>(&lds[3][tr_off(q >> 3, q & 7)]) =
+              *reinterpret_cast<const u32x4 *>(g3);
+        }
+        __syncthreads();
+        const float *lrow = lsep + (size_t)h * N + (size_t)u * kUnit;
+        const float *drow = delta + (size_t)h * N + (size_t)u * kUnit;
+        bf16x8 pb[4], db[4];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {  // queries 32a .. 32a + 31 of the unit
+          f32x16 s = f32x16{}, dp = f32x16{};
+          const int r = 32 * a + l32;
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            bf16x8 qa = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4 *>(&lds[0][rm_off(r, 2 * kk + hh)]));
+            bf16x8 da = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4 *>(&lds[1][rm_off(r, 2 * kk + hh)]));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[kk], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[kk], dp, 0, 0, 0);
+          }
+          // C layout: lane = key l32, register v = query 32a + (v/4)*8 + 4hh + v%4
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const int q0 = 32 * a + 8 * v4 + 4 * hh;
+            const float4 l4 = *reinterpret_cast<const float4 *>(lrow + q0);
+            const float4 d4 = *reinterpret_cast<const float4 *>(drow + q0);
+            const float lq[4] = {l4.x, l4.y, l4.z, l4.w}, dq4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int v = 4 * v4 + e;
+              const float p = __builtin_amdgcn_exp2f(s[v] * scale_log2e - lq[e] * 1.4426950408889634f);
+              const float ds = p * (dp[v] - dq4[e]);
+              const int g = 2 * a + (v >> 3), slot = v & 7;
+              pb[g][slot] = (__bf16)p;
+              db[g][slot] = (__bf16)ds;
+            }
+          }
+        }
+        // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int d = 32 * dt + l32;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            bf16x8 doa = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4 *>(&lds[3][tr_off(d, 2 * g + hh)]));
+            bf16x8 qta = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4 *>(&lds[2][tr_off(d, 2 * g + hh)]));
+            dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doa, pb[g], dvt[dt], 0, 0, 0);
+            dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, db[g], dkt[dt], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // epilogue: C layout lane = key l32, register v -> d = 32dt + (v/4)*8 + 4hh + v%4
+    const int token = perm[(size_t)h * N + key0 + l32];
+    uint16_t *krow = dk + ((size_t)token * heads + h) * kDB;
+    uint16_t *vrow = dv + ((size_t)token * heads + h) * kDB;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int d0 = 32 * dt + 8 * v4 + 4 * hh;
+        const f32x16 &K = dkt[dt], &V = dvt[dt];
+        uint32_t k0 = (uint32_t)f32_to_bf16(K[4 * v4] * scale) |
+                      ((uint32_t)f32_to_bf16(K[4 * v4 + 1] * scale) << 16);
+        uint32_t k1 = (uint32_t)f32_to_bf16(K[4 * v4 + 2] * scale) |
+                      ((uint32_t)f32_to_bf16(K[4 * v4 + 3] * scale) << 16);
+        uint32_t w0 = (uint32_t)f32_to_bf16(V[4 * v4]) |
+                      ((uint32_t)f32_to_bf16(V[4 * v4 + 1]) << 16);
+        uint32_t w1 = (uint32_t)f32_to_bf16(V[4 * v4 + 2]) |
+                      ((uint32_t)f32_to_bf16(V[4 * v4 + 3]) << 16);
+        *reinterpret_cast<u32x2 *>(krow + d0) = u32x2{k0, k1};
+        *reinterpret_cast<u32x2 *>(vrow + d0) = u32x2{w0, w1};
+      }
+  }
+}
+
+// ============================================================================ dQ (bf16)
+template <int NW>
+__global__ void __launch_bounds__(NW * 64)
+    attn_dq_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
+                        const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
+                        const uint16_t *__restrict__ kp, const uint16_t *__restrict__ kpt,
+                        const uint16_t *__restrict__ vp, const uint16_t *__restrict__ dop,
+                        const float *__restrict__ lsep, const float *__restrict__ delta,
+                        const int *__restrict__ unit_blk, const int *__restrict__ blk_start,
+                        const int *__restrict__ blk_size, const int *__restrict__ sel_count,
+                        const int *__restrict__ csr_col, const int *__restrict__ perm,
+                        float scale, float scale_log2e, uint16_t *__restrict__ dq) {
+  constexpr int NT = NW * 64;
+  constexpr int CPT = 1024 / NT;
+  __shared__ __align__(16) uint8_t lds[3][16384];  // K, V (row-major), K^T
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int ntiles = *tile_count;
+  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int2 tl = tiles[t];
+    const int h = tl.x, u0 = tl.y;
+    const int blk = unit_blk[(size_t)h * U + u0];
+    const int ncols = sel_count[(size_t)h * nb_max + blk];
+    const int *cols = csr_col + ((size_t)h * nb_max + blk) * nb_max;
+    const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
+    const int row0 = u0 * kUnit + wave * 32;
+    bf16x8 qreg[8], doreg[8];
+    {
+      const uint16_t *qr = qp + ((size_t)h * N + row0 + l32) * kDB + 8 * hh;
+      const uint16_t *dr = dop + ((size_t)h * N + row0 + l32) * kDB + 8 * hh;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        qreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qr + 16 * kk));
+        doreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(dr + 16 * kk));
+      }
+    }
+    const float lse2 = lsep[(size_t)h * N + row0 + l32] * 1.4426950408889634f;
+    const float dlt = delta[(size_t)h * N + row0 + l32];
+    f32x16 acc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+    for (int c = 0; c < ncols; ++c) {
+      const int j = cols[c];
+      const int us = bs[j] / kUnit, nu = bz[j] / kUnit;
+      for (int u = us; u < us + nu; ++u) {
+        __syncthreads();
+        const size_t ub = ((size_t)h * N + (size_t)u * kUnit) * kDB * 2;
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+          const int q = tid + NT * e;
+          *reinterpret_cast<u32x4 *>(&lds[0][rm_off(q >> 4, q & 15)]) =
+              *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint8_t *>(kp) + ub + 16 * q);
+          *reinterpret_cast<u32x4 *>(&lds[1][rm_off(q >> 4, q & 15)]) =
+              *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint8_t *>(vp) + ub + 16 * q);
+          *reinterpret_cast<u32x4 *>(&lds[2][tr_off(q >> 3, q & 7)]) =
+              *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint8_t *>(kpt) + ub + 16 * q);
+        }
+        __syncthreads();
+        bf16x8 db[4];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {  // keys 32a .. 32a + 31
+          f32x16 s = f32x16{}, dp = f32x16{};
+          const int r = 32 * a + l32;
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            bf16x8 ka = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4 *>(&lds[0][rm_off(r, 2 * kk + hh)]));
+            bf16x8 va = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4 *>(&lds[1][rm_off(r, 2 * kk + hh)]));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[kk], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, doreg[kk], dp, 0, 0, 0);
+          }
+          // lane = query, register v = key 32a + (v/4)*8 + 4hh + v%4
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float p = __builtin_amdgcn_exp2f(s[v] * scale_log2e - lse2);
+            db[2 * a + (v >> 3)][v & 7] = (__bf16)(p * (dp[v] - dlt));
+          }
+        }
+        // dQ^T[d][q] += K^T[d][keys] dS^T[keys][q]
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int d = 32 * dt + l32;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            bf16x8 kt = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4 *>(&lds[2][tr_off(d, 2 * g + hh)]));
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, db[g], acc[dt], 0, 0, 0);
+          }
+        }
+      }
+    }
+    const int token = perm[(size_t)h * N + row0 + l32];
+    uint16_t *qrow = dq + ((size_t)token * heads + h) * kDB;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int d0 = 32 * dt + 8 * v4 + 4 * hh;
+        uint32_t lo = (uint32_t)f32_to_bf16(acc[dt][4 * v4] * scale) |
+                      ((uint32_t)f32_to_bf16(acc[dt][4 * v4 + 1] * scale) << 16);
+        uint32_t hi = (uint32_t)f32_to_bf16(acc[dt][4 * v4 + 2] * scale) |
+                      ((uint32_t)f32_to_bf16(acc[dt][4 * v4 + 3] * scale) << 16);
+        *reinterpret_cast<u32x2 *>(qrow + d0) = u32x2{lo, hi};
+      }
+  }
+}
+
+// ============================================================================ float32
+// Small grids in float32 (products and sums in float64, as in the forward).
+// dQ: one workgroup per 64-row query unit, 4 threads per row.
+template <int D>
+__global__ void __launch_bounds__(256)
+    attn_dq_f32_kernel(int N, int U, int nb_max, int heads, const float *__restrict__ qp,
+                       const float *__restrict__ kp, const float *__restrict__ vp,
+                       const float *__restrict__ dop, const float *__restrict__ lsep,
+                       const float *__restrict__ delta, const int *__restrict__ unit_blk,
+                       const int *__restrict__ blk_start, const int *__restrict__ blk_size,
+                       const int *__restrict__ sel_count, const int *__restrict__ csr_col,
+                       const int *__restrict__ perm, float scale, float *__restrict__ dq) {
+  constexpr int DP = D / 4;
+  __shared__ float ks[kUnit][D], vs[kUnit][D];
+  const int u0 = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int r = tid >> 2, part = tid & 3;
+  const int blk = unit_blk[(size_t)h * U + u0];
+  const int ncols = sel_count[(size_t)h * nb_max + blk];
+  const int *cols = csr_col + ((size_t)h * nb_max + blk) * nb_max;
+  const int prow = u0 * kUnit + r;
+  float qv[DP], dov[DP];
+  double acc[DP];
+#pragma unroll
+  for (int e = 0; e < DP; ++e) {
+    qv[e] = qp[((size_t)h * N + prow) * D + part * DP + e];
+    dov[e] = dop[((size_t)h * N + prow) * D + part * DP + e];
+    acc[e] = 0.0;
+  }
+  const double l = lsep[(size_t)h * N + prow], dl = delta[(size_t)h * N + prow];
+  for (int c = 0; c < ncols; ++c) {
+    const int j = cols[c];
+    const int us = blk_start[(size_t)h * nb_max + j] / kUnit;
+    const int nu = blk_size[(size_t)h * nb_max + j] / kUnit;
+    for (int u = us; u < us + nu; ++u) {
+      __syncthreads();
+      for (int i = tid; i < kUnit * D; i += 256) {
+        ks[i / D][i % D] = kp[((size_t)h * N + (size_t)u * kUnit) * D + i];
+        vs[i / D][i % D] = vp[((size_t)h * N + (size_t)u * kUnit) * D + i];
+      }
+      __syncthreads();
+      for (int y = 0; y < kUnit; ++y) {
+        double a = 0.0, b = 0.0;
+#pragma unroll
+        for (int e = 0; e < DP; ++e) {
+          a += (double)qv[e] * (double)ks[y][part * DP + e];
+          b += (double)dov[e] * (double)vs[y][part * DP + e];
+        }
+        a += __shfl_xor(a, 1, 64);
+        a += __shfl_xor(a, 2, 64);
+        b += __shfl_xor(b, 1, 64);
+        b += __shfl_xor(b, 2, 64);
+        const double p = exp(a * (double)scale - l);
+        const double ds = p * (b - dl);
+#pragma unroll
+        for (int e = 0; e < DP; ++e) acc[e] += ds * (double)ks[y][part * DP + e];
+      }
+    }
+  }
+  const int token = perm[(size_t)h * N + prow];
+#pragma unroll
+  for (int e = 0; e < DP; ++e)
+    dq[((size_t)token * heads + h) * D + part * DP + e] = (float)(acc[e] * scale);
+}
+
+// dK/dV: one workgroup per 64-key unit, 4 threads per key row, over the transposed lists.
+template <int D>
+__global__ void __launch_bounds__(256)
+    attn_dkdv_f32_kernel(int N, int U, int nb_max, int heads, const float *__restrict__ qp,
+                         const float *__restrict__ kp, const float *__restrict__ vp,
+                         const float *__restrict__ dop, const float *__restrict__ lsep,
+                         const float *__restrict__ delta, const int *__restrict__ unit_blk,
+                         const int *__restrict__ blk_start, const int *__restrict__ blk_size,
+                         const int *__restrict__ csc_count, const int *__restrict__ csc_row,
+                         const int *__restrict__ perm, float scale, float *__restrict__ dk,
+                         float *__restrict__ dv) {
+  constexpr int DP = D / 4;
+  __shared__ float qs[kUnit][D], ds_[kUnit][D];
+  const int u0 = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int r = tid >> 2, part = tid & 3;
+  const int jblk = unit_blk[(size_t)h * U + u0];
+  const int nq = csc_count[(size_t)h * nb_max + jblk];
+  const int *qlist = csc_row + ((size_t)h * nb_max + jblk) * nb_max;
+  const int krow = u0 * kUnit + r;
+  float kv[DP], vv[DP];
+  double gk[DP], gv[DP];
+#pragma unroll
+  for (int e = 0; e < DP; ++e) {
+    kv[e] = kp[((size_t)h * N + krow) * D + part * DP + e];
+    vv[e] = vp[((size_t)h * N + krow) * D + part * DP + e];
+    gk[e] = gv[e] = 0.0;
+  }
+  for (int c = 0; c < nq; ++c) {
+    const int i = qlist[c];
+    const int us = blk_start[(size_t)h * nb_max + i] / kUnit;
+    const int nu = blk_size[(size_t)h * nb_max + i] / kUnit;
+    for (int u = us; u < us + nu; ++u) {
+      __syncthreads();
+      for (int x = tid; x < kUnit * D; x += 256) {
+        qs[x / D][x % D] = qp[((size_t)h * N + (size_t)u * kUnit) * D + x];
+        ds_[x / D][x % D] = dop[((size_t)h * N + (size_t)u * kUnit) * D + x];
+      }
+      __syncthreads();
+      for (int x = 0; x < kUnit; ++x) {
+        const size_t px = (size_t)h * N + (size_t)u * kUnit + x;
+        double a = 0.0, b = 0.0;
+#pragma unroll
+        for (int e = 0; e < DP; ++e) {
+          a += (double)kv[e] * (double)qs[x][part * DP + e];
+          b += (double)vv[e] * (double)ds_[x][part * DP + e];
+        }
+        a += __shfl_xor(a, 1, 64);
+        a += __shfl_xor(a, 2, 64);
+        b += __shfl_xor(b, 1, 64);
+        b += __shfl_xor(b, 2, 64);
+        const double p = exp(a * (double)scale - (double)lsep[px]);
+        const double g = p * (b - (double)delta[px]);
+#pragma unroll
+        for (int e = 0; e < DP; ++e) {
+          gv[e] += p * (double)ds_[x][part * DP + e];
+          gk[e] += g * (double)qs[x][part * DP + e];
+        }
+      }
+    }
+  }
+  const int token = perm[(size_t)h * N + krow];
+#pragma unroll
+  for (int e = 0; e < DP; ++e) {
+    dk[((size_t)token * heads + h) * D + part * DP + e] = (float)(gk[e] * scale);
+    dv[((size_t)token * heads + h) * D + part * DP + e] = (float)gv[e];
+  }
+}
+
+// ============================================================================ launcher
+hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout &L,
+                           const void *dout, void *dq, void *dk, void *dv, hipStream_t s) {
+  const int *perm = (const int *)(ws + L.pub.perm);
+  const int *unit_blk = (const int *)(ws + L.pub.unit_block);
+  const int *bstart = (const int *)(ws + L.pub.block_start);
+  const int *bsize = (const int *)(ws + L.pub.block_size);
+  const int *cnt = (const int *)(ws + L.pub.sel_count);
+  const int *cols = (const int *)(ws + L.pub.csr_col);
+  const int *tcnt = (const int *)(ws + L.pub.csc_count);
+  const int *trows = (const int *)(ws + L.pub.csc_row);
+  float *delta = (float *)(ws + L.delta);
+  const float *lsep = (const float *)(ws + L.lsep), *o32p = (const float *)(ws + L.o32p);
+  dim3 ugrid(d.U, d.heads);
+  if (d.dtype == PRISM_BF16) {
+    typedef uint16_t T;
+    hipLaunchKernelGGL((bwd_prep_kernel<T, 128, true>), ugrid, dim3(256), 0, s, d.N, d.heads,
+                       perm, (const T *)dout, o32p, (T *)(ws + L.dop), (T *)(ws + L.dopt),
+                       delta);
+    const int *counters = (const int *)(ws + L.counters);
+    const float sl2e = scale * 1.4426950408889634f;
+    const int max128 = d.heads * d.U / 2, max64 = d.heads * d.U;
+    const int g128 = max128 < 4096 ? (max128 > 0 ? max128 : 1) : 4096;
+    const int g64 = max64 < 4096 ? (max64 > 0 ? max64 : 1) : 4096;
+    const T *qp = (const T *)(ws + L.qp), *kp = (const T *)(ws + L.kp),
+            *vp = (const T *)(ws + L.vp), *qpt = (const T *)(ws + L.qpt),
+            *kpt = (const T *)(ws + L.kpt), *dop = (const T *)(ws + L.dop),
+            *dopt = (const T *)(ws + L.dopt);
+    const int2 *t128 = (const int2 *)(ws + L.tiles128), *t64 = (const int2 *)(ws + L.tiles64);
+    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<4>), dim3(g128), dim3(256), 0, s, d.N, d.U,
+                       d.nb_max, d.heads, t128, counters, qp, qpt, kp, vp, dop, dopt, lsep,
+                       delta, unit_blk, bstart, bsize, tcnt, trows, perm, scale, sl2e, (T *)dk,
+                       (T *)dv);
+    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<2>), dim3(g64), dim3(128), 0, s, d.N, d.U,
+                       d.nb_max, d.heads, t64, counters + 1, qp, qpt, kp, vp, dop, dopt, lsep,
+                       delta, unit_blk, bstart, bsize, tcnt, trows, perm, scale, sl2e, (T *)dk,
+                       (T *)dv);
+    hipLaunchKernelGGL((attn_dq_bf16_kernel<4>), dim3(g128), dim3(256), 0, s, d.N, d.U,
+                       d.nb_max, d.heads, t128, counters, qp, kp, kpt, vp, dop, lsep, delta,
+                       unit_blk, bstart, bsize, cnt, cols, perm, scale, sl2e, (T *)dq);
+    hipLaunchKernelGGL((attn_dq_bf16_kernel<2>), dim3(g64), dim3(128), 0, s, d.N, d.U,
+                       d.nb_max, d.heads, t64, counters + 1, qp, kp, kpt, vp, dop, lsep, delta,
+                       unit_blk, bstart, bsize, cnt, cols, perm, scale, sl2e, (T *)dq);
+  } else {
+    typedef float T;
+    const T *qp = (const T *)(ws + L.qp), *kp = (const T *)(ws + L.kp),
+            *vp = (const T *)(ws + L.vp), *dop = (const T *)(ws + L.dop);
+    if (d.D == 64) {
+      hipLaunchKernelGGL((bwd_prep_kernel<T, 64, false>), ugrid, dim3(256), 0, s, d.N, d.heads,
+                         perm, (const T *)dout, o32p, (T *)(ws + L.dop), nullptr, delta);
+      hipLaunchKernelGGL((attn_dq_f32_kernel<64>), ugrid, dim3(256), 0, s, d.N, d.U, d.nb_max,
+                         d.heads, qp, kp, vp, dop, lsep, delta, unit_blk, bstart, bsize, cnt,
+                         cols, perm, scale, (T *)dq);
+      hipLaunchKernelGGL((attn_dkdv_f32_kernel<64>), ugrid, dim3(256), 0, s, d.N, d.U,
+                         d.nb_max, d.heads, qp, kp, vp, dop, lsep, delta, unit_blk, bstart,
+                         bsize, tcnt, trows, perm, scale, (T *)dk, (T *)dv);
+    } else {
+      hipLaunchKernelGGL((bwd_prep_kernel<T, 128, false>), ugrid, dim3(256), 0, s, d.N,
+                         d.heads, perm, (const T *)dout, o32p, (T *)(ws + L.dop), nullptr,
+                         delta);
+      hipLaunchKernelGGL((attn_dq_f32_kernel<128>), ugrid, dim3(256), 0, s, d.N, d.U, d.nb_max,
+                         d.heads, qp, kp, vp, dop, lsep, delta, unit_blk, bstart, bsize, cnt,
+                         cols, perm, scale, (T *)dq);
+      hipLaunchKernelGGL((attn_dkdv_f32_kernel<128>), ugrid, dim3(256), 0, s, d.N, d.U,
+                         d.nb_max, d.heads, qp, kp, vp, dop, lsep, delta, unit_blk, bstart,
+                         bsize, tcnt, trows, perm, scale, (T *)dk, (T *)dv);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace prism

@@ -1,0 +1,543 @@
+// plan_kernels.hip -- planning stages of Prism's dynamic block-sparse attention on gfx950:
+// zone statistics, the per-zone shape quantiser, the block-contiguous permutation with the
+// gather of Q/K/V and block mean pooling, and the attention tile lists.
+//
+// Sources: arXiv 2610.05416 as described by the nanless audio-paper-digest post (sections
+// on the pipeline and Fig. 2, on guidance with Eq. g_d, on density with Eq. rho_raw and
+// Eq. J, on selection, on training) and by the xyznot.com review ("Метод" items 1-3).
+#include "prism_internal.h"
+
+namespace prism {
+
+// ============================================================================ audio stats
+// Zone mean and directional variances of the A2V norm field (digest, guidance section:
+// the norm is averaged inside the zone and its variance shares along each axis give the
+// audio direction; review item 1).  One wave per zone; float64 throughout.
+__global__ void __launch_bounds__(64) audio_stats_kernel(int H, int W, int nzh, int nzw,
+                                                         const float *__restrict__ a,
+                                                         double *__restrict__ out) {
+  const int m = blockIdx.x;
+  const int zw = m % nzw, zh = (m / nzw) % nzh, zt = m / (nzw * nzh);
+  __shared__ double vals[kZoneTok];
+  __shared__ double prof[3][kZone];
+  const int lane = threadIdx.x, i = lane >> 3, j = lane & 7;
+  const float *row = a + ((size_t)(zt * kZone + i) * H + zh * kZone + j) * W + zw * kZone;
+#pragma unroll
+  for (int l = 0; l < kZone; ++l) vals[(i * kZone + j) * kZone + l] = (double)row[l];
+  __syncthreads();
+  if (lane < 24) {
+    const int ax = lane >> 3, q = lane & 7;
+    double s = 0;
+    for (int x = 0; x < kZone; ++x)
+      for (int y = 0; y < kZone; ++y) {
+        int ii = ax == 0 ? q : x, jj = ax == 1 ? q : (ax == 0 ? x : y), ll = ax == 2 ? q : y;
+        s += vals[(ii * kZone + jj) * kZone + ll];
+      }
+    prof[ax][q] = s / (kZone * kZone);
+  }
+  __syncthreads();
+  if (lane == 0) {
+#pragma clang fp contract(off)
+    double mu = 0;
+    for (int q = 0; q < kZone; ++q) mu += prof[0][q];
+    mu /= kZone;
+    double vv[3];
+    for (int ax = 0; ax < 3; ++ax) {
+      double acc = 0;
+      for (int q = 0; q < kZone; ++q) acc += (prof[ax][q] - mu) * (prof[ax][q] - mu);
+      vv[ax] = acc / kZone;
+    }
+    out[4 * m + 0] = mu;
+    out[4 * m + 1] = vv[0];
+    out[4 * m + 2] = vv[1];
+    out[4 * m + 3] = vv[2];
+  }
+}
+
+hipError_t launch_audio_stats(const Dims &d, const float *a2v, double *astat, hipStream_t s) {
+  hipLaunchKernelGGL(audio_stats_kernel, dim3(d.Z), dim3(64), 0, s, d.H, d.W, d.nzh, d.nzw,
+                     a2v, astat);
+  return hipGetLastError();
+}
+
+// ============================================================================ zone stats
+// Per (head, zone): directional variances sigma2_{v,d} of the axis-pooled V profiles about
+// the zone mean, averaged over channels (review item 1), and rho_raw = channel-mean
+// spatial variance about the per-frame mean plus the channel-mean squared frame-to-frame
+// difference of the frame profile over Z_T - 1 pairs (digest, density section, Eq.
+// rho_raw).  One wave per (zone, head): the wave reads the zone's 512 token rows of this
+// head (each a contiguous D-element row, so every load instruction covers one row), and
+// every lane accumulates raw float64 sums of its channels: frame sums, h-row sums, w-column
+// sums and the sum of squares, all shifted by the zone's first token to keep the variance
+// formulas well conditioned.
+template <typename T, int D>
+__global__ void __launch_bounds__(64) zone_stats_kernel(int H, int W, int heads, int nzh,
+                                                        int nzw, const T *__restrict__ v,
+                                                        double *__restrict__ out, int Z) {
+  constexpr int CPL = D / 64;  // channels per lane
+  const int m = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int zw = m % nzw, zh = (m / nzw) % nzh, zt = m / (nzw * nzh);
+  const int c0 = lane * CPL;
+  const size_t tstride = (size_t)heads * D;
+  const T *base = v + ((((size_t)zt * kZone) * H + zh * kZone) * W + zw * kZone) * tstride +
+                  (size_t)h * D + c0;
+  auto load = [&](int i, int j, int l, double *x) {
+    const T *p = base + ((size_t)(i * H + j) * W + l) * tstride;
+    if constexpr (sizeof(T) == 2 && CPL == 2) {
+      uint32_t w2 = *reinterpret_cast<const uint32_t *>(p);
+      x[0] = (double)__uint_as_float(w2 << 16);
+      x[1] = (double)__uint_as_float(w2 & 0xffff0000u);
+    } else if constexpr (sizeof(T) == 4 && CPL == 2) {
+      float2 f2 = *reinterpret_cast<const float2 *>(p);
+      x[0] = (double)f2.x;
+      x[1] = (double)f2.y;
+    } else if constexpr (sizeof(T) == 2) {
+      x[0] = (double)bf16_to_f32(*reinterpret_cast<const uint16_t *>(p));
+    } else {
+      x[0] = (double)*reinterpret_cast<const float *>(p);
+    }
+  };
+  double ref[CPL];
+  load(0, 0, 0, ref);
+  double ST[kZone][CPL], SH[kZone][CPL], SW[kZone][CPL], SQ[CPL];
+#pragma unroll
+  for (int a = 0; a < kZone; ++a)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) ST[a][c] = SH[a][c] = SW[a][c] = 0;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) SQ[c] = 0;
+#pragma unroll
+  for (int i = 0; i < kZone; ++i) {
+#pragma unroll
+    for (int j = 0; j < kZone; ++j) {
+      double x[kZone][CPL];
+#pragma unroll
+      for (int l = 0; l < kZone; ++l) load(i, j, l, x[l]);
+#pragma unroll
+      for (int l = 0; l < kZone; ++l)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          double y = x[l][c] - ref[c];
+          ST[i][c] += y;
+          SH[j][c] += y;
+          SW[l][c] += y;
+          SQ[c] += y * y;
+        }
+    }
+  }
+  // per-channel statistics from the shifted sums
+  double acc[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    double pt[kZone], ph[kZone], pw[kZone], mu = 0;
+#pragma unroll
+    for (int a = 0; a < kZone; ++a) {
+      pt[a] = ST[a][c] / (kZone * kZone);
+      ph[a] = SH[a][c] / (kZone * kZone);
+      pw[a] = SW[a][c] / (kZone * kZone);
+      mu += pt[a];
+    }
+    mu /= kZone;
+    double vt = 0, vh = 0, vw = 0, pt2 = 0, td = 0;
+#pragma unroll
+    for (int a = 0; a < kZone; ++a) {
+      vt += (pt[a] - mu) * (pt[a] - mu);
+      vh += (ph[a] - mu) * (ph[a] - mu);
+      vw += (pw[a] - mu) * (pw[a] - mu);
+      pt2 += pt[a] * pt[a];
+    }
+#pragma unroll
+    for (int a = 0; a + 1 < kZone; ++a) td += (pt[a + 1] - pt[a]) * (pt[a + 1] - pt[a]);
+    double spatial = SQ[c] / kZoneTok - pt2 / kZone;
+    if (spatial < 0) spatial = 0;  // rounding guard: the exact value is a sum of squares
+    acc[0] += vt / kZone;
+    acc[1] += vh / kZone;
+    acc[2] += vw / kZone;
+    acc[3] += spatial + td / (kZone - 1);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] += __shfl_xor(acc[q], off, 64);
+  if (lane == 0) {
+    double *o = out + ((size_t)h * Z + m) * 4;
+    o[0] = acc[0] / D;
+    o[1] = acc[1] / D;
+    o[2] = acc[2] / D;
+    o[3] = acc[3] / D;
+  }
+}
+
+hipError_t launch_zone_stats(const Dims &d, const void *v, double *zstat, hipStream_t s) {
+  dim3 grid(d.Z, d.heads);
+  if (d.dtype == PRISM_BF16) {
+    hipLaunchKernelGGL((zone_stats_kernel<uint16_t, 128>), grid, dim3(64), 0, s, d.H, d.W,
+                       d.heads, d.nzh, d.nzw, (const uint16_t *)v, zstat, d.Z);
+  } else if (d.D == 64) {
+    hipLaunchKernelGGL((zone_stats_kernel<float, 64>), grid, dim3(64), 0, s, d.H, d.W, d.heads,
+                       d.nzh, d.nzw, (const float *)v, zstat, d.Z);
+  } else {
+    hipLaunchKernelGGL((zone_stats_kernel<float, 128>), grid, dim3(64), 0, s, d.H, d.W, d.heads,
+                       d.nzh, d.nzw, (const float *)v, zstat, d.Z);
+  }
+  return hipGetLastError();
+}
+
+// ============================================================================ quantiser
+// Per head: rho = rho_raw / max rho_raw and a_bar = zone mean / max zone mean (digest,
+// density and guidance sections: normalised by the global maximum), the variation
+// indicator g_d = r_{v,d} + a_bar * v_hat_{a,d} + eps (digest Eq. g_d; review item 1),
+// the volume tier (rho >= tau128 -> 64, >= tau256 -> 128, else 256; digest density
+// section; review item 2), the continuous optimum
+//   l*_d = -1/2 log2 g_d + 1/3 (S + 1/2 sum_d' log2 g_d'),  S = log2 B,
+// of J = sum_d g_d (b_d^2 - 1) under prod b_d = B (digest Eq. J; review item 2), and the
+// candidate of the pool nearest to l* in log2 space; candidates within 1e-9 of the best
+// distance are tied and the first in lexicographic (b_T, b_H, b_W) order wins.  The
+// arithmetic is written without fused multiply-adds so that each decision is taken on the
+// same float64 values a plain evaluation of these formulas gives.  Then the per-zone block
+// counts are scanned into the block table.
+__device__ void shape_of_zone(const double *vs, const double *as, double rho_max, double a_max,
+                              double tau128, double tau256, double eps, int mel, int *code_out,
+                              int *S_out, double *diag) {
+#pragma clang fp contract(off)
+  double rho = rho_max > 0 ? vs[3] / rho_max : 0.0;
+  double vsum = vs[0] + vs[1] + vs[2];
+  double r[3], va[3] = {0, 0, 0}, abar = 0;
+  for (int dd = 0; dd < 3; ++dd) r[dd] = vsum > 0 ? vs[dd] / vsum : 0.0;
+  if (as) {
+    abar = a_max > 0 ? as[0] / a_max : 0.0;
+    double asum = as[1] + as[2] + as[3];
+    for (int dd = 0; dd < 3; ++dd) va[dd] = asum > 0 ? as[1 + dd] / asum : 0.0;
+  }
+  double g[3], lg[3], ls[3];
+  for (int dd = 0; dd < 3; ++dd) {
+    double t = abar * va[dd];
+    g[dd] = r[dd] + t;
+    g[dd] = g[dd] + eps;
+  }
+  int S = rho >= tau128 ? 6 : (rho >= tau256 ? 7 : 8);
+  for (int dd = 0; dd < 3; ++dd) lg[dd] = log2(g[dd]);
+  double hs = (double)S;
+  hs = hs + 0.5 * lg[0];
+  hs = hs + 0.5 * lg[1];
+  hs = hs + 0.5 * lg[2];
+  hs = hs / 3.0;
+  for (int dd = 0; dd < 3; ++dd) ls[dd] = -0.5 * lg[dd] + hs;
+  double dist[19];
+  int cand[19];
+  int nc = 0;
+  double best = INFINITY;
+  for (int a = mel; a <= 3; ++a)
+    for (int b = mel; b <= 3; ++b)
+      for (int c = mel; c <= 3; ++c)
+        if (a + b + c == S) {
+          double e0 = ls[0] - a, e1 = ls[1] - b, e2 = ls[2] - c;
+          double dsum = e0 * e0;
+          dsum = dsum + e1 * e1;
+          dsum = dsum + e2 * e2;
+          dist[nc] = dsum;
+          cand[nc] = a * 16 + b * 4 + c;
+          if (dsum < best) best = dsum;
+          ++nc;
+        }
+  int win = -1;
+  double second = INFINITY;
+  for (int c = 0; c < nc; ++c) {
+    if (dist[c] <= best + 1e-9) {
+      if (win < 0) win = c;
+    } else if (dist[c] < second) {
+      second = dist[c];
+    }
+  }
+  *code_out = cand[win];
+  *S_out = S;
+  double tm = fabs(rho - tau128), tm2 = fabs(rho - tau256);
+  diag[0] = rho;
+  diag[1] = tm < tm2 ? tm : tm2;
+  diag[2] = second - best;
+  diag[3] = best;
+}
+
+constexpr int kQuantThreads = 1024;
+
+__global__ void __launch_bounds__(kQuantThreads)
+    quantize_kernel(int Z, int nb_max, const double *__restrict__ zstat,
+                    const double *__restrict__ astat, int have_audio, double tau128,
+                    double tau256, double eps, int mel, int *__restrict__ zshape,
+                    int *__restrict__ zblock, double *__restrict__ zdiag,
+                    int *__restrict__ blk_start, int *__restrict__ blk_size,
+                    int *__restrict__ unit_blk) {
+  const int h = blockIdx.x, tid = threadIdx.x;
+  __shared__ double red[2][kQuantThreads / 64];
+  __shared__ int scan[kQuantThreads];
+  const double *zs = zstat + (size_t)h * Z * 4;
+  double rmax = 0, amax = 0;
+  for (int m = tid; m < Z; m += kQuantThreads) {
+    rmax = fmax(rmax, zs[4 * m + 3]);
+    if (have_audio) amax = fmax(amax, astat[4 * m]);
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    rmax = fmax(rmax, __shfl_xor(rmax, off, 64));
+    amax = fmax(amax, __shfl_xor(amax, off, 64));
+  }
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = rmax;
+    red[1][tid >> 6] = amax;
+  }
+  __syncthreads();
+  rmax = 0;
+  amax = 0;
+  for (int w = 0; w < kQuantThreads / 64; ++w) {
+    rmax = fmax(rmax, red[0][w]);
+    amax = fmax(amax, red[1][w]);
+  }
+  // shapes; each thread owns a contiguous chunk of zones for the scan below
+  const int chunk = (Z + kQuantThreads - 1) / kQuantThreads;
+  const int m0 = tid * chunk, m1 = min(Z, m0 + chunk);
+  int local = 0;
+  for (int m = m0; m < m1; ++m) {
+    int code, S;
+    shape_of_zone(zs + 4 * m, have_audio ? astat + 4 * m : nullptr, rmax, amax, tau128, tau256,
+                  eps, mel, &code, &S, zdiag + ((size_t)h * Z + m) * 4);
+    zshape[(size_t)h * Z + m] = code;
+    local += kZoneTok >> S;
+  }
+  scan[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kQuantThreads; off <<= 1) {
+    int add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  int base = scan[tid] - local;  // exclusive prefix of this thread's chunk
+  int *zb = zblock + (size_t)h * (Z + 1);
+  for (int m = m0; m < m1; ++m) {
+    int code = zshape[(size_t)h * Z + m];
+    int S = ((code >> 4) & 3) + ((code >> 2) & 3) + (code & 3);
+    int B = 1 << S, nbz = kZoneTok >> S;
+    zb[m] = base;
+    for (int b = 0; b < nbz; ++b) {
+      blk_start[(size_t)h * nb_max + base + b] = kZoneTok * m + b * B;
+      blk_size[(size_t)h * nb_max + base + b] = B;
+    }
+    for (int s = 0; s < kZoneTok / kUnit; ++s)
+      unit_blk[(size_t)h * (Z * 8) + 8 * m + s] = base + s * kUnit / B;
+    base += nbz;
+  }
+  if (tid == kQuantThreads - 1) zb[Z] = scan[tid];
+}
+
+hipError_t launch_quantize(const Dims &d, const prism_config *cfg, const double *zstat,
+                           const double *astat, bool have_audio, uint8_t *ws, const Layout &L,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(quantize_kernel, dim3(d.heads), dim3(kQuantThreads), 0, s, d.Z, d.nb_max,
+                     zstat, astat, have_audio ? 1 : 0, (double)cfg->tau128,
+                     (double)cfg->tau256, cfg->eps, cfg->min_edge_log2,
+                     (int *)(ws + L.pub.zone_shape), (int *)(ws + L.pub.zone_block),
+                     (double *)(ws + L.pub.zone_diag), (int *)(ws + L.pub.block_start),
+                     (int *)(ws + L.pub.block_size), (int *)(ws + L.pub.unit_block));
+  return hipGetLastError();
+}
+
+// ============================================================================ gather + pool
+// Block-contiguous permutation (digest summary and pipeline: tokens are rearranged so each
+// block is contiguous, with one partition shared by Q, K and V): zones in raster order,
+// blocks inside a zone in raster order of block coordinates, tokens inside a block in
+// raster order.  One workgroup per (zone, head) writes perm / inv_perm, copies the zone's
+// 512 rows of Q, K, V into the permuted row-major layout (and, for bfloat16, into a
+// per-64-token-unit transposed layout [D][64] used as the key-major MFMA operand), and
+// forms the float32 block means of Q and K (digest obstacles and selection sections).
+//
+// Transposed layout: within each group of 16 keys the stored order is
+// 0-3, 8-11, 4-7, 12-15 (bits 2 and 3 of the key index swapped), which makes the 8 keys a
+// lane feeds to one 32x32x16 MFMA step contiguous.
+__device__ __forceinline__ int swap23(int e) {
+  return (e & ~12) | ((e >> 1) & 4) | ((e << 1) & 8);
+}
+
+template <typename T, int D, bool TRANSPOSE>
+__global__ void __launch_bounds__(256)
+    gather_kernel(int H, int W, int heads, int nzh, int nzw, int N, int nb_max, const T *q,
+                  const T *k, const T *v, const int *__restrict__ zshape,
+                  const int *__restrict__ zblock, int *__restrict__ perm,
+                  int *__restrict__ inv, T *qp, T *kp, T *vp, T *qpt, T *kpt, T *vpt,
+                  float *__restrict__ qbar, float *__restrict__ kbar, int Z) {
+  constexpr int VPC = 16 / (int)sizeof(T);  // values per 16-byte chunk
+  constexpr int CH = D / VPC;               // chunks per row
+  constexpr int RG = 256 / CH;              // rows per pass
+  constexpr int RPT = kUnit / RG;           // rows per thread per unit
+  const int m = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int zw = m % nzw, zh = (m / nzw) % nzh, zt = m / (nzw * nzh);
+  const int code = zshape[(size_t)h * Z + m];
+  const int lt = (code >> 4) & 3, lh = (code >> 2) & 3, lw = code & 3;
+  const int bT = 1 << lt, bH = 1 << lh, bW = 1 << lw, B = bT * bH * bW;
+  const int nbH = kZone / bH, nbW = kZone / bW;
+  const int blk0 = zblock[(size_t)h * (Z + 1) + m];
+
+  __shared__ int tok[kZoneTok];
+  __shared__ float psum[RG][D];
+  __shared__ __align__(16) uint16_t tile[TRANSPOSE ? kUnit * D : 8];
+
+  for (int p = tid; p < kZoneTok; p += 256) {
+    int beta = p / B, r = p % B;
+    int gT = beta / (nbH * nbW), gH = (beta / nbW) % nbH, gW = beta % nbW;
+    int rT = r / (bH * bW), rH = (r / bW) % bH, rW = r % bW;
+    int t = zt * kZone + gT * bT + rT, hh = zh * kZone + gH * bH + rH,
+        w = zw * kZone + gW * bW + rW;
+    int token = (t * H + hh) * W + w;
+    tok[p] = token;
+    perm[(size_t)h * N + kZoneTok * m + p] = token;
+    inv[(size_t)h * N + token] = kZoneTok * m + p;
+  }
+  __syncthreads();
+
+  const int c = tid % CH, rg = tid / CH;
+  const T *src[3] = {q, k, v};
+  T *dst[3] = {qp, kp, vp};
+  T *dstt[3] = {qpt, kpt, vpt};
+  float *bar[2] = {qbar, kbar};
+  const size_t tstride = (size_t)heads * D;
+  for (int x = 0; x < 3; ++x) {
+    float acc[VPC];
+#pragma unroll
+    for (int e = 0; e < VPC; ++e) acc[e] = 0.f;
+    for (int s = 0; s < kZoneTok / kUnit; ++s) {
+      u32x4 buf[RPT];
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr) {
+        int p = s * kUnit + rg + RG * rr;
+        buf[rr] = *reinterpret_cast<const u32x4 *>(src[x] + (size_t)tok[p] * tstride +
+                                                   (size_t)h * D + c * VPC);
+      }
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr) {
+        int p = s * kUnit + rg + RG * rr;
+        *reinterpret_cast<u32x4 *>(dst[x] + ((size_t)h * N + kZoneTok * m + p) * D + c * VPC) =
+            buf[rr];
+        if (x < 2) {
+          if constexpr (sizeof(T) == 2) {
+            const uint32_t *w32 = reinterpret_cast<const uint32_t *>(&buf[rr]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[2 * e] += __uint_as_float(w32[e] << 16);
+              acc[2 * e + 1] += __uint_as_float(w32[e] & 0xffff0000u);
+            }
+          } else {
+            const float *f = reinterpret_cast<const float *>(&buf[rr]);
+#pragma unroll
+            for (int e = 0; e < VPC; ++e) acc[e] += f[e];
+          }
+        }
+        if constexpr (TRANSPOSE) {
+          int row = rg + RG * rr;
+          *reinterpret_cast<u32x4 *>(&tile[row * D + c * VPC]) = buf[rr];
+        }
+      }
+      if constexpr (TRANSPOSE) {
+        __syncthreads();
+        // [D][64] for this unit: thread -> (d, half of the 64 keys)
+        const int dd = tid >> 1, half = tid & 1;
+        const size_t ubase = ((size_t)h * (N / kUnit) + (size_t)m * 8 + s) * (size_t)(D * kUnit);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          uint32_t pk[4];
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            int pos0 = 32 * half + 8 * cc + e;
+            int key0 = (pos0 & ~15) | swap23(pos0 & 15);
+            int key1 = ((pos0 + 1) & ~15) | swap23((pos0 + 1) & 15);
+            pk[e >> 1] = (uint32_t)tile[key0 * D + dd] | ((uint32_t)tile[key1 * D + dd] << 16);
+          }
+          *reinterpret_cast<u32x4 *>(dstt[x] + ubase + (size_t)dd * kUnit + 32 * half + 8 * cc) =
+              u32x4{pk[0], pk[1], pk[2], pk[3]};
+        }
+        __syncthreads();
+      }
+      // block boundary: reduce the pooled sums over the row groups
+      if (x < 2 && ((s + 1) * kUnit) % B == 0) {
+#pragma unroll
+        for (int e = 0; e < VPC; ++e) psum[rg][c * VPC + e] = acc[e];
+        __syncthreads();
+        if (tid < D) {
+          float sum = 0.f;
+          for (int g = 0; g < RG; ++g) sum += psum[g][tid];
+          int blk = blk0 + (s * kUnit) / B;
+          bar[x][((size_t)h * nb_max + blk) * D + tid] = sum / (float)B;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < VPC; ++e) acc[e] = 0.f;
+      }
+    }
+  }
+}
+
+hipError_t launch_gather(const Dims &d, const void *q, const void *k, const void *v,
+                         uint8_t *ws, const Layout &L, hipStream_t s) {
+  dim3 grid(d.Z, d.heads);
+  const int *zshape = (const int *)(ws + L.pub.zone_shape);
+  const int *zblock = (const int *)(ws + L.pub.zone_block);
+  int *perm = (int *)(ws + L.pub.perm), *inv = (int *)(ws + L.pub.inv_perm);
+  float *qbar = (float *)(ws + L.pub.qbar), *kbar = (float *)(ws + L.pub.kbar);
+  if (d.dtype == PRISM_BF16) {
+    typedef uint16_t T;
+    hipLaunchKernelGGL((gather_kernel<T, 128, true>), grid, dim3(256), 0, s, d.H, d.W, d.heads,
+                       d.nzh, d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k, (const T *)v,
+                       zshape, zblock, perm, inv, (T *)(ws + L.qp), (T *)(ws + L.kp),
+                       (T *)(ws + L.vp), (T *)(ws + L.qpt), (T *)(ws + L.kpt),
+                       (T *)(ws + L.vpt), qbar, kbar, d.Z);
+  } else if (d.D == 64) {
+    typedef float T;
+    hipLaunchKernelGGL((gather_kernel<T, 64, false>), grid, dim3(256), 0, s, d.H, d.W, d.heads,
+                       d.nzh, d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k, (const T *)v,
+                       zshape, zblock, perm, inv, (T *)(ws + L.qp), (T *)(ws + L.kp),
+                       (T *)(ws + L.vp), nullptr, nullptr, nullptr, qbar, kbar, d.Z);
+  } else {
+    typedef float T;
+    hipLaunchKernelGGL((gather_kernel<T, 128, false>), grid, dim3(256), 0, s, d.H, d.W,
+                       d.heads, d.nzh, d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k,
+                       (const T *)v, zshape, zblock, perm, inv, (T *)(ws + L.qp),
+                       (T *)(ws + L.kp), (T *)(ws + L.vp), nullptr, nullptr, nullptr, qbar,
+                       kbar, d.Z);
+  }
+  return hipGetLastError();
+}
+
+// ============================================================================ tile lists
+// Attention work items: 128-row tiles inside blocks of 128 or 256 tokens and 64-row tiles
+// for 64-token blocks (the 64-token atomic unit of the digest's training section; 128- and
+// 256-token blocks are 2 and 4 units).  The same tiles serve as query tiles (forward, dQ)
+// and key tiles (dK/dV) because Q, K and V share one partition.  Order inside a list is
+// immaterial to the results.
+__global__ void zero_ints_kernel(int *p, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+__global__ void tiles_kernel(int heads, int Z, const int *__restrict__ zshape, int2 *t128,
+                             int2 *t64, int *counters) {
+  int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= heads * Z) return;
+  int h = idx / Z, m = idx % Z;
+  int code = zshape[idx];
+  int S = ((code >> 4) & 3) + ((code >> 2) & 3) + (code & 3);
+  if (S >= 7) {
+    int at = atomicAdd(&counters[0], 4);
+    for (int s = 0; s < 4; ++s) t128[at + s] = make_int2(h, 8 * m + 2 * s);
+  } else {
+    int at = atomicAdd(&counters[1], 8);
+    for (int s = 0; s < 8; ++s) t64[at + s] = make_int2(h, 8 * m + s);
+  }
+}
+
+hipError_t launch_tiles(const Dims &d, uint8_t *ws, const Layout &L, hipStream_t s) {
+  hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(64), 0, s, (int *)(ws + L.counters), 16);
+  int n = d.heads * d.Z;
+  hipLaunchKernelGGL(tiles_kernel, dim3((n + 255) / 256), dim3(256), 0, s, d.heads, d.Z,
+                     (const int *)(ws + L.pub.zone_shape), (int2 *)(ws + L.tiles128),
+                     (int2 *)(ws + L.tiles64), (int *)(ws + L.counters));
+  return hipGetLastError();
+}
+
+}  // namespace prism

@@ -1,0 +1,242 @@
+// prism_api.hip -- host side of libprism.so: configuration checks, workspace layout and
+// the launch sequence of each entry point declared in include/prism.h.
+#include <math.h>
+#include <string.h>
+
+#include <string>
+
+#include "prism_internal.h"
+
+namespace prism {
+
+static thread_local std::string g_last_error;
+
+static prism_status fail(prism_status st, const std::string &msg) {
+  g_last_error = msg;
+  return st;
+}
+
+prism_status check_config(const prism_config *cfg, Dims *d, const char **why) {
+  *why = "";
+  if (!cfg) {
+    *why = "null configuration";
+    return PRISM_ERR_ARG;
+  }
+  if (cfg->T <= 0 || cfg->H <= 0 || cfg->W <= 0 || cfg->num_heads <= 0 || cfg->head_dim <= 0) {
+    *why = "grid sizes, heads and head_dim must be positive";
+    return PRISM_ERR_ARG;
+  }
+  if (cfg->T % kZone || cfg->H % kZone || cfg->W % kZone) {
+    *why = "T, H and W must be multiples of the 8-token zone edge";
+    return PRISM_ERR_UNSUPPORTED;
+  }
+  if (cfg->dtype != PRISM_F32 && cfg->dtype != PRISM_BF16) {
+    *why = "dtype must be PRISM_F32 or PRISM_BF16";
+    return PRISM_ERR_UNSUPPORTED;
+  }
+  if (cfg->dtype == PRISM_BF16 ? cfg->head_dim != 128
+                               : (cfg->head_dim != 64 && cfg->head_dim != 128)) {
+    *why = "head_dim must be 128 for bfloat16, 64 or 128 for float32";
+    return PRISM_ERR_UNSUPPORTED;
+  }
+  if (cfg->min_edge_log2 != 0 && cfg->min_edge_log2 != 1) {
+    *why = "min_edge_log2 must be 0 or 1";
+    return PRISM_ERR_ARG;
+  }
+  if (cfg->top_k < 0 || !(cfg->top_p >= 0.f) || !isfinite(cfg->top_p) ||
+      !isfinite(cfg->tau128) || !isfinite(cfg->tau256) || !(cfg->eps >= 0.0) ||
+      !isfinite(cfg->eps) || !isfinite(cfg->score_scale) || !isfinite(cfg->softmax_scale)) {
+    *why = "top_k, top_p, tau, eps and scales must be finite and non-negative";
+    return PRISM_ERR_ARG;
+  }
+  if (cfg->num_heads > 4096) {
+    *why = "too many heads in one call";
+    return PRISM_ERR_UNSUPPORTED;
+  }
+  long long N = (long long)cfg->T * cfg->H * cfg->W;
+  if (N / kUnit > kMaxUnits) {
+    *why = "more than 65535 64-token units per head";
+    return PRISM_ERR_UNSUPPORTED;
+  }
+  d->T = cfg->T;
+  d->H = cfg->H;
+  d->W = cfg->W;
+  d->heads = cfg->num_heads;
+  d->D = cfg->head_dim;
+  d->dtype = cfg->dtype;
+  d->N = (int)N;
+  d->Z = (int)(N / kZoneTok);
+  d->U = (int)(N / kUnit);
+  d->nb_max = d->U;
+  d->nzt = cfg->T / kZone;
+  d->nzh = cfg->H / kZone;
+  d->nzw = cfg->W / kZone;
+  d->words = (d->nb_max + 31) / 32;
+  d->elt = cfg->dtype == PRISM_BF16 ? 2 : 4;
+  return PRISM_OK;
+}
+
+Layout make_layout(const Dims &d) {
+  Layout L;
+  memset(&L, 0, sizeof(L));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return at;
+  };
+  const size_t H = d.heads, N = d.N, Z = d.Z, U = d.U, NB = d.nb_max, D = d.D;
+  L.pub.zone_stats = take(H * Z * 4 * sizeof(double));
+  L.pub.audio_stats = take(Z * 4 * sizeof(double));
+  L.pub.zone_diag = take(H * Z * 4 * sizeof(double));
+  L.pub.zone_shape = take(H * Z * sizeof(int));
+  L.pub.zone_block = take(H * (Z + 1) * sizeof(int));
+  L.pub.block_start = take(H * NB * sizeof(int));
+  L.pub.block_size = take(H * NB * sizeof(int));
+  L.pub.unit_block = take(H * U * sizeof(int));
+  L.pub.perm = take(H * N * sizeof(int));
+  L.pub.inv_perm = take(H * N * sizeof(int));
+  L.pub.qbar = take(H * NB * D * sizeof(float));
+  L.pub.kbar = take(H * NB * D * sizeof(float));
+  L.pub.sel_count = take(H * NB * sizeof(int));
+  L.pub.csr_col = take(H * NB * NB * sizeof(int));
+  L.pub.csc_count = take(H * NB * sizeof(int));
+  L.pub.csc_row = take(H * NB * NB * sizeof(int));
+  L.pub.scores = take(NB * NB * sizeof(float));
+  L.sel_bits = take(H * NB * d.words * sizeof(uint32_t));
+  L.csc_bits = take(H * NB * d.words * sizeof(uint32_t));
+  L.tiles128 = take(H * U * sizeof(int2));
+  L.tiles64 = take(H * U * sizeof(int2));
+  L.counters = take(16 * sizeof(int));
+  L.delta = take(H * N * sizeof(float));
+  L.lsep = take(H * N * sizeof(float));
+  L.o32p = take(H * N * D * sizeof(float));
+  const size_t tensor = H * N * D * d.elt;
+  L.qp = take(tensor);
+  L.kp = take(tensor);
+  L.vp = take(tensor);
+  L.dop = take(tensor);
+  if (d.dtype == PRISM_BF16) {
+    L.qpt = take(tensor);
+    L.kpt = take(tensor);
+    L.vpt = take(tensor);
+    L.dopt = take(tensor);
+  }
+  L.total = off;
+  L.pub.total = off;
+  L.pub.N = d.N;
+  L.pub.Z = d.Z;
+  L.pub.nb_max = d.nb_max;
+  return L;
+}
+
+Scales scales_of(const prism_config *cfg, const Dims &d) {
+  Scales s;
+  const float inv = 1.0f / sqrtf((float)d.D);
+  s.score = cfg->score_scale > 0 ? cfg->score_scale : inv;
+  s.softmax = cfg->softmax_scale > 0 ? cfg->softmax_scale : inv;
+  return s;
+}
+
+static prism_status launched(hipError_t e, const char *stage) {
+  if (e != hipSuccess)
+    return fail(PRISM_ERR_HIP, std::string(stage) + ": " + hipGetErrorString(e));
+  return PRISM_OK;
+}
+
+}  // namespace prism
+
+using namespace prism;
+
+extern "C" {
+
+size_t prism_workspace_bytes(const prism_config *cfg) {
+  Dims d;
+  const char *why;
+  if (check_config(cfg, &d, &why) != PRISM_OK) return 0;
+  return make_layout(d).total;
+}
+
+prism_status prism_plan_layout(const prism_config *cfg, prism_layout *out) {
+  Dims d;
+  const char *why;
+  prism_status st = check_config(cfg, &d, &why);
+  if (st != PRISM_OK) return fail(st, why);
+  if (!out) return fail(PRISM_ERR_ARG, "null layout pointer");
+  *out = make_layout(d).pub;
+  return PRISM_OK;
+}
+
+prism_status prism_plan(const prism_config *cfg, const void *q, const void *k, const void *v,
+                        const float *a2v_norm, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+  Dims d;
+  const char *why;
+  prism_status st = check_config(cfg, &d, &why);
+  if (st != PRISM_OK) return fail(st, why);
+  if (!q || !k || !v || !workspace) return fail(PRISM_ERR_ARG, "null tensor or workspace");
+  Layout L = make_layout(d);
+  if (workspace_bytes < L.total) return fail(PRISM_ERR_WORKSPACE, "workspace too small");
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *ws = (uint8_t *)workspace;
+  Scales sc = scales_of(cfg, d);
+  double *zstat = (double *)(ws + L.pub.zone_stats);
+  double *astat = (double *)(ws + L.pub.audio_stats);
+  if (a2v_norm) {
+    if ((st = launched(launch_audio_stats(d, a2v_norm, astat, s), "audio stats"))) return st;
+  }
+  if ((st = launched(launch_zone_stats(d, v, zstat, s), "zone stats"))) return st;
+  if ((st = launched(launch_quantize(d, cfg, zstat, astat, a2v_norm != nullptr, ws, L, s),
+                     "quantiser")))
+    return st;
+  if ((st = launched(launch_gather(d, q, k, v, ws, L, s), "gather"))) return st;
+  if ((st = launched(launch_tiles(d, ws, L, s), "tiles"))) return st;
+  if ((st = launched(launch_scores_select(d, cfg, sc.score, ws, L, s), "selection"))) return st;
+  return PRISM_OK;
+}
+
+prism_status prism_attn_fwd(const prism_config *cfg, void *workspace, size_t workspace_bytes,
+                            void *o, float *lse, void *stream) {
+  Dims d;
+  const char *why;
+  prism_status st = check_config(cfg, &d, &why);
+  if (st != PRISM_OK) return fail(st, why);
+  if (!o || !lse || !workspace) return fail(PRISM_ERR_ARG, "null output or workspace");
+  Layout L = make_layout(d);
+  if (workspace_bytes < L.total) return fail(PRISM_ERR_WORKSPACE, "workspace too small");
+  Scales sc = scales_of(cfg, d);
+  return launched(launch_attn_fwd(d, sc.softmax, (uint8_t *)workspace, L, o, lse,
+                                  (hipStream_t)stream),
+                  "attention forward");
+}
+
+prism_status prism_attn_bwd(const prism_config *cfg, void *workspace, size_t workspace_bytes,
+                            const void *dout, void *dq, void *dk, void *dv, void *stream) {
+  Dims d;
+  const char *why;
+  prism_status st = check_config(cfg, &d, &why);
+  if (st != PRISM_OK) return fail(st, why);
+  if (!dout || !dq || !dk || !dv || !workspace)
+    return fail(PRISM_ERR_ARG, "null tensor or workspace");
+  Layout L = make_layout(d);
+  if (workspace_bytes < L.total) return fail(PRISM_ERR_WORKSPACE, "workspace too small");
+  Scales sc = scales_of(cfg, d);
+  return launched(launch_attn_bwd(d, sc.softmax, (uint8_t *)workspace, L, dout, dq, dk, dv,
+                                  (hipStream_t)stream),
+                  "attention backward");
+}
+
+const char *prism_status_string(int status) {
+  switch (status) {
+    case PRISM_OK: return "ok";
+    case PRISM_ERR_ARG: return "invalid argument";
+    case PRISM_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PRISM_ERR_WORKSPACE: return "workspace too small";
+    case PRISM_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char *prism_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// prism_internal.h -- types, workspace layout and kernel launchers shared by the
+// translation units of libprism.so.  Not installed; the public ABI is include/prism.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/prism.h"
+
+namespace prism {
+
+constexpr int kZone = 8;       // macro-zone edge along T, H, W
+constexpr int kZoneTok = 512;  // tokens per zone
+constexpr int kUnit = 64;      // tokens per atomic compute unit of the attention kernels
+constexpr int kMaxUnits = 65535;  // units per head (block indices fit 16 bits)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+struct Dims {
+  int T, H, W, heads, D, dtype;
+  int N, Z, U, nb_max;   // tokens, zones, 64-token units, max blocks per head (= U)
+  int nzt, nzh, nzw;     // zones per axis
+  int words;             // 32-bit words per selection bitmask row
+  size_t elt;            // bytes per token-tensor element
+};
+
+// Internal workspace layout: the public arrays of prism_layout plus scratch.
+struct Layout {
+  prism_layout pub;
+  size_t qp, kp, vp;        // permuted copies, row-major [heads][N][D]
+  size_t qpt, kpt, vpt;     // bf16 only: per-unit transposed [heads][U][D][64]
+  size_t sel_bits;          // uint32 [heads][nb_max][words]
+  size_t csc_bits;          // uint32 [heads][nb_max][words]
+  size_t tiles128, tiles64; // int2 [heads*U]: (head, first unit) of each query/key tile
+  size_t counters;          // int32 [16]: tile counts
+  size_t dop, dopt;         // bwd: gathered dout, row-major and per-unit transposed
+  size_t o32p;              // fwd: float [heads][N][D] output in permuted order
+  size_t lsep;              // fwd: float [heads][N] lse in permuted order
+  size_t delta;             // bwd: float [heads][N] rowsum(dO * O) in permuted order
+  size_t total;
+};
+
+prism_status check_config(const prism_config *cfg, Dims *d, const char **why);
+Layout make_layout(const Dims &d);
+
+struct Scales {
+  float score, softmax;
+};
+Scales scales_of(const prism_config *cfg, const Dims &d);
+
+// ---------------------------------------------------------------------------- launchers
+// plan_kernels.hip
+hipError_t launch_audio_stats(const Dims &d, const float *a2v, double *astat, hipStream_t s);
+hipError_t launch_zone_stats(const Dims &d, const void *v, double *zstat, hipStream_t s);
+hipError_t launch_quantize(const Dims &d, const prism_config *cfg, const double *zstat,
+                           const double *astat, bool have_audio, uint8_t *ws, const Layout &L,
+                           hipStream_t s);
+hipError_t launch_gather(const Dims &d, const void *q, const void *k, const void *v,
+                         uint8_t *ws, const Layout &L, hipStream_t s);
+hipError_t launch_tiles(const Dims &d, uint8_t *ws, const Layout &L, hipStream_t s);
+// select_kernels.hip
+hipError_t launch_scores_select(const Dims &d, const prism_config *cfg, float score_scale,
+                                uint8_t *ws, const Layout &L, hipStream_t s);
+// attn_fwd.hip
+hipError_t launch_attn_fwd(const Dims &d, float scale, uint8_t *ws, const Layout &L, void *o,
+                           float *lse, hipStream_t s);
+// attn_bwd.hip
+hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout &L,
+                           const void *dout, void *dq, void *dk, void *dv, hipStream_t s);
+
+// ---------------------------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+// Round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ T *ws_ptr(uint8_t *ws, size_t off) {
+  return reinterpret_cast<T *>(ws + off);
+}
+
+}  // namespace prism

@@ -1,0 +1,138 @@
+/*
+ * prism.h -- C ABI of libprism.so: Prism's dynamic block-sparse video self-attention for
+ * one layer and one group of heads, on AMD Instinct MI355X (gfx950).
+ *
+ * The method (arXiv 2610.05416, "Prism: Dynamic Sparse Attention for Native 2K Joint
+ * Video-Audio Generation Model Training"), as described by the nanless audio-paper-digest
+ * post and the xyznot.com review:
+ *   1. the T x H x W video token grid is cut into 8 x 8 x 8 macro-zones (digest, pipeline
+ *      section and Fig. 2);
+ *   2. per zone and head, a variation indicator g_d = r_{v,d} + a_bar * v_hat_{a,d} + eps
+ *      from the channel variance of axis-pooled V and from the audio-to-video
+ *      cross-attention norm field (digest, guidance section, Eq. g_d; review, "Метод"
+ *      item 1);
+ *   3. a block volume B in {64, 128, 256} from the normalised information density rho
+ *      (thresholds 0.5 and 0.25) and the candidate shape nearest in log2 space to the
+ *      closed-form optimum of the shape loss J (digest, density section, Eq. rho_raw and
+ *      Eq. J; review item 2);
+ *   4. a permutation making every block contiguous (shared by Q, K, V), mean-pooled block
+ *      representatives, block scores, and Top-k union Top-p key-block selection per query
+ *      block (digest, selection section; review item 3);
+ *   5. exact attention over the selected key blocks with an online softmax, forward and
+ *      backward, the plan held constant for the gradient (digest, selection and training
+ *      sections), and the inverse permutation of the outputs.
+ *
+ * Conventions shared by every entry point
+ *   - Token order is raster over (t, h, w) with w fastest: n = (t*H + h)*W + w.
+ *   - Token tensors (q, k, v, o, dout, dq, dk, dv) are dense row-major [N][heads][D] in the
+ *     configured dtype (float32 or bfloat16); lse is float32 [heads][N]; the A2V norm
+ *     field is float32 [N] shared by all heads.
+ *   - All pointers are device pointers.  The caller owns every buffer, including the
+ *     workspace; the library allocates no device memory.
+ *   - Calls are asynchronous on the caller's HIP stream (a hipStream_t passed as void*,
+ *     NULL = the null stream) and never synchronise the host.
+ *   - Arguments are checked before any launch; a rejected call launches nothing and
+ *     returns a negative status.  No exception crosses this boundary.
+ *   - A call is thread-safe as long as concurrent calls use distinct workspaces.
+ */
+#ifndef PRISM_H
+#define PRISM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PRISM_OK = 0,
+    PRISM_ERR_ARG = -1,          /* null pointer, bad size, inconsistent configuration */
+    PRISM_ERR_UNSUPPORTED = -2,  /* grid not a multiple of 8, head_dim / dtype not built */
+    PRISM_ERR_WORKSPACE = -3,    /* workspace smaller than prism_workspace_bytes() */
+    PRISM_ERR_HIP = -4           /* a HIP launch failed; see prism_last_error() */
+} prism_status;
+
+typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
+
+typedef struct prism_config {
+    int T, H, W;          /* video latent grid; each a positive multiple of 8 (zone edge) */
+    int num_heads;        /* heads handled by one call, each with its own plan */
+    int head_dim;         /* D: 64 or 128 (float32), 128 (bfloat16) */
+    int dtype;            /* prism_dtype of every token tensor */
+    int min_edge_log2;    /* 1: edges {2,4,8}, 16 candidate shapes (the pages' pool);
+                             0: edges {1,2,4,8}, 19 shapes */
+    int top_k;            /* Top-k in key blocks (>= number of blocks keeps all) */
+    float top_p;          /* Top-p cumulative block relevance; 0 leaves Top-k alone */
+    float tau128;         /* rho >= tau128 -> B = 64 (pages: 0.5) */
+    float tau256;         /* tau256 <= rho < tau128 -> B = 128, else 256 (pages: 0.25) */
+    double eps;           /* epsilon in g_d (pages give no value; default 1e-6) */
+    float score_scale;    /* block-score logit scale; <= 0 selects 1/sqrt(D) */
+    float softmax_scale;  /* attention logit scale; <= 0 selects 1/sqrt(D) */
+} prism_config;
+
+/* Offsets (bytes from the workspace base) and element types of the plan's arrays, for
+ * inspection.  Nb_max = N / 64.  Per head h:
+ *   zone_stats  double [heads][Z][4]: sigma2_T, sigma2_H, sigma2_W, rho_raw (Z = N / 512)
+ *   audio_stats double [Z][4]: zone mean of a, sigma2_T, sigma2_H, sigma2_W
+ *   zone_diag   double [heads][Z][4]: rho, tier margin, shape margin, best distance
+ *   zone_shape  int32  [heads][Z]: log2 edges packed as lT*16 + lH*4 + lW
+ *   zone_block  int32  [heads][Z+1]: first block of each zone; [Z] = block count Nb
+ *   block_start int32  [heads][Nb_max]: permuted offset of each block (multiple of 64)
+ *   block_size  int32  [heads][Nb_max]: 64, 128 or 256
+ *   unit_block  int32  [heads][N/64]: block holding each 64-token unit
+ *   perm        int32  [heads][N]: permuted position -> token
+ *   inv_perm    int32  [heads][N]: token -> permuted position
+ *   qbar, kbar  float  [heads][Nb_max][D]: block means of Q and K
+ *   sel_count   int32  [heads][Nb_max]: selected key blocks per query block
+ *   csr_col     int32  [heads][Nb_max][Nb_max]: row i holds sel_count[i] key blocks,
+ *                      ascending (a CSR whose row i starts at i * Nb_max)
+ *   csc_count   int32  [heads][Nb_max], csc_row int32 [heads][Nb_max][Nb_max]: the
+ *                      transpose (query blocks selecting each key block, ascending)
+ *   scores      float  [Nb_max][Nb_max]: block logits of the last head planned */
+typedef struct prism_layout {
+    size_t zone_stats, audio_stats, zone_diag, zone_shape, zone_block, block_start,
+        block_size, unit_block, perm, inv_perm, qbar, kbar, sel_count, csr_col, csc_count,
+        csc_row, scores, total;
+    int N, Z, nb_max;
+} prism_layout;
+
+/* Bytes of workspace a configuration needs (0 if the configuration is rejected). */
+size_t prism_workspace_bytes(const prism_config *cfg);
+
+/* Fills *out with the workspace layout of cfg.  PRISM_ERR_ARG / _UNSUPPORTED on a
+ * rejected configuration. */
+prism_status prism_plan_layout(const prism_config *cfg, prism_layout *out);
+
+/* Plans every head: zone statistics of V and of the A2V norm field, shapes, permutation,
+ * permuted copies of Q, K, V, block means, block scores and the Top-k union Top-p
+ * selection (steps 1-4 above).  q, k, v: [N][heads][D]; a2v_norm: [N] float32, or NULL
+ * for a layer with no cached A2V norm (the first layer: video guidance only).  The plan
+ * is written into workspace, which must stay untouched until the last fwd/bwd using it. */
+prism_status prism_plan(const prism_config *cfg, const void *q, const void *k, const void *v,
+                        const float *a2v_norm, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/* Sparse attention forward over the plan in workspace (step 5): o [N][heads][D] in token
+ * order, lse [heads][N] float32 (natural-log sum of exp of the scaled logits).  Also keeps
+ * a float32 copy of o and the lse in workspace for prism_attn_bwd. */
+prism_status prism_attn_fwd(const prism_config *cfg, void *workspace, size_t workspace_bytes,
+                            void *o, float *lse, void *stream);
+
+/* Sparse attention backward with the plan held constant (digest, training section): given
+ * dout [N][heads][D], writes dq, dk, dv [N][heads][D] (overwritten, token order).  Reads
+ * the float32 copy of the output and the lse that prism_attn_fwd left in workspace, so
+ * prism_attn_fwd must have run on this workspace since the last prism_plan. */
+prism_status prism_attn_bwd(const prism_config *cfg, void *workspace, size_t workspace_bytes,
+                            const void *dout, void *dq, void *dk, void *dv, void *stream);
+
+/* Text of a status code. */
+const char *prism_status_string(int status);
+
+/* Message of the last failed call on the calling thread ("" if none). */
+const char *prism_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PRISM_H */

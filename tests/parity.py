@@ -1,0 +1,138 @@
+"""Comparison of the HIP path (through the C ABI) with the CPU oracle on the same seeded
+inputs.  Plans: zone shapes, permutations, block tables bit-exact (zones whose tier or shape
+decision margin is below 1e-9 are counted and excluded); selections bit-exact as sets except
+key blocks whose logit lies within 1e-5 of the row's cut logit or whose inclusion by Top-p
+depends on a cumulative mass within 1e-5 of p (counted).  Attention outputs and gradients
+within max-abs 1e-4 (float32) or 2e-2 plus one bfloat16 ulp of the reference value
+(bfloat16) on rows whose selection matched."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import dynamic_block_sparse_stats_amd as P
+import oracle
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def ulp_bf16(x):
+    """One unit in the last place of bfloat16 at |x| (8 significant bits)."""
+    ax = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+def check_close(got, ref, dtype, what=""):
+    """float32: max-abs <= 1e-4.  bfloat16: |got - ref| <= 2e-2 + one bf16 ulp of ref (the
+    stored result cannot be closer to the exact value than its own rounding step, which
+    exceeds 2e-2 once |ref| >= 8).  Returns (max abs error, max error / bound)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    bound = TOL[dtype] + (ulp_bf16(ref) if dtype == "bf16" else 0.0)
+    ratio = float((err / bound).max()) if err.size else 0.0
+    worst = np.unravel_index(int(np.argmax(err / bound)), err.shape) if err.size else ()
+    assert ratio <= 1.0, (f"{what}: error {err[worst]:.3e} at {worst} exceeds bound "
+                          f"{np.broadcast_to(bound, err.shape)[worst]:.3e} (ref {ref[worst]:.4f})")
+    return float(err.max()) if err.size else 0.0, ratio
+
+
+SEL_TOL = 1e-5
+MARGIN = 1e-9
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()
+
+
+def run_plan(cfg, inp, a2v=True):
+    att = P.PrismAttention(cfg)
+    att.plan(inp["q"], inp["k"], inp["v"], inp["a2v"] if a2v else None)
+    torch.cuda.synchronize()
+    return att
+
+
+def oracle_plan(wl, inp, h, a2v=True, **over):
+    kw = dict(top_k=wl.top_k, top_p=wl.top_p, min_edge_log2=wl.min_edge_log2)
+    kw.update(over)
+    return oracle.plan_head(wl.T, wl.H, wl.W, inp["q"][:, h], inp["k"][:, h], inp["v"][:, h],
+                            inp["a2v"] if a2v else None, **kw)
+
+
+class PlanReport(dict):
+    pass
+
+
+def compare_plan(views, h, op: oracle.HeadPlan, check_scores=True) -> PlanReport:
+    """Asserts the GPU plan of head h equals the oracle's; returns counts."""
+    rep = PlanReport()
+    zs = to_np(views["zone_stats"][h])
+    np.testing.assert_allclose(zs, op.vstats, rtol=1e-9, atol=1e-12)
+    gshape = to_np(views["zone_shape"][h])
+    near = (op.zone_diag[:, 9] < MARGIN) | (op.zone_diag[:, 10] < MARGIN)
+    rep["near_tie_zones"] = int(near.sum())
+    mism = gshape != op.shape
+    assert not np.any(mism & ~near), f"zone shapes differ at {np.nonzero(mism & ~near)[0][:10]}"
+    rep["shape_mismatch_near_tie"] = int(mism.sum())
+    if mism.any():
+        rep["downstream_skipped"] = True
+        return rep
+    nb = op.nb
+    assert int(views["zone_block"][h, -1]) == nb
+    np.testing.assert_array_equal(to_np(views["perm"][h]), op.perm)
+    np.testing.assert_array_equal(to_np(views["inv_perm"][h]), op.inv)
+    np.testing.assert_array_equal(to_np(views["block_start"][h, :nb]), op.bstart)
+    np.testing.assert_array_equal(to_np(views["block_size"][h, :nb]), op.bsize)
+    ub = to_np(views["unit_block"][h])
+    np.testing.assert_array_equal(ub, op.bof[::64])
+    np.testing.assert_allclose(to_np(views["qbar"][h, :nb]), op.qbar, rtol=1e-5, atol=2e-6)
+    np.testing.assert_allclose(to_np(views["kbar"][h, :nb]), op.kbar, rtol=1e-5, atol=2e-6)
+    rep["nb"] = nb
+    return rep
+
+
+def compare_selection(views, h, op: oracle.HeadPlan, top_p, scores=None):
+    """Returns (rows whose selection matched exactly, excluded-block count, nnz)."""
+    nb = op.nb
+    cnt = to_np(views["sel_count"][h, :nb])
+    cols = to_np(views["csr_col"][h, :nb, :nb])
+    if scores is not None:
+        np.testing.assert_allclose(scores[:nb, :nb], op.s, atol=SEL_TOL)
+    exact = np.zeros(nb, dtype=bool)
+    excluded = 0
+    for i in range(nb):
+        g = cols[i, :cnt[i]]
+        assert np.all(np.diff(g) > 0), f"row {i} not ascending"
+        o_ = op.cols[i, :op.count[i]]
+        if cnt[i] == op.count[i] and np.array_equal(g, o_):
+            exact[i] = True
+            continue
+        diff = np.setxor1d(g, o_)
+        order = np.lexsort((np.arange(nb), -op.P[i]))
+        pos = np.empty(nb, dtype=np.int64)
+        pos[order] = np.arange(nb)
+        cum = np.concatenate([[0.0], np.cumsum(op.P[i][order])])
+        s_cut = op.s[i, order[op.count[i] - 1]]
+        for j in diff:
+            near_logit = abs(op.s[i, j] - s_cut) <= SEL_TOL
+            near_mass = abs(cum[pos[j]] - top_p) <= SEL_TOL
+            assert near_logit or near_mass, (
+                f"head {h} row {i}: block {j} differs (logit {op.s[i, j]:.7f}, cut "
+                f"{s_cut:.7f}, mass before {cum[pos[j]]:.7f})")
+            excluded += 1
+    # the transpose lists
+    tc = to_np(views["csc_count"][h, :nb])
+    tr = to_np(views["csc_row"][h, :nb, :nb])
+    sel = np.zeros((nb, nb), dtype=bool)
+    for i in range(nb):
+        sel[i, cols[i, :cnt[i]]] = True
+    for j in range(nb):
+        np.testing.assert_array_equal(tr[j, :tc[j]], np.nonzero(sel[:, j])[0])
+    return exact, excluded, int(cnt.sum())
+
+
+def rows_of_exact_blocks(op: oracle.HeadPlan, exact):
+    """Token indices whose query block's selection matched exactly."""
+    tok_blk = np.empty(len(op.perm), dtype=np.int64)
+    tok_blk[op.perm] = op.bof
+    return exact[tok_blk]

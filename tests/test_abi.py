@@ -1,0 +1,76 @@
+"""The C ABI of libprism.so: it loads, exports every entry point include/prism.h declares,
+and rejects bad configurations with status codes before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_block_sparse_stats_amd as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "prism.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(prism_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(P.LIB_PATH):
+        pytest.skip("libprism.so not built")
+    return P.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(P.EXPORTS)
+    handle = ctypes.CDLL(P.LIB_PATH)
+    for n in names:
+        assert hasattr(handle, n), n
+
+
+def test_layout_and_workspace(lib):
+    cfg = P.make_config(8, 16, 16, 2, 64, "f32", min_edge_log2=0, top_k=4, top_p=0.9)
+    L = P.plan_layout(cfg)
+    assert L.N == 2048 and L.Z == 4 and L.nb_max == 32
+    offs = [getattr(L, f) for f in P._LAYOUT_FIELDS if f != "total"]
+    assert all(o % 256 == 0 for o in offs)
+    assert len(set(offs)) == len(offs)
+    assert P.workspace_bytes(cfg) == L.total >= max(offs)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(T=12), -2), (dict(H=0), -1), (dict(head_dim=96), -2), (dict(dtype=7), -2),
+    (dict(min_edge_log2=2), -1), (dict(top_k=-1), -1), (dict(top_p=float("nan")), -1),
+    (dict(T=4096, H=1024, W=1024), -2),
+])
+def test_rejected_configs(lib, over, code):
+    base = dict(T=8, H=16, W=16, num_heads=2, head_dim=128, dtype=P.BF16, min_edge_log2=1,
+                top_k=8, top_p=0.9, tau128=0.5, tau256=0.25, eps=1e-6, score_scale=0.0,
+                softmax_scale=0.0)
+    base.update(over)
+    cfg = P.PrismConfig(**base)
+    assert lib.prism_workspace_bytes(ctypes.byref(cfg)) == 0
+    out = P.PrismLayout()
+    assert lib.prism_plan_layout(ctypes.byref(cfg), ctypes.byref(out)) == code
+    # the same check runs first in every entry point: nothing is launched
+    dummy = ctypes.c_void_p(16)
+    assert lib.prism_plan(ctypes.byref(cfg), dummy, dummy, dummy, None, dummy, 1 << 40,
+                          None) == code
+    assert lib.prism_attn_fwd(ctypes.byref(cfg), dummy, 1 << 40, dummy, dummy, None) == code
+    assert lib.prism_last_error().decode() != ""
+
+
+def test_null_and_small_workspace(lib):
+    cfg = P.make_config(8, 16, 16, 2, 128, "bf16")
+    d = ctypes.c_void_p(256)
+    assert lib.prism_plan(ctypes.byref(cfg), None, d, d, None, d, 1 << 40, None) == -1
+    need = lib.prism_workspace_bytes(ctypes.byref(cfg))
+    assert lib.prism_plan(ctypes.byref(cfg), d, d, d, None, d, need - 1, None) == -3
+    assert lib.prism_attn_fwd(ctypes.byref(cfg), d, need - 1, d, d, None) == -3
+    assert lib.prism_attn_bwd(ctypes.byref(cfg), d, need, d, d, None, d, None) == -1
+    assert lib.prism_attn_bwd(ctypes.byref(cfg), d, need - 1, d, d, d, d, None) == -3
+    assert lib.prism_status_string(-3) == b"workspace too small"
