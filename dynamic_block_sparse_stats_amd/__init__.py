@@ -61,7 +61,10 @@ class PrismError(RuntimeError):
 
 _lib = None
 EXPORTS = ["prism_workspace_bytes", "prism_plan_layout", "prism_plan", "prism_attn_fwd",
-           "prism_attn_bwd", "prism_status_string", "prism_last_error"]
+           "prism_attn_bwd", "prism_status_string", "prism_last_error", "prism_trace_enable",
+           "prism_trace_read", "prism_stage_name"]
+STAGES = ["audio_stats", "zone_stats", "quantize", "gather", "tiles", "scores", "select",
+          "attn_fwd", "bwd_prep", "bwd_dkdv", "bwd_dq"]
 
 
 def lib():
@@ -87,6 +90,12 @@ def lib():
         L.prism_status_string.restype = ctypes.c_char_p
         L.prism_last_error.argtypes = []
         L.prism_last_error.restype = ctypes.c_char_p
+        L.prism_trace_enable.argtypes = [ctypes.c_int]
+        L.prism_trace_enable.restype = ctypes.c_int
+        L.prism_trace_read.argtypes = [vp, vp]
+        L.prism_trace_read.restype = ctypes.c_int
+        L.prism_stage_name.argtypes = [ctypes.c_int]
+        L.prism_stage_name.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -172,6 +181,21 @@ def attn_bwd(cfg, ws, dout, dq, dk, dv, stream=None):
     _check(lib().prism_attn_bwd(ctypes.byref(cfg), _ptr(ws), ws.numel() * ws.element_size(),
                                 _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)),
            "prism_attn_bwd")
+
+
+def trace_enable(on: bool = True):
+    """Per-stage HIP-event tracing inside the library (see prism_trace_enable)."""
+    _check(lib().prism_trace_enable(1 if on else 0), "prism_trace_enable")
+
+
+def trace_read() -> dict:
+    """{stage: (milliseconds, launches)} accumulated since the last read."""
+    n = len(STAGES)
+    ms = (ctypes.c_double * n)()
+    calls = (ctypes.c_int * n)()
+    _check(lib().prism_trace_read(ctypes.addressof(ms), ctypes.addressof(calls)),
+           "prism_trace_read")
+    return {lib().prism_stage_name(i).decode(): (ms[i], calls[i]) for i in range(n)}
 
 
 def plan_views(cfg, ws) -> dict:

@@ -95,7 +95,10 @@ __global__ void __launch_bounds__(256)
 }
 
 // ============================================================================ dK / dV (bf16)
-template <int NW>
+// Four waves per workgroup; a 64-key tile (a 64-token block) leaves waves 2-3 to help stage
+// the query units only.
+constexpr int NW = 4;
+
 __global__ void __launch_bounds__(NW * 64)
     attn_dkdv_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
                           const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
@@ -115,7 +118,8 @@ __global__ void __launch_bounds__(NW * 64)
   const int ntiles = *tile_count;
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int2 tl = tiles[t];
-    const int h = tl.x, u0 = tl.y;
+    const int h = tl.x, u0 = tl.y & (kTile64 - 1);
+    const bool active = !(tl.y & kTile64) || wave < 2;
     const int jblk = unit_blk[(size_t)h * U + u0];
     const int nq = csc_count[(size_t)h * nb_max + jblk];
     const int *qlist = csc_row + ((size_t)h * nb_max + jblk) * nb_max;
@@ -123,7 +127,7 @@ __global__ void __launch_bounds__(NW * 64)
     // this wave's 32 keys: K^T and V^T as B operands (lane = key, 8 dims per k-step)
     const int key0 = u0 * kUnit + wave * 32;
     bf16x8 kreg[8], vreg[8];
-    {
+    if (active) {
       const uint16_t *kr = kp + ((size_t)h * N + key0 + l32) * kDB + 8 * hh;
       const uint16_t *vr = vp + ((size_t)h * N + key0 + l32) * kDB + 8 * hh;
 #pragma unroll
@@ -159,6 +163,7 @@ __global__ void __launch_bounds__(NW * 64)
               *reinterpret_cast<const u32x4 *>(g3);
         }
         __syncthreads();
+        if (!active) continue;
         const float *lrow = lsep + (size_t)h * N + (size_t)u * kUnit;
         const float *drow = delta + (size_t)h * N + (size_t)u * kUnit;
         bf16x8 pb[4], db[4];
@@ -210,6 +215,7 @@ __global__ void __launch_bounds__(NW * 64)
       }
     }
     // epilogue: C layout lane = key l32, register v -> d = 32dt + (v/4)*8 + 4hh + v%4
+    if (!active) continue;
     const int token = perm[(size_t)h * N + key0 + l32];
     uint16_t *krow = dk + ((size_t)token * heads + h) * kDB;
     uint16_t *vrow = dv + ((size_t)token * heads + h) * kDB;
@@ -234,7 +240,6 @@ __global__ void __launch_bounds__(NW * 64)
 }
 
 // ============================================================================ dQ (bf16)
-template <int NW>
 __global__ void __launch_bounds__(NW * 64)
     attn_dq_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
                         const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
@@ -253,14 +258,16 @@ __global__ void __launch_bounds__(NW * 64)
   const int ntiles = *tile_count;
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int2 tl = tiles[t];
-    const int h = tl.x, u0 = tl.y;
+    const int h = tl.x, u0 = tl.y & (kTile64 - 1);
+    const bool active = !(tl.y & kTile64) || wave < 2;
     const int blk = unit_blk[(size_t)h * U + u0];
     const int ncols = sel_count[(size_t)h * nb_max + blk];
     const int *cols = csr_col + ((size_t)h * nb_max + blk) * nb_max;
     const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
     const int row0 = u0 * kUnit + wave * 32;
     bf16x8 qreg[8], doreg[8];
-    {
+    float lse2 = 0.f, dlt = 0.f;
+    if (active) {
       const uint16_t *qr = qp + ((size_t)h * N + row0 + l32) * kDB + 8 * hh;
       const uint16_t *dr = dop + ((size_t)h * N + row0 + l32) * kDB + 8 * hh;
 #pragma unroll
@@ -269,8 +276,10 @@ __global__ void __launch_bounds__(NW * 64)
         doreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(dr + 16 * kk));
       }
     }
-    const float lse2 = lsep[(size_t)h * N + row0 + l32] * 1.4426950408889634f;
-    const float dlt = delta[(size_t)h * N + row0 + l32];
+    if (active) {
+      lse2 = lsep[(size_t)h * N + row0 + l32] * 1.4426950408889634f;
+      dlt = delta[(size_t)h * N + row0 + l32];
+    }
     f32x16 acc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
@@ -291,6 +300,7 @@ __global__ void __launch_bounds__(NW * 64)
               *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint8_t *>(kpt) + ub + 16 * q);
         }
         __syncthreads();
+        if (!active) continue;
         bf16x8 db[4];
 #pragma unroll
         for (int a = 0; a < 2; ++a) {  // keys 32a .. 32a + 31
@@ -325,6 +335,7 @@ __global__ void __launch_bounds__(NW * 64)
         }
       }
     }
+    if (!active) continue;
     const int token = perm[(size_t)h * N + row0 + l32];
     uint16_t *qrow = dq + ((size_t)token * heads + h) * kDB;
 #pragma unroll
@@ -489,35 +500,37 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
   dim3 ugrid(d.U, d.heads);
   if (d.dtype == PRISM_BF16) {
     typedef uint16_t T;
-    hipLaunchKernelGGL((bwd_prep_kernel<T, 128, true>), ugrid, dim3(256), 0, s, d.N, d.heads,
+    {
+      TraceScope tr(PRISM_STAGE_BWD_PREP, s);
+      hipLaunchKernelGGL((bwd_prep_kernel<T, 128, true>), ugrid, dim3(256), 0, s, d.N, d.heads,
                        perm, (const T *)dout, o32p, (T *)(ws + L.dop), (T *)(ws + L.dopt),
                        delta);
+    }
     const int *counters = (const int *)(ws + L.counters);
     const float sl2e = scale * 1.4426950408889634f;
-    const int max128 = d.heads * d.U / 2, max64 = d.heads * d.U;
-    const int g128 = max128 < 4096 ? (max128 > 0 ? max128 : 1) : 4096;
-    const int g64 = max64 < 4096 ? (max64 > 0 ? max64 : 1) : 4096;
+    const int maxt = d.heads * d.U;
+    const int grid = maxt < 8192 ? maxt : 8192;
     const T *qp = (const T *)(ws + L.qp), *kp = (const T *)(ws + L.kp),
             *vp = (const T *)(ws + L.vp), *qpt = (const T *)(ws + L.qpt),
             *kpt = (const T *)(ws + L.kpt), *dop = (const T *)(ws + L.dop),
             *dopt = (const T *)(ws + L.dopt);
-    const int2 *t128 = (const int2 *)(ws + L.tiles128), *t64 = (const int2 *)(ws + L.tiles64);
-    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<4>), dim3(g128), dim3(256), 0, s, d.N, d.U,
-                       d.nb_max, d.heads, t128, counters, qp, qpt, kp, vp, dop, dopt, lsep,
-                       delta, unit_blk, bstart, bsize, tcnt, trows, perm, scale, sl2e, (T *)dk,
-                       (T *)dv);
-    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<2>), dim3(g64), dim3(128), 0, s, d.N, d.U,
-                       d.nb_max, d.heads, t64, counters + 1, qp, qpt, kp, vp, dop, dopt, lsep,
-                       delta, unit_blk, bstart, bsize, tcnt, trows, perm, scale, sl2e, (T *)dk,
-                       (T *)dv);
-    hipLaunchKernelGGL((attn_dq_bf16_kernel<4>), dim3(g128), dim3(256), 0, s, d.N, d.U,
-                       d.nb_max, d.heads, t128, counters, qp, kp, kpt, vp, dop, lsep, delta,
-                       unit_blk, bstart, bsize, cnt, cols, perm, scale, sl2e, (T *)dq);
-    hipLaunchKernelGGL((attn_dq_bf16_kernel<2>), dim3(g64), dim3(128), 0, s, d.N, d.U,
-                       d.nb_max, d.heads, t64, counters + 1, qp, kp, kpt, vp, dop, lsep, delta,
-                       unit_blk, bstart, bsize, cnt, cols, perm, scale, sl2e, (T *)dq);
+    const int2 *tiles = (const int2 *)(ws + L.tiles);
+    {
+      TraceScope tr(PRISM_STAGE_BWD_DKDV, s);
+      hipLaunchKernelGGL(attn_dkdv_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, d.N, d.U,
+                         d.nb_max, d.heads, tiles, counters, qp, qpt, kp, vp, dop, dopt, lsep,
+                         delta, unit_blk, bstart, bsize, tcnt, trows, perm, scale, sl2e,
+                         (T *)dk, (T *)dv);
+    }
+    {
+      TraceScope tr(PRISM_STAGE_BWD_DQ, s);
+      hipLaunchKernelGGL(attn_dq_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, d.N, d.U,
+                         d.nb_max, d.heads, tiles, counters, qp, kp, kpt, vp, dop, lsep, delta,
+                         unit_blk, bstart, bsize, cnt, cols, perm, scale, sl2e, (T *)dq);
+    }
   } else {
     typedef float T;
+    TraceScope tr(PRISM_STAGE_BWD_DKDV, s);
     const T *qp = (const T *)(ws + L.qp), *kp = (const T *)(ws + L.kp),
             *vp = (const T *)(ws + L.vp), *dop = (const T *)(ws + L.dop);
     if (d.D == 64) {

@@ -5,9 +5,9 @@
 // block 4, taken in turn; xyznot review, "Метод" item 3).
 //
 // bfloat16 path, head_dim 128, gfx950 MFMA v_mfma_f32_32x32x16_bf16:
-//   * a workgroup owns a query tile of 32 * NW rows inside one block (NW = 4 for blocks of
-//     128 or 256 tokens, NW = 2 for 64-token blocks); each wave keeps its 32 query rows in
-//     registers as the B operand;
+//   * a workgroup (4 waves) owns a query tile inside one block: 128 rows for blocks of 128
+//     or 256 tokens, 64 rows for 64-token blocks (then waves 2-3 only help stage K/V);
+//     each wave keeps its 32 query rows in registers as the B operand;
 //   * the key units of the block's selected key blocks stream through LDS, double
 //     buffered: K as [64 keys][128] (row-major) and V as [128][64 keys] (the per-unit
 //     transposed copy written by the planner), both XOR-swizzled by 16-byte chunk so the
@@ -61,7 +61,8 @@ struct UnitCursor {
   }
 };
 
-template <int NW>
+constexpr int NW = 4;
+
 __global__ void __launch_bounds__(NW * 64)
     attn_fwd_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
                          const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
@@ -81,7 +82,8 @@ __global__ void __launch_bounds__(NW * 64)
 
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int2 tl = tiles[t];
-    const int h = tl.x, u0 = tl.y;
+    const int h = tl.x, u0 = tl.y & (kTile64 - 1);
+    const bool active = !(tl.y & kTile64) || wave < 2;
     const int blk = unit_blk[(size_t)h * U + u0];
     const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
     UnitCursor cur;
@@ -92,9 +94,11 @@ __global__ void __launch_bounds__(NW * 64)
     const int row0 = u0 * kUnit + wave * 32;
     const uint16_t *qrow = qp + ((size_t)h * N + row0 + l32) * kD + 8 * hh;
     bf16x8 qreg[8];
+    if (active) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      qreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 16 * kk));
+      for (int kk = 0; kk < 8; ++kk)
+        qreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 16 * kk));
+    }
 
     const uint8_t *kbase = reinterpret_cast<const uint8_t *>(kp) + (size_t)h * N * kD * 2;
     const uint8_t *vbase = reinterpret_cast<const uint8_t *>(vpt) + (size_t)h * N * kD * 2;
@@ -132,64 +136,67 @@ __global__ void __launch_bounds__(NW * 64)
       const bool more = cur.next();
       if (more) gload(cur.unit());
       const uint8_t *Kt = lds[buf][0], *Vt = lds[buf][1];
-      // S^T for keys 0-31 (a = 0) and 32-63 (a = 1)
-      f32x16 s[2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        s[a] = f32x16{};
-        const int r = 32 * a + l32;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          bf16x8 ka = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4 *>(Kt + k_lds_off(r, 2 * kk + hh)));
-          s[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[kk], s[a], 0, 0, 0);
+      if (active) {
+        // S^T for keys 0-31 (a = 0) and 32-63 (a = 1)
+        f32x16 s[2];
+  #pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          s[a] = f32x16{};
+          const int r = 32 * a + l32;
+  #pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            bf16x8 ka = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4 *>(Kt + k_lds_off(r, 2 * kk + hh)));
+            s[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[kk], s[a], 0, 0, 0);
+          }
         }
-      }
-      // online softmax, log2 domain; lane = query l32, keys split over the two half waves
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          s[a][v] *= scale_log2e;
-          tmax = fmaxf(tmax, s[a][v]);
+        // online softmax, log2 domain; lane = query l32, keys split over the two half waves
+        float tmax = -INFINITY;
+  #pragma unroll
+        for (int a = 0; a < 2; ++a)
+  #pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            s[a][v] *= scale_log2e;
+            tmax = fmaxf(tmax, s[a][v]);
+          }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float mnew = fmaxf(m, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        m = mnew;
+        float psum = 0.f;
+        bf16x8 pb[4];
+  #pragma unroll
+        for (int g = 0; g < 4; ++g)
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float p = __builtin_amdgcn_exp2f(s[g >> 1][8 * (g & 1) + e] - mnew);
+            psum += p;
+            pb[g][e] = (__bf16)p;
+          }
+        lsum = lsum * alpha + psum;
+  #pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+  #pragma unroll
+          for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+        // O^T[d][q] += V^T[d][keys] P^T[keys][q]
+  #pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int d = 32 * dt + l32;
+  #pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            bf16x8 va = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4 *>(Vt + vt_lds_off(d, 2 * g + hh)));
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[g], o[dt], 0, 0, 0);
+          }
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mnew = fmaxf(m, tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      m = mnew;
-      float psum = 0.f;
-      bf16x8 pb[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float p = __builtin_amdgcn_exp2f(s[g >> 1][8 * (g & 1) + e] - mnew);
-          psum += p;
-          pb[g][e] = (__bf16)p;
-        }
-      lsum = lsum * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
-      // O^T[d][q] += V^T[d][keys] P^T[keys][q]
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int d = 32 * dt + l32;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x8 va = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4 *>(Vt + vt_lds_off(d, 2 * g + hh)));
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[g], o[dt], 0, 0, 0);
-        }
-      }
+      }  // active
       if (!more) break;
       lstore(buf ^ 1);
       __syncthreads();
       buf ^= 1;
     }
     // epilogue
+    if (!active) continue;
     const float ltot = lsum + __shfl_xor(lsum, 32, 64);
     const float inv = 1.f / ltot;
     const int prow = row0 + l32;
@@ -300,19 +307,14 @@ hipError_t launch_attn_fwd(const Dims &d, float scale, uint8_t *ws, const Layout
   const int *cols = (const int *)(ws + L.pub.csr_col);
   const int *perm = (const int *)(ws + L.pub.perm);
   float *o32p = (float *)(ws + L.o32p), *lsep = (float *)(ws + L.lsep);
+  TraceScope tr(PRISM_STAGE_ATTN_FWD, s);
   if (d.dtype == PRISM_BF16) {
     const int *counters = (const int *)(ws + L.counters);
     const float sl2e = scale * 1.4426950408889634f;
-    const int max128 = d.heads * d.U / 2, max64 = d.heads * d.U;
-    const int g128 = max128 < 4096 ? (max128 > 0 ? max128 : 1) : 4096;
-    const int g64 = max64 < 4096 ? (max64 > 0 ? max64 : 1) : 4096;
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<4>), dim3(g128), dim3(256), 0, s, d.N, d.U,
-                       d.nb_max, d.heads, (const int2 *)(ws + L.tiles128), counters,
-                       (const uint16_t *)(ws + L.qp), (const uint16_t *)(ws + L.kp),
-                       (const uint16_t *)(ws + L.vpt), unit_blk, bstart, bsize, cnt, cols, perm,
-                       sl2e, (uint16_t *)o, lse, o32p, lsep);
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<2>), dim3(g64), dim3(128), 0, s, d.N, d.U,
-                       d.nb_max, d.heads, (const int2 *)(ws + L.tiles64), counters + 1,
+    const int maxt = d.heads * d.U;
+    const int grid = maxt < 8192 ? maxt : 8192;
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, d.N, d.U,
+                       d.nb_max, d.heads, (const int2 *)(ws + L.tiles), counters,
                        (const uint16_t *)(ws + L.qp), (const uint16_t *)(ws + L.kp),
                        (const uint16_t *)(ws + L.vpt), unit_blk, bstart, bsize, cnt, cols, perm,
                        sl2e, (uint16_t *)o, lse, o32p, lsep);

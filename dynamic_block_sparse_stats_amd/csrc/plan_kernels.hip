@@ -55,6 +55,7 @@ __global__ void __launch_bounds__(64) audio_stats_kernel(int H, int W, int nzh, 
 }
 
 hipError_t launch_audio_stats(const Dims &d, const float *a2v, double *astat, hipStream_t s) {
+  TraceScope tr(PRISM_STAGE_AUDIO_STATS, s);
   hipLaunchKernelGGL(audio_stats_kernel, dim3(d.Z), dim3(64), 0, s, d.H, d.W, d.nzh, d.nzw,
                      a2v, astat);
   return hipGetLastError();
@@ -169,6 +170,7 @@ __global__ void __launch_bounds__(64) zone_stats_kernel(int H, int W, int heads,
 }
 
 hipError_t launch_zone_stats(const Dims &d, const void *v, double *zstat, hipStream_t s) {
+  TraceScope tr(PRISM_STAGE_ZONE_STATS, s);
   dim3 grid(d.Z, d.heads);
   if (d.dtype == PRISM_BF16) {
     hipLaunchKernelGGL((zone_stats_kernel<uint16_t, 128>), grid, dim3(64), 0, s, d.H, d.W,
@@ -331,6 +333,7 @@ __global__ void __launch_bounds__(kQuantThreads)
 hipError_t launch_quantize(const Dims &d, const prism_config *cfg, const double *zstat,
                            const double *astat, bool have_audio, uint8_t *ws, const Layout &L,
                            hipStream_t s) {
+  TraceScope tr(PRISM_STAGE_QUANTIZE, s);
   hipLaunchKernelGGL(quantize_kernel, dim3(d.heads), dim3(kQuantThreads), 0, s, d.Z, d.nb_max,
                      zstat, astat, have_audio ? 1 : 0, (double)cfg->tau128,
                      (double)cfg->tau256, cfg->eps, cfg->min_edge_log2,
@@ -475,6 +478,7 @@ __global__ void __launch_bounds__(256)
 
 hipError_t launch_gather(const Dims &d, const void *q, const void *k, const void *v,
                          uint8_t *ws, const Layout &L, hipStream_t s) {
+  TraceScope tr(PRISM_STAGE_GATHER, s);
   dim3 grid(d.Z, d.heads);
   const int *zshape = (const int *)(ws + L.pub.zone_shape);
   const int *zblock = (const int *)(ws + L.pub.zone_block);
@@ -508,15 +512,15 @@ hipError_t launch_gather(const Dims &d, const void *q, const void *k, const void
 // Attention work items: 128-row tiles inside blocks of 128 or 256 tokens and 64-row tiles
 // for 64-token blocks (the 64-token atomic unit of the digest's training section; 128- and
 // 256-token blocks are 2 and 4 units).  The same tiles serve as query tiles (forward, dQ)
-// and key tiles (dK/dV) because Q, K and V share one partition.  Order inside a list is
-// immaterial to the results.
+// and key tiles (dK/dV) because Q, K and V share one partition.  Entry (head, first unit |
+// kTile64 flag).  Order inside the list is immaterial to the results.
 __global__ void zero_ints_kernel(int *p, int n) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
 }
 
-__global__ void tiles_kernel(int heads, int Z, const int *__restrict__ zshape, int2 *t128,
-                             int2 *t64, int *counters) {
+__global__ void tiles_kernel(int heads, int Z, const int *__restrict__ zshape, int2 *tiles,
+                             int *counters) {
   int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= heads * Z) return;
   int h = idx / Z, m = idx % Z;
@@ -524,19 +528,20 @@ __global__ void tiles_kernel(int heads, int Z, const int *__restrict__ zshape, i
   int S = ((code >> 4) & 3) + ((code >> 2) & 3) + (code & 3);
   if (S >= 7) {
     int at = atomicAdd(&counters[0], 4);
-    for (int s = 0; s < 4; ++s) t128[at + s] = make_int2(h, 8 * m + 2 * s);
+    for (int s = 0; s < 4; ++s) tiles[at + s] = make_int2(h, 8 * m + 2 * s);
   } else {
-    int at = atomicAdd(&counters[1], 8);
-    for (int s = 0; s < 8; ++s) t64[at + s] = make_int2(h, 8 * m + s);
+    int at = atomicAdd(&counters[0], 8);
+    for (int s = 0; s < 8; ++s) tiles[at + s] = make_int2(h, (8 * m + s) | kTile64);
   }
 }
 
 hipError_t launch_tiles(const Dims &d, uint8_t *ws, const Layout &L, hipStream_t s) {
+  TraceScope tr(PRISM_STAGE_TILES, s);
   hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(64), 0, s, (int *)(ws + L.counters), 16);
   int n = d.heads * d.Z;
   hipLaunchKernelGGL(tiles_kernel, dim3((n + 255) / 256), dim3(256), 0, s, d.heads, d.Z,
-                     (const int *)(ws + L.pub.zone_shape), (int2 *)(ws + L.tiles128),
-                     (int2 *)(ws + L.tiles64), (int *)(ws + L.counters));
+                     (const int *)(ws + L.pub.zone_shape), (int2 *)(ws + L.tiles),
+                     (int *)(ws + L.counters));
   return hipGetLastError();
 }
 

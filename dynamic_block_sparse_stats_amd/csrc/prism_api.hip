@@ -3,11 +3,62 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "prism_internal.h"
 
 namespace prism {
+
+// ---------------------------------------------------------------------------- tracing
+namespace {
+struct TraceRecord {
+  int stage;
+  hipEvent_t start, end;
+};
+std::mutex g_trace_mu;
+bool g_trace_on = false;
+std::vector<TraceRecord> g_records;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void drop_records() {
+  for (auto &r : g_records) {
+    hipEventSynchronize(r.end);
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.end);
+  }
+  g_records.clear();
+}
+}  // namespace
+
+TraceScope::TraceScope(int st, hipStream_t s) : stage(st), stream(s), start(nullptr) {
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  if (!g_trace_on) return;
+  hipEvent_t e = take_event();
+  if (e && hipEventRecord(e, s) == hipSuccess) start = e;
+}
+
+TraceScope::~TraceScope() {
+  if (!start) return;
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  hipEvent_t e = take_event();
+  if (e && hipEventRecord(e, stream) == hipSuccess)
+    g_records.push_back(TraceRecord{stage, (hipEvent_t)start, e});
+  else
+    g_event_pool.push_back((hipEvent_t)start);
+}
 
 static thread_local std::string g_last_error;
 
@@ -105,8 +156,7 @@ Layout make_layout(const Dims &d) {
   L.pub.scores = take(NB * NB * sizeof(float));
   L.sel_bits = take(H * NB * d.words * sizeof(uint32_t));
   L.csc_bits = take(H * NB * d.words * sizeof(uint32_t));
-  L.tiles128 = take(H * U * sizeof(int2));
-  L.tiles64 = take(H * U * sizeof(int2));
+  L.tiles = take(H * U * sizeof(int2));
   L.counters = take(16 * sizeof(int));
   L.delta = take(H * N * sizeof(float));
   L.lsep = take(H * N * sizeof(float));
@@ -238,5 +288,40 @@ const char *prism_status_string(int status) {
 }
 
 const char *prism_last_error(void) { return g_last_error.c_str(); }
+
+prism_status prism_trace_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  drop_records();
+  g_trace_on = on != 0;
+  return PRISM_OK;
+}
+
+prism_status prism_trace_read(double *ms, int *calls) {
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  if (ms)
+    for (int i = 0; i < PRISM_STAGE_COUNT; ++i) ms[i] = 0.0;
+  if (calls)
+    for (int i = 0; i < PRISM_STAGE_COUNT; ++i) calls[i] = 0;
+  prism_status st = PRISM_OK;
+  for (auto &r : g_records) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.end) != hipSuccess ||
+        hipEventElapsedTime(&t, r.start, r.end) != hipSuccess) {
+      st = fail(PRISM_ERR_HIP, "trace event query failed");
+      continue;
+    }
+    if (ms) ms[r.stage] += t;
+    if (calls) calls[r.stage] += 1;
+  }
+  drop_records();
+  return st;
+}
+
+const char *prism_stage_name(int stage) {
+  static const char *names[PRISM_STAGE_COUNT] = {
+      "audio_stats", "zone_stats", "quantize", "gather", "tiles", "scores",
+      "select",      "attn_fwd",   "bwd_prep", "bwd_dkdv", "bwd_dq"};
+  return stage >= 0 && stage < PRISM_STAGE_COUNT ? names[stage] : "unknown";
+}
 
 }  // extern "C"

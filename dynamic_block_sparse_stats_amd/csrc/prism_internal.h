@@ -14,6 +14,17 @@ constexpr int kZone = 8;       // macro-zone edge along T, H, W
 constexpr int kZoneTok = 512;  // tokens per zone
 constexpr int kUnit = 64;      // tokens per atomic compute unit of the attention kernels
 constexpr int kMaxUnits = 65535;  // units per head (block indices fit 16 bits)
+constexpr int kTile64 = 1 << 30;  // tile flag: 64 rows (a 64-token block) instead of 128
+
+// Per-stage tracing: while enabled, records a HIP event pair on the stream around the
+// launches of a stage (prism_api.hip).
+struct TraceScope {
+  TraceScope(int stage, hipStream_t s);
+  ~TraceScope();
+  int stage;
+  hipStream_t stream;
+  void *start;
+};
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -36,8 +47,8 @@ struct Layout {
   size_t qpt, kpt, vpt;     // bf16 only: per-unit transposed [heads][U][D][64]
   size_t sel_bits;          // uint32 [heads][nb_max][words]
   size_t csc_bits;          // uint32 [heads][nb_max][words]
-  size_t tiles128, tiles64; // int2 [heads*U]: (head, first unit) of each query/key tile
-  size_t counters;          // int32 [16]: tile counts
+  size_t tiles;             // int2 [heads*U]: (head, first unit | kTile64) per query/key tile
+  size_t counters;          // int32 [16]: [0] = tile count
   size_t dop, dopt;         // bwd: gathered dout, row-major and per-unit transposed
   size_t o32p;              // fwd: float [heads][N][D] output in permuted order
   size_t lsep;              // fwd: float [heads][N] lse in permuted order

@@ -382,8 +382,12 @@ hipError_t launch_scores_select(const Dims &d, const prism_config *cfg, float sc
     int *cols = (int *)(ws + L.pub.csr_col) + (size_t)h * d.nb_max * d.nb_max;
     int *tcnt = (int *)(ws + L.pub.csc_count) + (size_t)h * d.nb_max;
     int *trows = (int *)(ws + L.pub.csc_row) + (size_t)h * d.nb_max * d.nb_max;
-    hipLaunchKernelGGL(score_gemm_kernel, dim3(gemm_grid), dim3(256), 0, s, d.D, d.nb_max, nbp,
-                       qbar, kbar, score_scale, scores);
+    {
+      TraceScope tr(PRISM_STAGE_SCORES, s);
+      hipLaunchKernelGGL(score_gemm_kernel, dim3(gemm_grid), dim3(256), 0, s, d.D, d.nb_max,
+                         nbp, qbar, kbar, score_scale, scores);
+    }
+    TraceScope tr(PRISM_STAGE_SELECT, s);
     if (small) {
       hipLaunchKernelGGL((select_kernel<256, 2>), dim3(sel_grid), dim3(256), 0, s, d.nb_max,
                          d.words, nbp, scores, cfg->top_k, cfg->top_p, bits, cnt, cols);

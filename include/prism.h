@@ -126,6 +126,32 @@ prism_status prism_attn_fwd(const prism_config *cfg, void *workspace, size_t wor
 prism_status prism_attn_bwd(const prism_config *cfg, void *workspace, size_t workspace_bytes,
                             const void *dout, void *dq, void *dk, void *dv, void *stream);
 
+/* Per-stage tracing with HIP events (for benchmarks and profiles; off by default).  While
+ * enabled, every entry point records a HIP event pair on the caller's stream around the
+ * kernel launches of each stage it runs; prism_trace_read waits for the recorded events,
+ * writes the summed milliseconds and the number of traced launches per stage into
+ * ms[PRISM_STAGE_COUNT] and calls[PRISM_STAGE_COUNT] (either may be NULL) and forgets
+ * them.  Enabling or disabling also forgets pending records.  Tracing state is
+ * process-wide; the stage names are those of prism_stage_name. */
+typedef enum {
+    PRISM_STAGE_AUDIO_STATS = 0, /* zone statistics of the A2V norm field */
+    PRISM_STAGE_ZONE_STATS,      /* zone statistics of V */
+    PRISM_STAGE_QUANTIZE,        /* g_d, tier, shape, block table */
+    PRISM_STAGE_GATHER,          /* permutation, permuted Q/K/V, block means */
+    PRISM_STAGE_TILES,           /* attention tile list */
+    PRISM_STAGE_SCORES,          /* block-score GEMM (per head) */
+    PRISM_STAGE_SELECT,          /* Top-k union Top-p, CSR and CSC lists (per head) */
+    PRISM_STAGE_ATTN_FWD,        /* sparse attention forward */
+    PRISM_STAGE_BWD_PREP,        /* dO gather and rowsum(dO * O) */
+    PRISM_STAGE_BWD_DKDV,        /* dK, dV */
+    PRISM_STAGE_BWD_DQ,          /* dQ */
+    PRISM_STAGE_COUNT
+} prism_stage;
+
+prism_status prism_trace_enable(int on);
+prism_status prism_trace_read(double *ms, int *calls);
+const char *prism_stage_name(int stage);
+
 /* Text of a status code. */
 const char *prism_status_string(int status);
 
