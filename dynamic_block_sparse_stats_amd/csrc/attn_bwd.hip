@@ -14,8 +14,9 @@
 //            key block (the transposed selection lists);
 //   dQ    -- one workgroup per query tile (32 queries per wave, Q and dO in registers),
 //            streaming the selected key units as in the forward pass.
-// Both MFMA passes recompute P from the stored lse; outputs go straight to the tokens'
-// original positions.
+// Both MFMA passes recompute P from the stored lse; the products with P and dS run on the
+// float16 MFMA (P scaled by 2^10, as in the forward) against the float16 transposed copies;
+// outputs go straight to the tokens' original positions.
 #include "prism_internal.h"
 
 namespace prism {
@@ -86,7 +87,8 @@ __global__ void __launch_bounds__(256)
         int pos0 = 32 * half + 8 * cc + e;
         int key0 = (pos0 & ~15) | swap23b(pos0 & 15);
         int key1 = ((pos0 + 1) & ~15) | swap23b((pos0 + 1) & 15);
-        pk[e >> 1] = (uint32_t)tile[key0 * D + dd] | ((uint32_t)tile[key1 * D + dd] << 16);
+        pk[e >> 1] = (uint32_t)bf16_to_f16_bits(tile[key0 * D + dd]) |
+                     ((uint32_t)bf16_to_f16_bits(tile[key1 * D + dd]) << 16);
       }
       *reinterpret_cast<u32x4 *>(dopt + ubase + (size_t)dd * kUnit + 32 * half + 8 * cc) =
           u32x4{pk[0], pk[1], pk[2], pk[3]};
@@ -166,7 +168,7 @@ __global__ void __launch_bounds__(NW * 64)
         if (!active) continue;
         const float *lrow = lsep + (size_t)h * N + (size_t)u * kUnit;
         const float *drow = delta + (size_t)h * N + (size_t)u * kUnit;
-        bf16x8 pb[4], db[4];
+        f16x8 pb[4], db[4];
 #pragma unroll
         for (int a = 0; a < 2; ++a) {  // queries 32a .. 32a + 31 of the unit
           f32x16 s = f32x16{}, dp = f32x16{};
@@ -177,8 +179,8 @@ __global__ void __launch_bounds__(NW * 64)
                 bf16x8, *reinterpret_cast<const u32x4 *>(&lds[0][rm_off(r, 2 * kk + hh)]));
             bf16x8 da = __builtin_bit_cast(
                 bf16x8, *reinterpret_cast<const u32x4 *>(&lds[1][rm_off(r, 2 * kk + hh)]));
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[kk], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[kk], dp, 0, 0, 0);
+            s = mfma_bf16(qa, kreg[kk], s);
+            dp = mfma_bf16(da, vreg[kk], dp);
           }
           // C layout: lane = key l32, register v = query 32a + (v/4)*8 + 4hh + v%4
 #pragma unroll
@@ -193,8 +195,8 @@ __global__ void __launch_bounds__(NW * 64)
               const float p = __builtin_amdgcn_exp2f(s[v] * scale_log2e - lq[e] * 1.4426950408889634f);
               const float ds = p * (dp[v] - dq4[e]);
               const int g = 2 * a + (v >> 3), slot = v & 7;
-              pb[g][slot] = (__bf16)p;
-              db[g][slot] = (__bf16)ds;
+              pb[g][slot] = (_Float16)(p * kPScale);
+              db[g][slot] = (_Float16)ds;
             }
           }
         }
@@ -204,12 +206,12 @@ __global__ void __launch_bounds__(NW * 64)
           const int d = 32 * dt + l32;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            bf16x8 doa = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4 *>(&lds[3][tr_off(d, 2 * g + hh)]));
-            bf16x8 qta = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4 *>(&lds[2][tr_off(d, 2 * g + hh)]));
-            dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(doa, pb[g], dvt[dt], 0, 0, 0);
-            dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta, db[g], dkt[dt], 0, 0, 0);
+            f16x8 doa = __builtin_bit_cast(
+                f16x8, *reinterpret_cast<const u32x4 *>(&lds[3][tr_off(d, 2 * g + hh)]));
+            f16x8 qta = __builtin_bit_cast(
+                f16x8, *reinterpret_cast<const u32x4 *>(&lds[2][tr_off(d, 2 * g + hh)]));
+            dvt[dt] = mfma_f16(doa, pb[g], dvt[dt]);
+            dkt[dt] = mfma_f16(qta, db[g], dkt[dt]);
           }
         }
       }
@@ -229,10 +231,11 @@ __global__ void __launch_bounds__(NW * 64)
                       ((uint32_t)f32_to_bf16(K[4 * v4 + 1] * scale) << 16);
         uint32_t k1 = (uint32_t)f32_to_bf16(K[4 * v4 + 2] * scale) |
                       ((uint32_t)f32_to_bf16(K[4 * v4 + 3] * scale) << 16);
-        uint32_t w0 = (uint32_t)f32_to_bf16(V[4 * v4]) |
-                      ((uint32_t)f32_to_bf16(V[4 * v4 + 1]) << 16);
-        uint32_t w1 = (uint32_t)f32_to_bf16(V[4 * v4 + 2]) |
-                      ((uint32_t)f32_to_bf16(V[4 * v4 + 3]) << 16);
+        const float vs = 1.f / kPScale;
+        uint32_t w0 = (uint32_t)f32_to_bf16(V[4 * v4] * vs) |
+                      ((uint32_t)f32_to_bf16(V[4 * v4 + 1] * vs) << 16);
+        uint32_t w1 = (uint32_t)f32_to_bf16(V[4 * v4 + 2] * vs) |
+                      ((uint32_t)f32_to_bf16(V[4 * v4 + 3] * vs) << 16);
         *reinterpret_cast<u32x2 *>(krow + d0) = u32x2{k0, k1};
         *reinterpret_cast<u32x2 *>(vrow + d0) = u32x2{w0, w1};
       }
@@ -301,7 +304,7 @@ __global__ void __launch_bounds__(NW * 64)
         }
         __syncthreads();
         if (!active) continue;
-        bf16x8 db[4];
+        f16x8 db[4];
 #pragma unroll
         for (int a = 0; a < 2; ++a) {  // keys 32a .. 32a + 31
           f32x16 s = f32x16{}, dp = f32x16{};
@@ -312,14 +315,14 @@ __global__ void __launch_bounds__(NW * 64)
                 bf16x8, *reinterpret_cast<const u32x4 *>(&lds[0][rm_off(r, 2 * kk + hh)]));
             bf16x8 va = __builtin_bit_cast(
                 bf16x8, *reinterpret_cast<const u32x4 *>(&lds[1][rm_off(r, 2 * kk + hh)]));
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[kk], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, doreg[kk], dp, 0, 0, 0);
+            s = mfma_bf16(ka, qreg[kk], s);
+            dp = mfma_bf16(va, doreg[kk], dp);
           }
           // lane = query, register v = key 32a + (v/4)*8 + 4hh + v%4
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const float p = __builtin_amdgcn_exp2f(s[v] * scale_log2e - lse2);
-            db[2 * a + (v >> 3)][v & 7] = (__bf16)(p * (dp[v] - dlt));
+            db[2 * a + (v >> 3)][v & 7] = (_Float16)(p * (dp[v] - dlt));
           }
         }
         // dQ^T[d][q] += K^T[d][keys] dS^T[keys][q]
@@ -328,9 +331,9 @@ __global__ void __launch_bounds__(NW * 64)
           const int d = 32 * dt + l32;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            bf16x8 kt = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4 *>(&lds[2][tr_off(d, 2 * g + hh)]));
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, db[g], acc[dt], 0, 0, 0);
+            f16x8 kt = __builtin_bit_cast(
+                f16x8, *reinterpret_cast<const u32x4 *>(&lds[2][tr_off(d, 2 * g + hh)]));
+            acc[dt] = mfma_f16(kt, db[g], acc[dt]);
           }
         }
       }

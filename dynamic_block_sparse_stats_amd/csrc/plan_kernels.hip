@@ -349,7 +349,8 @@ hipError_t launch_quantize(const Dims &d, const prism_config *cfg, const double 
 // blocks inside a zone in raster order of block coordinates, tokens inside a block in
 // raster order.  One workgroup per (zone, head) writes perm / inv_perm, copies the zone's
 // 512 rows of Q, K, V into the permuted row-major layout (and, for bfloat16, into a
-// per-64-token-unit transposed layout [D][64] used as the key-major MFMA operand), and
+// per-64-token-unit transposed float16 layout [D][64] used as the key-major MFMA operand
+// against float16 softmax weights), and
 // forms the float32 block means of Q and K (digest obstacles and selection sections).
 //
 // Transposed layout: within each group of 16 keys the stored order is
@@ -450,7 +451,8 @@ __global__ void __launch_bounds__(256)
             int pos0 = 32 * half + 8 * cc + e;
             int key0 = (pos0 & ~15) | swap23(pos0 & 15);
             int key1 = ((pos0 + 1) & ~15) | swap23((pos0 + 1) & 15);
-            pk[e >> 1] = (uint32_t)tile[key0 * D + dd] | ((uint32_t)tile[key1 * D + dd] << 16);
+            pk[e >> 1] = (uint32_t)bf16_to_f16_bits(tile[key0 * D + dd]) |
+                         ((uint32_t)bf16_to_f16_bits(tile[key1 * D + dd]) << 16);
           }
           *reinterpret_cast<u32x4 *>(dstt[x] + ubase + (size_t)dd * kUnit + 32 * half + 8 * cc) =
               u32x4{pk[0], pk[1], pk[2], pk[3]};

@@ -27,6 +27,7 @@ struct TraceScope {
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -44,12 +45,12 @@ struct Dims {
 struct Layout {
   prism_layout pub;
   size_t qp, kp, vp;        // permuted copies, row-major [heads][N][D]
-  size_t qpt, kpt, vpt;     // bf16 only: per-unit transposed [heads][U][D][64]
+  size_t qpt, kpt, vpt;     // bf16 path only: per-unit transposed float16 [heads][U][D][64]
   size_t sel_bits;          // uint32 [heads][nb_max][words]
   size_t csc_bits;          // uint32 [heads][nb_max][words]
   size_t tiles;             // int2 [heads*U]: (head, first unit | kTile64) per query/key tile
   size_t counters;          // int32 [16]: [0] = tile count
-  size_t dop, dopt;         // bwd: gathered dout, row-major and per-unit transposed
+  size_t dop, dopt;         // bwd: gathered dout, row-major (bf16) and transposed (f16)
   size_t o32p;              // fwd: float [heads][N][D] output in permuted order
   size_t lsep;              // fwd: float [heads][N] lse in permuted order
   size_t delta;             // bwd: float [heads][N] rowsum(dO * O) in permuted order
@@ -94,6 +95,28 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
+
+// Typed MFMA wrappers: the builtins accept any 8-element 16-bit vector silently, these do
+// not (32x32 output tile, K = 16; C/D layout: lane -> column lane % 32, register v -> row
+// (v / 4) * 8 + 4 * (lane / 32) + v % 4).
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// bfloat16 -> float16 bits (exact inside the float16 range; saturates beyond +-65504).
+__device__ __forceinline__ uint16_t bf16_to_f16_bits(uint16_t b) {
+  float f = fminf(fmaxf(bf16_to_f32(b), -65504.f), 65504.f);
+  _Float16 h = (_Float16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Softmax weights fed to the f16 MFMA are scaled by 2^10 so that weights down to 2^-24 of
+// the row maximum stay normal float16 numbers; the scale cancels in O = sum(p v) / sum(p).
+constexpr float kPShift = 10.f;
+constexpr float kPScale = 1024.f;
 
 template <typename T>
 __device__ __forceinline__ T *ws_ptr(uint8_t *ws, size_t off) {

@@ -1,0 +1,80 @@
+"""HIP path vs CPU oracle at the full workload sizes (720p, 1080p, 2K; 24 heads), in the
+launch configuration the benchmark times.  The oracle recomputes the plan of two heads in
+full and, for those heads, a seeded sample of output rows one by one; gradients are checked
+element by element with an upstream gradient that is zero except on a sample of query
+rows (then every dK/dV row the oracle sums is exact, and all others must be zero)."""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_block_sparse_stats_amd as P
+from dynamic_block_sparse_stats_amd import synth
+import oracle
+from parity import check_close, compare_plan, compare_selection, rows_of_exact_blocks, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _head_inputs(inp, h):
+    return {n: inp[n][:, h].double().cpu().numpy() for n in ("q", "k", "v")}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cid", [1, 2, 4])
+def test_fullsize(cid):
+    wl = synth.workload(cid)
+    print(f"\n== {wl.name}: generating inputs", flush=True)
+    inp = synth.make_inputs(wl, device="cuda", with_dout=False)
+    cfg = P.config_for(wl)
+    att = P.PrismAttention(cfg)
+    att.plan(inp["q"], inp["k"], inp["v"], inp["a2v"])
+    o, lse = att.forward()
+    torch.cuda.synchronize()
+    print("   plan + forward done", flush=True)
+    rng = np.random.default_rng(100 + cid)
+    a2v = inp["a2v"].double().cpu().numpy()
+    heads = [0, wl.heads - 1]
+    samples = {}
+    views = att.views()
+    for h in heads:
+        hi = _head_inputs(inp, h)
+        op = oracle.plan_head(wl.T, wl.H, wl.W, hi["q"], hi["k"], hi["v"], a2v, top_k=wl.top_k,
+                              top_p=wl.top_p, min_edge_log2=wl.min_edge_log2)
+        rep = compare_plan(views, h, op)
+        assert not rep.get("downstream_skipped"), rep
+        exact, excl, nnz = compare_selection(views, h, op, wl.top_p)
+        ok_rows = np.nonzero(rows_of_exact_blocks(op, exact))[0]
+        rows = np.sort(rng.choice(ok_rows, size=64, replace=False))
+        oo, ol = oracle.attn_fwd(op, hi["q"], hi["k"], hi["v"], rows=rows)
+        e_o, r_o = check_close(o[rows, h].float().cpu().numpy(), oo[rows], "bf16", f"h{h} O")
+        e_l, r_l = check_close(lse[h, rows].cpu().numpy(), ol[rows], "bf16", f"h{h} lse")
+        print(f"   head {h}: nb {op.nb} nnz {nnz} excluded {excl} near-tie zones "
+              f"{rep['near_tie_zones']} | O err {e_o:.2e} (bound use {r_o:.2f}) "
+              f"lse err {e_l:.2e}", flush=True)
+        samples[h] = (op, hi, rows)
+    if not wl.backward:
+        return
+    # gradients: upstream gradient nonzero on 16 sampled rows of each checked head
+    dout = torch.zeros(wl.N, wl.heads, wl.head_dim, dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7 + cid)
+    brows = {}
+    for h in heads:
+        br = samples[h][2][::4][:16]
+        brows[h] = br
+        idx = torch.from_numpy(br).cuda()
+        dout[idx, h] = torch.randn(len(br), wl.head_dim, generator=g, device="cuda").bfloat16()
+    dq, dk, dv = att.backward(dout)
+    torch.cuda.synchronize()
+    print("   backward done", flush=True)
+    for h in heads:
+        op, hi, _ = samples[h]
+        br = brows[h]
+        d_np = dout[:, h].double().cpu().numpy()
+        rq, rk, rv = oracle.attn_bwd(op, hi["q"], hi["k"], hi["v"], d_np, rows=br)
+        e_q, _ = check_close(dq[:, h].float().cpu().numpy(), rq, "bf16", f"h{h} dq")
+        e_k, _ = check_close(dk[:, h].float().cpu().numpy(), rk, "bf16", f"h{h} dk")
+        e_v, _ = check_close(dv[:, h].float().cpu().numpy(), rv, "bf16", f"h{h} dv")
+        nz = int((np.abs(rv).sum(1) > 0).sum())
+        print(f"   head {h}: dq err {e_q:.2e} dk err {e_k:.2e} dv err {e_v:.2e} "
+              f"({nz} key rows with nonzero gradient)", flush=True)
