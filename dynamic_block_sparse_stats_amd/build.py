@@ -18,7 +18,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libprism.so")
 SOURCES = ["plan_kernels.hip", "select_kernels.hip", "attn_fwd.hip", "attn_bwd.hip",
-           "prism_api.hip"]
+           "attn_bwd_dkdv.hip", "prism_api.hip"]
+# The attention kernels never see NaN inputs; without IEEE-mode NaN quieting the compiler
+# can feed MFMA results straight into v_max instead of canonicalising each one first.
+# The forward and dQ kernels also keep their MFMA accumulators in ordinary VGPRs (no
+# accvgpr copies around the softmax); dK/dV, with more live accumulators, does not.
+_NAN = ["-fno-honor-nans", "-mno-amdgpu-ieee"]
+_VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA = {"attn_fwd.hip": _NAN + _VGPR_MFMA, "attn_bwd.hip": _NAN + _VGPR_MFMA,
+         "attn_bwd_dkdv.hip": _NAN}
 ARCH = "gfx950"
 
 
@@ -45,7 +53,8 @@ def build(verbose: bool = False) -> str:
         objs = []
         for src in SOURCES:
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
-            cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *compile_flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src),
+                   "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,

@@ -96,151 +96,7 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// ============================================================================ dK / dV (bf16)
-// Four waves per workgroup; a 64-key tile (a 64-token block) leaves waves 2-3 to help stage
-// the query units only.
 constexpr int NW = 4;
-
-__global__ void __launch_bounds__(NW * 64)
-    attn_dkdv_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
-                          const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
-                          const uint16_t *__restrict__ qpt, const uint16_t *__restrict__ kp,
-                          const uint16_t *__restrict__ vp, const uint16_t *__restrict__ dop,
-                          const uint16_t *__restrict__ dopt, const float *__restrict__ lsep,
-                          const float *__restrict__ delta, const int *__restrict__ unit_blk,
-                          const int *__restrict__ blk_start, const int *__restrict__ blk_size,
-                          const int *__restrict__ csc_count, const int *__restrict__ csc_row,
-                          const int *__restrict__ perm, float scale, float scale_log2e,
-                          uint16_t *__restrict__ dk, uint16_t *__restrict__ dv) {
-  constexpr int NT = NW * 64;
-  constexpr int CPT = 1024 / NT;
-  __shared__ __align__(16) uint8_t lds[4][16384];  // Q, dO (row-major), Q^T, dO^T
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int ntiles = *tile_count;
-  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int2 tl = tiles[t];
-    const int h = tl.x, u0 = tl.y & (kTile64 - 1);
-    const bool active = !(tl.y & kTile64) || wave < 2;
-    const int jblk = unit_blk[(size_t)h * U + u0];
-    const int nq = csc_count[(size_t)h * nb_max + jblk];
-    const int *qlist = csc_row + ((size_t)h * nb_max + jblk) * nb_max;
-    const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
-    // this wave's 32 keys: K^T and V^T as B operands (lane = key, 8 dims per k-step)
-    const int key0 = u0 * kUnit + wave * 32;
-    bf16x8 kreg[8], vreg[8];
-    if (active) {
-      const uint16_t *kr = kp + ((size_t)h * N + key0 + l32) * kDB + 8 * hh;
-      const uint16_t *vr = vp + ((size_t)h * N + key0 + l32) * kDB + 8 * hh;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        kreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kr + 16 * kk));
-        vreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(vr + 16 * kk));
-      }
-    }
-    f32x16 dkt[4], dvt[4];  // [d][key] accumulators, 4 tiles of 32 dims
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) dkt[dt] = dvt[dt] = f32x16{};
-
-    for (int qi = 0; qi < nq; ++qi) {
-      const int iblk = qlist[qi];
-      const int us = bs[iblk] / kUnit, nu = bz[iblk] / kUnit;
-      for (int u = us; u < us + nu; ++u) {
-        __syncthreads();
-        const size_t ub = ((size_t)h * N + (size_t)u * kUnit) * kDB * 2;  // bytes
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) {
-          const int q = tid + NT * e;
-          const uint8_t *g0 = reinterpret_cast<const uint8_t *>(qp) + ub + 16 * q;
-          const uint8_t *g1 = reinterpret_cast<const uint8_t *>(dop) + ub + 16 * q;
-          const uint8_t *g2 = reinterpret_cast<const uint8_t *>(qpt) + ub + 16 * q;
-          const uint8_t *g3 = reinterpret_cast<const uint8_t *>(dopt) + ub + 16 * q;
-          *reinterpret_cast<u32x4 *>(&lds[0][rm_off(q >> 4, q & 15)]) =
-              *reinterpret_cast<const u32x4 *>(g0);
-          *reinterpret_cast<u32x4 *>(&lds[1][rm_off(q >> 4, q & 15)]) =
-              *reinterpret_cast<const u32x4 *>(g1);
-          *reinterpret_cast<u32x4 *>(&lds[2][tr_off(q >> 3, q & 7)]) =
-              *reinterpret_cast<const u32x4 *>(g2);
-          *reinterpret_cast<u32x4 *>(&lds[3][tr_off(q >> 3, q & 7)]) =
-              *reinterpret_cast<const u32x4 *>(g3);
-        }
-        __syncthreads();
-        if (!active) continue;
-        const float *lrow = lsep + (size_t)h * N + (size_t)u * kUnit;
-        const float *drow = delta + (size_t)h * N + (size_t)u * kUnit;
-        f16x8 pb[4], db[4];
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {  // queries 32a .. 32a + 31 of the unit
-          f32x16 s = f32x16{}, dp = f32x16{};
-          const int r = 32 * a + l32;
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            bf16x8 qa = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4 *>(&lds[0][rm_off(r, 2 * kk + hh)]));
-            bf16x8 da = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4 *>(&lds[1][rm_off(r, 2 * kk + hh)]));
-            s = mfma_bf16(qa, kreg[kk], s);
-            dp = mfma_bf16(da, vreg[kk], dp);
-          }
-          // C layout: lane = key l32, register v = query 32a + (v/4)*8 + 4hh + v%4
-#pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) {
-            const int q0 = 32 * a + 8 * v4 + 4 * hh;
-            const float4 l4 = *reinterpret_cast<const float4 *>(lrow + q0);
-            const float4 d4 = *reinterpret_cast<const float4 *>(drow + q0);
-            const float lq[4] = {l4.x, l4.y, l4.z, l4.w}, dq4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int v = 4 * v4 + e;
-              const float p = __builtin_amdgcn_exp2f(s[v] * scale_log2e - lq[e] * 1.4426950408889634f);
-              const float ds = p * (dp[v] - dq4[e]);
-              const int g = 2 * a + (v >> 3), slot = v & 7;
-              pb[g][slot] = (_Float16)(p * kPScale);
-              db[g][slot] = (_Float16)ds;
-            }
-          }
-        }
-        // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int d = 32 * dt + l32;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f16x8 doa = __builtin_bit_cast(
-                f16x8, *reinterpret_cast<const u32x4 *>(&lds[3][tr_off(d, 2 * g + hh)]));
-            f16x8 qta = __builtin_bit_cast(
-                f16x8, *reinterpret_cast<const u32x4 *>(&lds[2][tr_off(d, 2 * g + hh)]));
-            dvt[dt] = mfma_f16(doa, pb[g], dvt[dt]);
-            dkt[dt] = mfma_f16(qta, db[g], dkt[dt]);
-          }
-        }
-      }
-    }
-    // epilogue: C layout lane = key l32, register v -> d = 32dt + (v/4)*8 + 4hh + v%4
-    if (!active) continue;
-    const int token = perm[(size_t)h * N + key0 + l32];
-    uint16_t *krow = dk + ((size_t)token * heads + h) * kDB;
-    uint16_t *vrow = dv + ((size_t)token * heads + h) * kDB;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const int d0 = 32 * dt + 8 * v4 + 4 * hh;
-        const f32x16 &K = dkt[dt], &V = dvt[dt];
-        uint32_t k0 = (uint32_t)f32_to_bf16(K[4 * v4] * scale) |
-                      ((uint32_t)f32_to_bf16(K[4 * v4 + 1] * scale) << 16);
-        uint32_t k1 = (uint32_t)f32_to_bf16(K[4 * v4 + 2] * scale) |
-                      ((uint32_t)f32_to_bf16(K[4 * v4 + 3] * scale) << 16);
-        const float vs = 1.f / kPScale;
-        uint32_t w0 = (uint32_t)f32_to_bf16(V[4 * v4] * vs) |
-                      ((uint32_t)f32_to_bf16(V[4 * v4 + 1] * vs) << 16);
-        uint32_t w1 = (uint32_t)f32_to_bf16(V[4 * v4 + 2] * vs) |
-                      ((uint32_t)f32_to_bf16(V[4 * v4 + 3] * vs) << 16);
-        *reinterpret_cast<u32x2 *>(krow + d0) = u32x2{k0, k1};
-        *reinterpret_cast<u32x2 *>(vrow + d0) = u32x2{w0, w1};
-      }
-  }
-}
 
 // ============================================================================ dQ (bf16)
 __global__ void __launch_bounds__(NW * 64)
@@ -321,7 +177,7 @@ __global__ void __launch_bounds__(NW * 64)
           // lane = query, register v = key 32a + (v/4)*8 + 4hh + v%4
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const float p = __builtin_amdgcn_exp2f(s[v] * scale_log2e - lse2);
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[v], scale_log2e, -lse2));
             db[2 * a + (v >> 3)][v & 7] = (_Float16)(p * (dp[v] - dlt));
           }
         }
@@ -520,10 +376,9 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
     const int2 *tiles = (const int2 *)(ws + L.tiles);
     {
       TraceScope tr(PRISM_STAGE_BWD_DKDV, s);
-      hipLaunchKernelGGL(attn_dkdv_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, d.N, d.U,
-                         d.nb_max, d.heads, tiles, counters, qp, qpt, kp, vp, dop, dopt, lsep,
-                         delta, unit_blk, bstart, bsize, tcnt, trows, perm, scale, sl2e,
-                         (T *)dk, (T *)dv);
+      launch_dkdv_bf16(grid, s, d.N, d.U, d.nb_max, d.heads, tiles, counters, qp, qpt, kp, vp,
+                       dop, dopt, lsep, delta, unit_blk, bstart, bsize, tcnt, trows, perm, scale,
+                       sl2e, (T *)dk, (T *)dv);
     }
     {
       TraceScope tr(PRISM_STAGE_BWD_DQ, s);

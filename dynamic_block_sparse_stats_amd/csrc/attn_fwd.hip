@@ -128,7 +128,8 @@ __global__ void __launch_bounds__(NW * 64)
     f32x16 o[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-    float m = -INFINITY;
+    // running max of the scaled logits (log2 domain) and its shifted copy used in exp2
+    float m = -INFINITY, mk = -INFINITY;
     double lsum = 0.0;
 
     __syncthreads();  // previous tile's readers are done with both buffers
@@ -141,7 +142,7 @@ __global__ void __launch_bounds__(NW * 64)
       if (more) gload(cur.unit());
       const uint8_t *Kt = lds[buf][0], *Vt = lds[buf][1];
       if (active) {
-        // S^T for keys 0-31 (a = 0) and 32-63 (a = 1)
+        // S^T for keys 0-31 (a = 0) and 32-63 (a = 1): lane = query l32, 16 keys per tile
         f32x16 s[2];
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
@@ -154,34 +155,44 @@ __global__ void __launch_bounds__(NW * 64)
             s[a] = mfma_bf16(ka, qreg[kk], s[a]);
           }
         }
-        // online softmax, log2 domain; lane = query l32, keys split over the two half waves
-        float tmax = -INFINITY;
+        // online softmax (log2 domain) with lazy rescaling: the running max only moves when
+        // a query's new maximum exceeds it by more than 2^kLazy, so the float16 weights
+        // 2^(t - m + 10) stay below 2^15
+        float tmax = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int v = 2; v < 16; v += 2) tmax = fmaxf(tmax, fmaxf(s[0][v], s[0][v + 1]));
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            s[a][v] *= scale_log2e;
-            tmax = fmaxf(tmax, s[a][v]);
-          }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float mnew = fmaxf(m, tmax);
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        m = mnew;
+        for (int v = 0; v < 16; v += 2) tmax = fmaxf(tmax, fmaxf(s[1][v], s[1][v + 1]));
+        {
+          auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax),
+                                                     __float_as_uint(tmax), false, false);
+          tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float tm = tmax * scale_log2e;
+        const bool grow = tm > m + kLazy;
+        if (__ballot(grow)) {
+          const float mnew = grow ? tm : m;
+          const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+          m = mnew;
+          mk = mnew - kPShift;
+          lsum *= (double)alpha;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+        }
         float psum = 0.f;
         f16x8 pb[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            float p = __builtin_amdgcn_exp2f(s[g >> 1][8 * (g & 1) + e] - mnew + kPShift);
+            const float p =
+                __builtin_amdgcn_exp2f(fmaf(s[g >> 1][8 * (g & 1) + e], scale_log2e, -mk));
             psum += p;
             pb[g][e] = (_Float16)p;
           }
-        lsum = lsum * (double)alpha + (double)psum;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+        lsum += (double)psum;
         // O^T[d][q] += V^T[d][keys] P^T[keys][q]
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
@@ -201,7 +212,7 @@ __global__ void __launch_bounds__(NW * 64)
     }
     // epilogue
     if (!active) continue;
-    const double ltot = lsum + __shfl_xor(lsum, 32, 64);
+    const double ltot = lsum + __shfl_xor(lsum, 32, 64);  // the two half waves' keys
     const float inv = (float)(1.0 / ltot);
     const int prow = row0 + l32;
     const int token = perm[(size_t)h * N + prow];

@@ -85,6 +85,16 @@ hipError_t launch_attn_fwd(const Dims &d, float scale, uint8_t *ws, const Layout
 hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout &L,
                            const void *dout, void *dq, void *dk, void *dv, hipStream_t s);
 
+// attn_bwd_dkdv.hip
+hipError_t launch_dkdv_bf16(int grid, hipStream_t s, int N, int U, int nb_max, int heads,
+                            const int2 *tiles, const int *counters, const uint16_t *qp,
+                            const uint16_t *qpt, const uint16_t *kp, const uint16_t *vp,
+                            const uint16_t *dop, const uint16_t *dopt, const float *lsep,
+                            const float *delta, const int *unit_blk, const int *bstart,
+                            const int *bsize, const int *tcnt, const int *trows,
+                            const int *perm, float scale, float sl2e, uint16_t *dk,
+                            uint16_t *dv);
+
 // ---------------------------------------------------------------------------- device helpers
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
@@ -117,6 +127,9 @@ __device__ __forceinline__ uint16_t bf16_to_f16_bits(uint16_t b) {
 // the row maximum stay normal float16 numbers; the scale cancels in O = sum(p v) / sum(p).
 constexpr float kPShift = 10.f;
 constexpr float kPScale = 1024.f;
+// Lazy rescaling in the forward: the running max is kept until a new maximum exceeds it
+// by more than kLazy (log2 units); weights then stay below 2^(kPShift + kLazy) = 2^15.
+constexpr float kLazy = 5.f;
 
 template <typename T>
 __device__ __forceinline__ T *ws_ptr(uint8_t *ws, size_t off) {
