@@ -368,7 +368,6 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
     const int *counters = (const int *)(ws + L.counters);
     const float sl2e = scale * 1.4426950408889634f;
     const int maxt = d.heads * d.U;
-    const int grid = maxt < 8192 ? maxt : 8192;
     const T *qp = (const T *)(ws + L.qp), *kp = (const T *)(ws + L.kp),
             *vp = (const T *)(ws + L.vp), *qpt = (const T *)(ws + L.qpt),
             *kpt = (const T *)(ws + L.kpt), *dop = (const T *)(ws + L.dop),
@@ -376,12 +375,13 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
     const int2 *tiles = (const int2 *)(ws + L.tiles);
     {
       TraceScope tr(PRISM_STAGE_BWD_DKDV, s);
-      launch_dkdv_bf16(grid, s, d.N, d.U, d.nb_max, d.heads, tiles, counters, qp, qpt, kp, vp,
+      launch_dkdv_bf16(maxt, s, d.N, d.U, d.nb_max, d.heads, tiles, counters, qp, qpt, kp, vp,
                        dop, dopt, lsep, delta, unit_blk, bstart, bsize, tcnt, trows, perm, scale,
                        sl2e, (T *)dk, (T *)dv);
     }
     {
       TraceScope tr(PRISM_STAGE_BWD_DQ, s);
+      const int grid = resident_grid((const void *)attn_dq_bf16_kernel, NW * 64, maxt);
       hipLaunchKernelGGL(attn_dq_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, d.N, d.U,
                          d.nb_max, d.heads, tiles, counters, qp, kp, kpt, vp, dop, lsep, delta,
                          unit_blk, bstart, bsize, cnt, cols, perm, scale, sl2e, (T *)dq);

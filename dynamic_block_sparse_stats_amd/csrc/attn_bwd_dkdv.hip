@@ -167,7 +167,7 @@ __global__ void __launch_bounds__(NW * 64)
 }
 
 
-hipError_t launch_dkdv_bf16(int grid, hipStream_t s, int N, int U, int nb_max, int heads,
+hipError_t launch_dkdv_bf16(int work_items, hipStream_t s, int N, int U, int nb_max, int heads,
                             const int2 *tiles, const int *counters, const uint16_t *qp,
                             const uint16_t *qpt, const uint16_t *kp, const uint16_t *vp,
                             const uint16_t *dop, const uint16_t *dopt, const float *lsep,
@@ -175,6 +175,7 @@ hipError_t launch_dkdv_bf16(int grid, hipStream_t s, int N, int U, int nb_max, i
                             const int *bsize, const int *tcnt, const int *trows,
                             const int *perm, float scale, float sl2e, uint16_t *dk,
                             uint16_t *dv) {
+  const int grid = resident_grid((const void *)attn_dkdv_bf16_kernel, NW * 64, work_items);
   hipLaunchKernelGGL(attn_dkdv_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, N, U, nb_max,
                      heads, tiles, counters, qp, qpt, kp, vp, dop, dopt, lsep, delta, unit_blk,
                      bstart, bsize, tcnt, trows, perm, scale, sl2e, dk, dv);

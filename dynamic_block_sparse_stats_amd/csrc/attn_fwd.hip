@@ -326,8 +326,7 @@ hipError_t launch_attn_fwd(const Dims &d, float scale, uint8_t *ws, const Layout
   if (d.dtype == PRISM_BF16) {
     const int *counters = (const int *)(ws + L.counters);
     const float sl2e = scale * 1.4426950408889634f;
-    const int maxt = d.heads * d.U;
-    const int grid = maxt < 8192 ? maxt : 8192;
+    const int grid = resident_grid((const void *)attn_fwd_bf16_kernel, NW * 64, d.heads * d.U);
     hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, d.N, d.U,
                        d.nb_max, d.heads, (const int2 *)(ws + L.tiles), counters,
                        (const uint16_t *)(ws + L.qp), (const uint16_t *)(ws + L.kp),

@@ -515,33 +515,49 @@ hipError_t launch_gather(const Dims &d, const void *q, const void *k, const void
 // for 64-token blocks (the 64-token atomic unit of the digest's training section; 128- and
 // 256-token blocks are 2 and 4 units).  The same tiles serve as query tiles (forward, dQ)
 // and key tiles (dK/dV) because Q, K and V share one partition.  Entry (head, first unit |
-// kTile64 flag).  Order inside the list is immaterial to the results.
-__global__ void zero_ints_kernel(int *p, int n) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
-}
+// kTile64 flag).  The order of the list changes no result, only which tiles run together.
+// Tiles in (head, zone, position) order: the persistent attention kernels take tiles
+// t, t + grid, ... so the workgroups resident at any moment work on neighbouring tiles of
+// one head and stream that head's keys in the same ascending order, sharing them in L2.
+constexpr int kTileThreads = 1024;
 
-__global__ void tiles_kernel(int heads, int Z, const int *__restrict__ zshape, int2 *tiles,
-                             int *counters) {
-  int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= heads * Z) return;
-  int h = idx / Z, m = idx % Z;
-  int code = zshape[idx];
-  int S = ((code >> 4) & 3) + ((code >> 2) & 3) + (code & 3);
-  if (S >= 7) {
-    int at = atomicAdd(&counters[0], 4);
-    for (int s = 0; s < 4; ++s) tiles[at + s] = make_int2(h, 8 * m + 2 * s);
-  } else {
-    int at = atomicAdd(&counters[0], 8);
-    for (int s = 0; s < 8; ++s) tiles[at + s] = make_int2(h, (8 * m + s) | kTile64);
+__global__ void __launch_bounds__(kTileThreads)
+    tiles_kernel(int heads, int Z, const int *__restrict__ zshape, int2 *tiles, int *counters) {
+  __shared__ int scan[kTileThreads];
+  const int tid = threadIdx.x, n = heads * Z;
+  const int chunk = (n + kTileThreads - 1) / kTileThreads;
+  const int i0 = min(n, tid * chunk), i1 = min(n, i0 + chunk);
+  auto ntile = [&](int idx) {
+    const int code = zshape[idx];
+    return ((code >> 4) & 3) + ((code >> 2) & 3) + (code & 3) >= 7 ? 4 : 8;
+  };
+  int local = 0;
+  for (int i = i0; i < i1; ++i) local += ntile(i);
+  scan[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kTileThreads; off <<= 1) {
+    const int add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
   }
+  int at = scan[tid] - local;
+  for (int i = i0; i < i1; ++i) {
+    const int h = i / Z, m = i % Z;
+    if (ntile(i) == 4) {
+      for (int s = 0; s < 4; ++s) tiles[at + s] = make_int2(h, 8 * m + 2 * s);
+      at += 4;
+    } else {
+      for (int s = 0; s < 8; ++s) tiles[at + s] = make_int2(h, (8 * m + s) | kTile64);
+      at += 8;
+    }
+  }
+  if (tid == kTileThreads - 1) counters[0] = scan[tid];
 }
 
 hipError_t launch_tiles(const Dims &d, uint8_t *ws, const Layout &L, hipStream_t s) {
   TraceScope tr(PRISM_STAGE_TILES, s);
-  hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(64), 0, s, (int *)(ws + L.counters), 16);
-  int n = d.heads * d.Z;
-  hipLaunchKernelGGL(tiles_kernel, dim3((n + 255) / 256), dim3(256), 0, s, d.heads, d.Z,
+  hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(kTileThreads), 0, s, d.heads, d.Z,
                      (const int *)(ws + L.pub.zone_shape), (int2 *)(ws + L.tiles),
                      (int *)(ws + L.counters));
   return hipGetLastError();

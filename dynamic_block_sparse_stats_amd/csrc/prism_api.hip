@@ -188,6 +188,19 @@ Scales scales_of(const prism_config *cfg, const Dims &d) {
   return s;
 }
 
+int resident_grid(const void *kernel, int block, int work_items) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess ||
+      cus <= 0 || per_cu <= 0) {
+    cus = 256;
+    per_cu = 1;
+  }
+  const long long g = (long long)cus * per_cu;
+  return (int)(g < work_items ? g : (work_items > 0 ? work_items : 1));
+}
+
 static prism_status launched(hipError_t e, const char *stage) {
   if (e != hipSuccess)
     return fail(PRISM_ERR_HIP, std::string(stage) + ": " + hipGetErrorString(e));

@@ -86,7 +86,7 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
                            const void *dout, void *dq, void *dk, void *dv, hipStream_t s);
 
 // attn_bwd_dkdv.hip
-hipError_t launch_dkdv_bf16(int grid, hipStream_t s, int N, int U, int nb_max, int heads,
+hipError_t launch_dkdv_bf16(int work_items, hipStream_t s, int N, int U, int nb_max, int heads,
                             const int2 *tiles, const int *counters, const uint16_t *qp,
                             const uint16_t *qpt, const uint16_t *kp, const uint16_t *vp,
                             const uint16_t *dop, const uint16_t *dopt, const float *lsep,
@@ -94,6 +94,10 @@ hipError_t launch_dkdv_bf16(int grid, hipStream_t s, int N, int U, int nb_max, i
                             const int *bsize, const int *tcnt, const int *trows,
                             const int *perm, float scale, float sl2e, uint16_t *dk,
                             uint16_t *dv);
+
+// Workgroups of `kernel` (block size `block`) that fit on the current device at once: the
+// grid of the persistent attention kernels.
+int resident_grid(const void *kernel, int block, int work_items);
 
 // ---------------------------------------------------------------------------- device helpers
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
