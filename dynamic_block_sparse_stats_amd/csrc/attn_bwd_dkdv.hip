@@ -19,9 +19,140 @@ __device__ __forceinline__ int tr_off(int d, int c) {  // [128][64] f16 tile, 8 
 }  // namespace
 
 // ============================================================================ dK / dV (bf16)
-// Four waves per workgroup; a 64-key tile (a 64-token block) leaves waves 2-3 to help stage
-// the query units only.
+// One workgroup of four waves per key tile; each wave owns 32 keys (its K and V rows are
+// the B operands, held in registers) and accumulates dK^T and dV^T over the 64-token
+// query units of every query block that selected the key block.  A 64-key tile leaves
+// waves 2-3 idle in the arithmetic.
+//
+// Query units stream through a two-stage LDS ring filled by direct global->LDS copies
+// (global_load_lds_dwordx4: lane l of one instruction lands at +16*l, so the XOR swizzle
+// is applied by choosing which source chunk each lane fetches).  Per stage: Q and dO
+// row-major [64][128] bf16, Q^T and dO^T [128][64] f16, lse and delta [64].  Each wave
+// copies one of the four tiles (16 instructions) and one 256-byte vector, so every wave
+// has the same number of copies in flight; the copy of the next unit is issued right after
+// the barrier that publishes the current one and overlaps its 64 MFMAs.
 constexpr int NW = 4;
+
+__device__ __forceinline__ void dma16(const void *src, void *dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                   (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *src, void *dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                   (__attribute__((address_space(3))) void *)dst, 4, 0, 0);
+}
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone), then a workgroup barrier that the
+// compiler may not move memory operations across.
+__device__ __forceinline__ void wait_copies_and_sync() {
+  __builtin_amdgcn_s_waitcnt(0x0070 | 0x0f00);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+struct QueryUnits {  // the 64-token units of the listed query blocks, in order
+  int idx, sub, us, nu, n;
+  const int *list, *bstart, *bsize;
+  __device__ void load() {
+    const int i = list[idx];
+    us = bstart[i] / kUnit;
+    nu = bsize[i] / kUnit;
+  }
+  __device__ void init(const int *l, int count, const int *bs, const int *bz) {
+    list = l;
+    n = count;
+    bstart = bs;
+    bsize = bz;
+    idx = sub = 0;
+    load();
+  }
+  __device__ int unit() const { return us + sub; }
+  __device__ bool next() {
+    if (++sub < nu) return true;
+    sub = 0;
+    if (++idx >= n) return false;
+    load();
+    return true;
+  }
+};
+
+// The two stages are distinct LDS objects and the unit loop is unrolled by two, so every
+// LDS read names its stage statically; the compiler can then see that the copies in flight
+// (into the other stage) do not feed the reads, and issues no wait for them.
+struct Stage {
+  uint8_t tile[4][16384];  // Q, dO (row-major bf16), Q^T, dO^T (f16)
+  float vec[4][kUnit];     // lse, delta, unused, unused
+};
+__shared__ __align__(16) Stage g_stage0;
+__shared__ __align__(16) Stage g_stage1;
+template <int S>
+__device__ __forceinline__ Stage &stage() {
+  return S ? g_stage1 : g_stage0;
+}
+
+struct DkdvState {
+  bf16x8 kreg[8], vreg[8];
+  f32x16 dkt[4], dvt[4];
+};
+
+template <int S>
+__device__ __forceinline__ void dkdv_unit(DkdvState &w, int l32, int hh, float scale_log2e) {
+  const Stage &sg = stage<S>();
+  f16x8 pb[4], db[4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {  // queries 32a .. 32a + 31 of the unit
+    const int r = 32 * a + l32;
+    bf16x8 qa[8], da[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      qa[kk] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4 *>(sg.tile[0] + rm_off(r, 2 * kk + hh)));
+      da[kk] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4 *>(sg.tile[1] + rm_off(r, 2 * kk + hh)));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the 16 reads ahead of the MFMAs below
+    f32x16 sacc = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      sacc = mfma_bf16(qa[kk], w.kreg[kk], sacc);
+      dp = mfma_bf16(da[kk], w.vreg[kk], dp);
+    }
+    // C layout: lane = key l32, register v = query 32a + (v/4)*8 + 4hh + v%4
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int q0 = 32 * a + 8 * v4 + 4 * hh;
+      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sg.vec[0] + q0);
+      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sg.vec[1] + q0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * v4 + e;
+        const float p =
+            __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2e, -l4[e] * 1.4426950408889634f));
+        const int g = 2 * a + (v >> 3), slot = v & 7;
+        pb[g][slot] = (_Float16)(p * kPScale);
+        db[g][slot] = (_Float16)(p * (dp[v] - d4[e]));
+      }
+    }
+  }
+  // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int d = 32 * dt + l32;
+    f16x8 doa[4], qta[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      doa[g] = __builtin_bit_cast(
+          f16x8, *reinterpret_cast<const u32x4 *>(sg.tile[3] + tr_off(d, 2 * g + hh)));
+      qta[g] = __builtin_bit_cast(
+          f16x8, *reinterpret_cast<const u32x4 *>(sg.tile[2] + tr_off(d, 2 * g + hh)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      w.dvt[dt] = mfma_f16(doa[g], pb[g], w.dvt[dt]);
+      w.dkt[dt] = mfma_f16(qta[g], db[g], w.dkt[dt]);
+    }
+  }
+}
 
 __global__ void __launch_bounds__(NW * 64)
     attn_dkdv_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
@@ -34,13 +165,23 @@ __global__ void __launch_bounds__(NW * 64)
                           const int *__restrict__ csc_count, const int *__restrict__ csc_row,
                           const int *__restrict__ perm, float scale, float scale_log2e,
                           uint16_t *__restrict__ dk, uint16_t *__restrict__ dv) {
-  constexpr int NT = NW * 64;
-  constexpr int CPT = 1024 / NT;
-  __shared__ __align__(16) uint8_t lds[4][16384];  // Q, dO (row-major), Q^T, dO^T
-  __shared__ __align__(16) float lsd[2][kUnit];    // lse * log2(e), delta of the unit
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   const int ntiles = *tile_count;
+  const uint8_t *tsrc = reinterpret_cast<const uint8_t *>(
+      wave == 0 ? qp : (wave == 1 ? dop : (wave == 2 ? qpt : dopt)));
+  const float *vsrc = wave == 1 ? delta : lsep;
+  // this lane's byte offset inside copy i (1 KB) of its wave's tile: rows 4i.. (row-major
+  // tiles) or 8i.. (transposed tiles); the swizzle only depends on the row within 16 / 8
+  auto lofs = [&](int i) {
+    if (wave < 2) {
+      const int r = 4 * i + (lane >> 4);
+      return r * 256 + (((lane & 15) ^ (r & 15)) << 4);
+    }
+    const int d = 8 * i + (lane >> 3);
+    return d * 128 + (((lane & 7) ^ ((d >> 1) & 7)) << 4);
+  };
+
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int2 tl = tiles[t];
     const int h = tl.x, u0 = tl.y & (kTile64 - 1);
@@ -51,93 +192,50 @@ __global__ void __launch_bounds__(NW * 64)
     const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
     // this wave's 32 keys: K^T and V^T as B operands (lane = key, 8 dims per k-step)
     const int key0 = u0 * kUnit + wave * 32;
-    bf16x8 kreg[8], vreg[8];
+    DkdvState w;
     if (active) {
       const uint16_t *kr = kp + ((size_t)h * N + key0 + l32) * kDB + 8 * hh;
       const uint16_t *vr = vp + ((size_t)h * N + key0 + l32) * kDB + 8 * hh;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        kreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kr + 16 * kk));
-        vreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(vr + 16 * kk));
+        w.kreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kr + 16 * kk));
+        w.vreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(vr + 16 * kk));
       }
     }
-    f32x16 dkt[4], dvt[4];  // [d][key] accumulators, 4 tiles of 32 dims
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) dkt[dt] = dvt[dt] = f32x16{};
+    for (int dt = 0; dt < 4; ++dt) w.dkt[dt] = w.dvt[dt] = f32x16{};
 
-    for (int qi = 0; qi < nq; ++qi) {
-      const int iblk = qlist[qi];
-      const int us = bs[iblk] / kUnit, nu = bz[iblk] / kUnit;
-      for (int u = us; u < us + nu; ++u) {
-        __syncthreads();
-        const size_t ub = ((size_t)h * N + (size_t)u * kUnit) * kDB * 2;  // bytes
+    const size_t hb = (size_t)h * N;
+    auto issue0 = [&](int u) {
+      const uint8_t *src = tsrc + (hb + (size_t)u * kUnit) * kDB * 2;
 #pragma unroll
-        for (int e = 0; e < CPT; ++e) {
-          const int q = tid + NT * e;
-          const uint8_t *g0 = reinterpret_cast<const uint8_t *>(qp) + ub + 16 * q;
-          const uint8_t *g1 = reinterpret_cast<const uint8_t *>(dop) + ub + 16 * q;
-          const uint8_t *g2 = reinterpret_cast<const uint8_t *>(qpt) + ub + 16 * q;
-          const uint8_t *g3 = reinterpret_cast<const uint8_t *>(dopt) + ub + 16 * q;
-          *reinterpret_cast<u32x4 *>(&lds[0][rm_off(q >> 4, q & 15)]) =
-              *reinterpret_cast<const u32x4 *>(g0);
-          *reinterpret_cast<u32x4 *>(&lds[1][rm_off(q >> 4, q & 15)]) =
-              *reinterpret_cast<const u32x4 *>(g1);
-          *reinterpret_cast<u32x4 *>(&lds[2][tr_off(q >> 3, q & 7)]) =
-              *reinterpret_cast<const u32x4 *>(g2);
-          *reinterpret_cast<u32x4 *>(&lds[3][tr_off(q >> 3, q & 7)]) =
-              *reinterpret_cast<const u32x4 *>(g3);
-        }
-        if (tid < 2 * kUnit) {
-          const size_t pr = (size_t)h * N + (size_t)u * kUnit + (tid & (kUnit - 1));
-          lsd[tid >> 6][tid & (kUnit - 1)] =
-              tid < kUnit ? lsep[pr] * 1.4426950408889634f : delta[pr];
-        }
-        __syncthreads();
-        if (!active) continue;
-        f16x8 pb[4], db[4];
+      for (int i = 0; i < 16; ++i) dma16(src + lofs(i), g_stage0.tile[wave] + 1024 * i);
+      dma4(vsrc + hb + (size_t)u * kUnit + lane, g_stage0.vec[wave]);
+    };
+    auto issue1 = [&](int u) {
+      const uint8_t *src = tsrc + (hb + (size_t)u * kUnit) * kDB * 2;
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {  // queries 32a .. 32a + 31 of the unit
-          f32x16 s = f32x16{}, dp = f32x16{};
-          const int r = 32 * a + l32;
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            bf16x8 qa = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4 *>(&lds[0][rm_off(r, 2 * kk + hh)]));
-            bf16x8 da = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4 *>(&lds[1][rm_off(r, 2 * kk + hh)]));
-            s = mfma_bf16(qa, kreg[kk], s);
-            dp = mfma_bf16(da, vreg[kk], dp);
-          }
-          // C layout: lane = key l32, register v = query 32a + (v/4)*8 + 4hh + v%4
-#pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) {
-            const int q0 = 32 * a + 8 * v4 + 4 * hh;
-            const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lsd[0][q0]);
-            const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&lsd[1][q0]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int v = 4 * v4 + e;
-              const float p = __builtin_amdgcn_exp2f(fmaf(s[v], scale_log2e, -l4[e]));
-              const int g = 2 * a + (v >> 3), slot = v & 7;
-              pb[g][slot] = (_Float16)(p * kPScale);
-              db[g][slot] = (_Float16)(p * (dp[v] - d4[e]));
-            }
-          }
-        }
-        // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int d = 32 * dt + l32;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f16x8 doa = __builtin_bit_cast(
-                f16x8, *reinterpret_cast<const u32x4 *>(&lds[3][tr_off(d, 2 * g + hh)]));
-            f16x8 qta = __builtin_bit_cast(
-                f16x8, *reinterpret_cast<const u32x4 *>(&lds[2][tr_off(d, 2 * g + hh)]));
-            dvt[dt] = mfma_f16(doa, pb[g], dvt[dt]);
-            dkt[dt] = mfma_f16(qta, db[g], dkt[dt]);
-          }
-        }
+      for (int i = 0; i < 16; ++i) dma16(src + lofs(i), g_stage1.tile[wave] + 1024 * i);
+      dma4(vsrc + hb + (size_t)u * kUnit + lane, g_stage1.vec[wave]);
+    };
+
+    __builtin_amdgcn_s_barrier();  // every wave is done with the previous tile's stages
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (nq > 0) {
+      QueryUnits cur;
+      cur.init(qlist, nq, bs, bz);
+      issue0(cur.unit());
+      while (true) {
+        bool more = cur.next();
+        wait_copies_and_sync();  // stage 0 has landed everywhere; stage 1 is free
+        if (more) issue1(cur.unit());
+        if (active) dkdv_unit<0>(w, l32, hh, scale_log2e);
+        if (!more) break;
+        more = cur.next();
+        wait_copies_and_sync();  // stage 1 has landed everywhere; stage 0 is free
+        if (more) issue0(cur.unit());
+        if (active) dkdv_unit<1>(w, l32, hh, scale_log2e);
+        if (!more) break;
       }
     }
     // epilogue: C layout lane = key l32, register v -> d = 32dt + (v/4)*8 + 4hh + v%4
@@ -150,7 +248,7 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         const int d0 = 32 * dt + 8 * v4 + 4 * hh;
-        const f32x16 &K = dkt[dt], &V = dvt[dt];
+        const f32x16 &K = w.dkt[dt], &V = w.dvt[dt];
         uint32_t k0 = (uint32_t)f32_to_bf16(K[4 * v4] * scale) |
                       ((uint32_t)f32_to_bf16(K[4 * v4 + 1] * scale) << 16);
         uint32_t k1 = (uint32_t)f32_to_bf16(K[4 * v4 + 2] * scale) |
@@ -165,7 +263,6 @@ __global__ void __launch_bounds__(NW * 64)
       }
   }
 }
-
 
 hipError_t launch_dkdv_bf16(int work_items, hipStream_t s, int N, int U, int nb_max, int heads,
                             const int2 *tiles, const int *counters, const uint16_t *qp,
