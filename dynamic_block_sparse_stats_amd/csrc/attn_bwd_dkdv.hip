@@ -33,22 +33,6 @@ __device__ __forceinline__ int tr_off(int d, int c) {  // [128][64] f16 tile, 8 
 // the barrier that publishes the current one and overlaps its 64 MFMAs.
 constexpr int NW = 4;
 
-__device__ __forceinline__ void dma16(const void *src, void *dst) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                   (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void *src, void *dst) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                   (__attribute__((address_space(3))) void *)dst, 4, 0, 0);
-}
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone), then a workgroup barrier that the
-// compiler may not move memory operations across.
-__device__ __forceinline__ void wait_copies_and_sync() {
-  __builtin_amdgcn_s_waitcnt(0x0070 | 0x0f00);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 struct QueryUnits {  // the 64-token units of the listed query blocks, in order
   int idx, sub, us, nu, n;
   const int *list, *bstart, *bsize;

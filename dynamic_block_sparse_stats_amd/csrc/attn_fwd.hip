@@ -8,10 +8,10 @@
 //   * a workgroup (4 waves) owns a query tile inside one block: 128 rows for blocks of 128
 //     or 256 tokens, 64 rows for 64-token blocks (then waves 2-3 only help stage K/V);
 //     each wave keeps its 32 query rows in registers as the B operand;
-//   * the key units of the block's selected key blocks stream through LDS, double
-//     buffered: K as [64 keys][128] bf16 (row-major) and V as [128][64 keys] float16 (the
-//     per-unit transposed copy written by the planner), both XOR-swizzled by 16-byte chunk
-//     so the MFMA operand reads are free of bank conflicts;
+//   * the key units of the block's selected key blocks stream through a two-stage LDS ring
+//     filled by direct global->LDS copies: K as [64 keys][128] bf16 (row-major) and V as
+//     [128][64 keys] float16 (the per-unit transposed copy written by the planner), both
+//     XOR-swizzled by 16-byte chunk so the MFMA operand reads are free of bank conflicts;
 //   * the softmax weights go to the PV product as float16 scaled by 2^10 (11-bit
 //     significands where bf16 has 8: at 2K, value rows reach |v| ~ 20 and the PV sums
 //     cancel, so bf16 weights cost ~3e-2 absolute); the row sum is kept in float64;
@@ -66,7 +66,99 @@ struct UnitCursor {
 
 constexpr int NW = 4;
 
-__global__ void __launch_bounds__(NW * 64)
+// Two LDS stages (distinct objects, named statically by the unrolled unit loop) filled by
+// direct global->LDS copies: waves 0-1 copy the K rows, waves 2-3 the V^T rows of a unit,
+// 8 instructions of 1 KB each.
+struct FwdStage {
+  uint8_t k[16384];   // [64 keys][128] bf16, swizzled
+  uint8_t vt[16384];  // [128][64 keys] f16, swizzled
+};
+__shared__ __align__(16) FwdStage g_fwd0;
+__shared__ __align__(16) FwdStage g_fwd1;
+template <int S>
+__device__ __forceinline__ const FwdStage &fwd_stage() {
+  return S ? g_fwd1 : g_fwd0;
+}
+
+struct FwdState {
+  bf16x8 qreg[8];
+  f32x16 o[4];
+  float m, mk;
+  double lsum;
+};
+
+template <int S>
+__device__ __forceinline__ void fwd_unit(FwdState &w, int l32, int hh, float scale_log2e) {
+  const uint8_t *Kt = fwd_stage<S>().k, *Vt = fwd_stage<S>().vt;
+  // S^T for keys 0-31 (a = 0) and 32-63 (a = 1): lane = query l32, 16 keys per tile
+  f32x16 s[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int r = 32 * a + l32;
+    bf16x8 ka[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      ka[kk] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4 *>(Kt + k_lds_off(r, 2 * kk + hh)));
+    __builtin_amdgcn_sched_barrier(0);
+    s[a] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) s[a] = mfma_bf16(ka[kk], w.qreg[kk], s[a]);
+  }
+  // online softmax (log2 domain) with lazy rescaling: the running max only moves when a
+  // query's new maximum exceeds it by more than 2^kLazy, so the float16 weights
+  // 2^(t - m + 10) stay below 2^15
+  float tmax = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+  for (int v = 2; v < 16; v += 2) tmax = fmaxf(tmax, fmaxf(s[0][v], s[0][v + 1]));
+#pragma unroll
+  for (int v = 0; v < 16; v += 2) tmax = fmaxf(tmax, fmaxf(s[1][v], s[1][v + 1]));
+  {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
+                                               false, false);
+    tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
+  const float tm = tmax * scale_log2e;
+  const bool grow = tm > w.m + kLazy;
+  if (__ballot(grow)) {
+    const float mnew = grow ? tm : w.m;
+    const float alpha = __builtin_amdgcn_exp2f(w.m - mnew);
+    w.m = mnew;
+    w.mk = mnew - kPShift;
+    w.lsum *= (double)alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) w.o[dt][v] *= alpha;
+  }
+  float psum = 0.f;
+  f16x8 pb[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[g >> 1][8 * (g & 1) + e], scale_log2e, -w.mk));
+      psum += p;
+      pb[g][e] = (_Float16)p;
+    }
+  w.lsum += (double)psum;
+  // O^T[d][q] += V^T[d][keys] P^T[keys][q]
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int d = 32 * dt + l32;
+    f16x8 va[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      va[g] = __builtin_bit_cast(
+          f16x8, *reinterpret_cast<const u32x4 *>(Vt + vt_lds_off(d, 2 * g + hh)));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) w.o[dt] = mfma_f16(va[g], pb[g], w.o[dt]);
+  }
+}
+
+// two waves per SIMD (2 workgroups per CU: 64 KB of LDS and <= 256 VGPRs each)
+__global__ void __launch_bounds__(NW * 64, 2)
     attn_fwd_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
                          const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
                          const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vpt,
@@ -76,12 +168,21 @@ __global__ void __launch_bounds__(NW * 64)
                          float scale_log2e, uint16_t *__restrict__ out,
                          float *__restrict__ lse_out, float *__restrict__ o32p,
                          float *__restrict__ lsep) {
-  constexpr int NT = NW * 64;
-  constexpr int CPT = 1024 / NT;  // 16-byte chunks per thread per tile (K and V^T each)
-  __shared__ __align__(16) uint8_t lds[2][2][16384];  // [buffer][K, V^T]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   const int ntiles = *tile_count;
+  // copies of this wave: K rows 32w.. (w < 2) or V^T rows 64(w-2).. (w >= 2)
+  const uint8_t *csrc =
+      reinterpret_cast<const uint8_t *>(wave < 2 ? kp : vpt) + (wave & 1) * 8192;
+  const int cdst = (wave < 2 ? 0 : 16384) + (wave & 1) * 8192;
+  auto cofs = [&](int i) {
+    if (wave < 2) {
+      const int r = 32 * wave + 4 * i + (lane >> 4);
+      return (4 * i + (lane >> 4)) * 256 + (((lane & 15) ^ (r & 15)) << 4);
+    }
+    const int d = 64 * (wave - 2) + 8 * i + (lane >> 3);
+    return (8 * i + (lane >> 3)) * 128 + (((lane & 7) ^ ((d >> 1) & 7)) << 4);
+  };
 
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int2 tl = tiles[t];
@@ -95,124 +196,51 @@ __global__ void __launch_bounds__(NW * 64)
 
     // this wave's 32 query rows as B operands: Q[row][16kk + 8hh .. +8]
     const int row0 = u0 * kUnit + wave * 32;
-    const uint16_t *qrow = qp + ((size_t)h * N + row0 + l32) * kD + 8 * hh;
-    bf16x8 qreg[8];
+    FwdState w;
     if (active) {
+      const uint16_t *qrow = qp + ((size_t)h * N + row0 + l32) * kD + 8 * hh;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
-        qreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 16 * kk));
+        w.qreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 16 * kk));
     }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) w.o[dt] = f32x16{};
+    w.m = -INFINITY;
+    w.mk = -INFINITY;
+    w.lsum = 0.0;
 
-    const uint8_t *kbase = reinterpret_cast<const uint8_t *>(kp) + (size_t)h * N * kD * 2;
-    const uint8_t *vbase = reinterpret_cast<const uint8_t *>(vpt) + (size_t)h * N * kD * 2;
-    u32x4 pk[CPT], pv[CPT];
-    auto gload = [&](int u) {
-      const uint8_t *ks = kbase + (size_t)u * kUnit * kD * 2;
-      const uint8_t *vs = vbase + (size_t)u * kUnit * kD * 2;
+    const uint8_t *hbase = csrc + (size_t)h * N * kD * 2;
+    auto issue0 = [&](int u) {
+      const uint8_t *src = hbase + (size_t)u * kUnit * kD * 2;
 #pragma unroll
-      for (int e = 0; e < CPT; ++e) {
-        int q = tid + NT * e;
-        pk[e] = *reinterpret_cast<const u32x4 *>(ks + 16 * q);
-        pv[e] = *reinterpret_cast<const u32x4 *>(vs + 16 * q);
-      }
+      for (int i = 0; i < 8; ++i)
+        dma16(src + cofs(i), reinterpret_cast<uint8_t *>(&g_fwd0) + cdst + 1024 * i);
     };
-    auto lstore = [&](int buf) {
+    auto issue1 = [&](int u) {
+      const uint8_t *src = hbase + (size_t)u * kUnit * kD * 2;
 #pragma unroll
-      for (int e = 0; e < CPT; ++e) {
-        int q = tid + NT * e;
-        *reinterpret_cast<u32x4 *>(&lds[buf][0][k_lds_off(q >> 4, q & 15)]) = pk[e];
-        *reinterpret_cast<u32x4 *>(&lds[buf][1][vt_lds_off(q >> 3, q & 7)]) = pv[e];
-      }
+      for (int i = 0; i < 8; ++i)
+        dma16(src + cofs(i), reinterpret_cast<uint8_t *>(&g_fwd1) + cdst + 1024 * i);
     };
 
-    f32x16 o[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-    // running max of the scaled logits (log2 domain) and its shifted copy used in exp2
-    float m = -INFINITY, mk = -INFINITY;
-    double lsum = 0.0;
-
-    __syncthreads();  // previous tile's readers are done with both buffers
-    gload(cur.unit());
-    lstore(0);
-    __syncthreads();
-    int buf = 0;
+    __builtin_amdgcn_s_barrier();  // every wave is done with the previous tile's stages
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    issue0(cur.unit());
     while (true) {
-      const bool more = cur.next();
-      if (more) gload(cur.unit());
-      const uint8_t *Kt = lds[buf][0], *Vt = lds[buf][1];
-      if (active) {
-        // S^T for keys 0-31 (a = 0) and 32-63 (a = 1): lane = query l32, 16 keys per tile
-        f32x16 s[2];
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          s[a] = f32x16{};
-          const int r = 32 * a + l32;
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            bf16x8 ka = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4 *>(Kt + k_lds_off(r, 2 * kk + hh)));
-            s[a] = mfma_bf16(ka, qreg[kk], s[a]);
-          }
-        }
-        // online softmax (log2 domain) with lazy rescaling: the running max only moves when
-        // a query's new maximum exceeds it by more than 2^kLazy, so the float16 weights
-        // 2^(t - m + 10) stay below 2^15
-        float tmax = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-        for (int v = 2; v < 16; v += 2) tmax = fmaxf(tmax, fmaxf(s[0][v], s[0][v + 1]));
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) tmax = fmaxf(tmax, fmaxf(s[1][v], s[1][v + 1]));
-        {
-          auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax),
-                                                     __float_as_uint(tmax), false, false);
-          tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        const float tm = tmax * scale_log2e;
-        const bool grow = tm > m + kLazy;
-        if (__ballot(grow)) {
-          const float mnew = grow ? tm : m;
-          const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-          m = mnew;
-          mk = mnew - kPShift;
-          lsum *= (double)alpha;
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
-        }
-        float psum = 0.f;
-        f16x8 pb[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p =
-                __builtin_amdgcn_exp2f(fmaf(s[g >> 1][8 * (g & 1) + e], scale_log2e, -mk));
-            psum += p;
-            pb[g][e] = (_Float16)p;
-          }
-        lsum += (double)psum;
-        // O^T[d][q] += V^T[d][keys] P^T[keys][q]
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int d = 32 * dt + l32;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f16x8 va = __builtin_bit_cast(
-                f16x8, *reinterpret_cast<const u32x4 *>(Vt + vt_lds_off(d, 2 * g + hh)));
-            o[dt] = mfma_f16(va, pb[g], o[dt]);
-          }
-        }
-      }  // active
+      bool more = cur.next();
+      wait_copies_and_sync();  // stage 0 has landed everywhere; stage 1 is free
+      if (more) issue1(cur.unit());
+      if (active) fwd_unit<0>(w, l32, hh, scale_log2e);
       if (!more) break;
-      lstore(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
+      more = cur.next();
+      wait_copies_and_sync();  // stage 1 has landed everywhere; stage 0 is free
+      if (more) issue0(cur.unit());
+      if (active) fwd_unit<1>(w, l32, hh, scale_log2e);
+      if (!more) break;
     }
     // epilogue
     if (!active) continue;
-    const double ltot = lsum + __shfl_xor(lsum, 32, 64);  // the two half waves' keys
+    const double ltot = w.lsum + __shfl_xor(w.lsum, 32, 64);  // the two half waves' keys
     const float inv = (float)(1.0 / ltot);
     const int prow = row0 + l32;
     const int token = perm[(size_t)h * N + prow];
@@ -223,14 +251,14 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         const int d0 = 32 * dt + 8 * v4 + 4 * hh;
-        const float a0 = o[dt][4 * v4 + 0] * inv, a1 = o[dt][4 * v4 + 1] * inv,
-                    a2 = o[dt][4 * v4 + 2] * inv, a3 = o[dt][4 * v4 + 3] * inv;
+        const float a0 = w.o[dt][4 * v4 + 0] * inv, a1 = w.o[dt][4 * v4 + 1] * inv,
+                    a2 = w.o[dt][4 * v4 + 2] * inv, a3 = w.o[dt][4 * v4 + 3] * inv;
         uint32_t lo = (uint32_t)f32_to_bf16(a0) | ((uint32_t)f32_to_bf16(a1) << 16);
         uint32_t hi = (uint32_t)f32_to_bf16(a2) | ((uint32_t)f32_to_bf16(a3) << 16);
         *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{lo, hi};
         *reinterpret_cast<f32x4 *>(frow + d0) = f32x4{a0, a1, a2, a3};
       }
-    const float lse = (float)(((double)m - kPShift + log2(ltot)) * 0.69314718055994530942);
+    const float lse = (float)(((double)w.m - kPShift + log2(ltot)) * 0.69314718055994530942);
     if (hh == 0) {
       lse_out[(size_t)h * N + token] = lse;
       lsep[(size_t)h * N + prow] = lse;

@@ -120,6 +120,24 @@ __device__ __forceinline__ f32x16 mfma_f16(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// Direct global -> LDS copies (global_load_lds): lane l of one instruction writes its
+// 16 (or 4) bytes at dst + 16 * l (4 * l); dst must be uniform across the wave.
+__device__ __forceinline__ void dma16(const void *src, void *dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                   (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *src, void *dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                   (__attribute__((address_space(3))) void *)dst, 4, 0, 0);
+}
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone), then a workgroup barrier that the
+// compiler may not move memory operations across.
+__device__ __forceinline__ void wait_copies_and_sync() {
+  __builtin_amdgcn_s_waitcnt(0x0070 | 0x0f00);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // bfloat16 -> float16 bits (exact inside the float16 range; saturates beyond +-65504).
 __device__ __forceinline__ uint16_t bf16_to_f16_bits(uint16_t b) {
   float f = fminf(fmaxf(bf16_to_f32(b), -65504.f), 65504.f);
