@@ -8,7 +8,11 @@
 //   dv_y = sum_x P_xy do_x,  dk_y = scale sum_x dS_xy q_x,  dq_x = scale sum_y dS_xy k_y.
 // Three passes, none with atomics (results are bit-reproducible):
 //   prep  -- gathers dO into the permuted layout (row-major and per-unit transposed) and
-//            forms delta from the float32 output the forward kept;
+//            forms delta from the float32 output the forward kept;  for bfloat16 it also
+//            folds the constants of the two MFMA passes into their inputs: the row-major dO
+//            copy is scaled by 2^-10 and delta stored as -delta * 2^-10 (so the dP
+//            accumulator starts at -delta and ends at (dP - delta) * 2^-10), and lse is
+//            stored as lse * log2(e) - 10 (so the exp2 gives P * 2^10 directly);
 //   dK/dV -- one workgroup per key tile (32 keys per wave, K and V rows held in registers),
 //            streaming the 64-token query units of every query block that selected the
 //            key block (the transposed selection lists);
@@ -37,8 +41,9 @@ __device__ __forceinline__ int swap23b(int e) {
 template <typename T, int D, bool TRANSPOSE>
 __global__ void __launch_bounds__(256)
     bwd_prep_kernel(int N, int heads, const int *__restrict__ perm, const T *__restrict__ dout,
-                    const float *__restrict__ o32p, T *__restrict__ dop, T *__restrict__ dopt,
-                    float *__restrict__ delta) {
+                    const float *__restrict__ o32p, const float *__restrict__ lsep,
+                    T *__restrict__ dop, T *__restrict__ dopt, float *__restrict__ delta,
+                    float *__restrict__ lse2) {
   constexpr int VPC = 16 / (int)sizeof(T);
   constexpr int CH = D / VPC;
   constexpr int RG = 256 / CH;
@@ -53,7 +58,19 @@ __global__ void __launch_bounds__(256)
     const size_t p = (size_t)u * kUnit + row;
     const int token = perm[(size_t)h * N + p];
     u32x4 a = *reinterpret_cast<const u32x4 *>(dout + token * tstride + (size_t)h * D + c * VPC);
-    *reinterpret_cast<u32x4 *>(dop + ((size_t)h * N + p) * D + c * VPC) = a;
+    if constexpr (TRANSPOSE) {
+      // dO * 2^-kPShift: an exact power-of-two scaling of each bfloat16
+      u32x4 sc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(a[e] << 16) * (1.f / kPScale);
+        const float hi = __uint_as_float(a[e] & 0xffff0000u) * (1.f / kPScale);
+        sc[e] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+      }
+      *reinterpret_cast<u32x4 *>(dop + ((size_t)h * N + p) * D + c * VPC) = sc;
+    } else {
+      *reinterpret_cast<u32x4 *>(dop + ((size_t)h * N + p) * D + c * VPC) = a;
+    }
     const float *orow = o32p + ((size_t)h * N + p) * D + c * VPC;
     float dot = 0.f;
     if constexpr (sizeof(T) == 2) {
@@ -72,7 +89,14 @@ __global__ void __launch_bounds__(256)
     }
 #pragma unroll
     for (int off = 1; off < CH; off <<= 1) dot += __shfl_xor(dot, off, 64);
-    if (c == 0) delta[(size_t)h * N + p] = dot;
+    if (c == 0) {
+      if constexpr (TRANSPOSE) {
+        delta[(size_t)h * N + p] = -dot * (1.f / kPScale);
+        lse2[(size_t)h * N + p] = lsep[(size_t)h * N + p] * 1.4426950408889634f - kPShift;
+      } else {
+        delta[(size_t)h * N + p] = dot;
+      }
+    }
     if constexpr (TRANSPOSE) *reinterpret_cast<u32x4 *>(&tile[row * D + c * VPC]) = a;
   }
   if constexpr (TRANSPOSE) {
@@ -99,100 +123,160 @@ __global__ void __launch_bounds__(256)
 constexpr int NW = 4;
 
 // ============================================================================ dQ (bf16)
+// One workgroup of four waves per query tile (32 queries per wave, Q and dO rows held as B
+// operands), streaming the selected key units through a two-stage LDS ring of direct
+// global->LDS copies as in the forward: per stage K and V row-major [64][128] bf16 and
+// K^T [128][64] f16 (48 KB); each wave issues 12 of the 48 one-kilobyte copies.
+struct DqStage {
+  uint8_t tile[3][16384];  // K, V, K^T
+};
+__shared__ __align__(16) DqStage g_dq0;
+__shared__ __align__(16) DqStage g_dq1;
+template <int S>
+__device__ __forceinline__ const DqStage &dq_stage() {
+  return S ? g_dq1 : g_dq0;
+}
+
+struct DqState {
+  bf16x8 qreg[8], doreg[8];
+  f32x16 acc[4];
+  float lse2, ndlt;
+};
+
+template <int S>
+__device__ __forceinline__ void dq_unit(DqState &w, int l32, int hh, float scale_log2e) {
+  const DqStage &sg = dq_stage<S>();
+  f16x8 db[4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {  // keys 32a .. 32a + 31
+    const int r = 32 * a + l32;
+    bf16x8 ka[8], va[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      ka[kk] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4 *>(sg.tile[0] + rm_off(r, 2 * kk + hh)));
+      va[kk] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4 *>(sg.tile[1] + rm_off(r, 2 * kk + hh)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s = f32x16{}, dp;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dp[v] = w.ndlt;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      s = mfma_bf16(ka[kk], w.qreg[kk], s);
+      dp = mfma_bf16(va[kk], w.doreg[kk], dp);
+    }
+    // lane = query, register v = key 32a + (v/4)*8 + 4hh + v%4;  P * 2^10 times
+    // (dP - delta) * 2^-10
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[v], scale_log2e, -w.lse2));
+      db[2 * a + (v >> 3)][v & 7] = (_Float16)(p * dp[v]);
+    }
+  }
+  // dQ^T[d][q] += K^T[d][keys] dS^T[keys][q]
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int d = 32 * dt + l32;
+    f16x8 kt[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      kt[g] = __builtin_bit_cast(
+          f16x8, *reinterpret_cast<const u32x4 *>(sg.tile[2] + tr_off(d, 2 * g + hh)));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) w.acc[dt] = mfma_f16(kt[g], db[g], w.acc[dt]);
+  }
+}
+
 __global__ void __launch_bounds__(NW * 64)
     attn_dq_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
                         const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
                         const uint16_t *__restrict__ kp, const uint16_t *__restrict__ kpt,
                         const uint16_t *__restrict__ vp, const uint16_t *__restrict__ dop,
-                        const float *__restrict__ lsep, const float *__restrict__ delta,
+                        const float *__restrict__ lse2, const float *__restrict__ ndelta,
                         const int *__restrict__ unit_blk, const int *__restrict__ blk_start,
                         const int *__restrict__ blk_size, const int *__restrict__ sel_count,
                         const int *__restrict__ csr_col, const int *__restrict__ perm,
                         float scale, float scale_log2e, uint16_t *__restrict__ dq) {
-  constexpr int NT = NW * 64;
-  constexpr int CPT = 1024 / NT;
-  __shared__ __align__(16) uint8_t lds[3][16384];  // K, V (row-major), K^T
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   const int ntiles = *tile_count;
+  // copy j in 12*wave .. 12*wave + 11 of [K (16), V (16), K^T (16)] one-kilobyte copies
+  auto csrc_of = [&](int j) -> const uint8_t * {
+    const int tsel = j >> 4;
+    return reinterpret_cast<const uint8_t *>(tsel == 0 ? kp : (tsel == 1 ? vp : kpt));
+  };
+  auto cofs = [&](int j) {
+    const int i = j & 15;
+    if (j < 32) {
+      const int r = 4 * i + (lane >> 4);
+      return r * 256 + (((lane & 15) ^ (r & 15)) << 4);
+    }
+    const int d = 8 * i + (lane >> 3);
+    return d * 128 + (((lane & 7) ^ ((d >> 1) & 7)) << 4);
+  };
+
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int2 tl = tiles[t];
     const int h = tl.x, u0 = tl.y & (kTile64 - 1);
     const bool active = !(tl.y & kTile64) || wave < 2;
     const int blk = unit_blk[(size_t)h * U + u0];
-    const int ncols = sel_count[(size_t)h * nb_max + blk];
-    const int *cols = csr_col + ((size_t)h * nb_max + blk) * nb_max;
     const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
+    BlockUnits cur;
+    cur.init(csr_col + ((size_t)h * nb_max + blk) * nb_max,
+             sel_count[(size_t)h * nb_max + blk], bs, bz, lane);
     const int row0 = u0 * kUnit + wave * 32;
-    bf16x8 qreg[8], doreg[8];
-    float lse2 = 0.f, dlt = 0.f;
+    DqState w;
+    w.lse2 = 0.f;
+    w.ndlt = 0.f;
     if (active) {
       const uint16_t *qr = qp + ((size_t)h * N + row0 + l32) * kDB + 8 * hh;
       const uint16_t *dr = dop + ((size_t)h * N + row0 + l32) * kDB + 8 * hh;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        qreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qr + 16 * kk));
-        doreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(dr + 16 * kk));
+        w.qreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qr + 16 * kk));
+        w.doreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(dr + 16 * kk));
       }
+      w.lse2 = lse2[(size_t)h * N + row0 + l32];
+      w.ndlt = ndelta[(size_t)h * N + row0 + l32];
     }
-    if (active) {
-      lse2 = lsep[(size_t)h * N + row0 + l32] * 1.4426950408889634f;
-      dlt = delta[(size_t)h * N + row0 + l32];
-    }
-    f32x16 acc[4];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
-    for (int c = 0; c < ncols; ++c) {
-      const int j = cols[c];
-      const int us = bs[j] / kUnit, nu = bz[j] / kUnit;
-      for (int u = us; u < us + nu; ++u) {
-        __syncthreads();
-        const size_t ub = ((size_t)h * N + (size_t)u * kUnit) * kDB * 2;
+    for (int dt = 0; dt < 4; ++dt) w.acc[dt] = f32x16{};
+
+    const size_t hb = (size_t)h * N * kDB * 2;
+    auto issue0 = [&](int u) {
 #pragma unroll
-        for (int e = 0; e < CPT; ++e) {
-          const int q = tid + NT * e;
-          *reinterpret_cast<u32x4 *>(&lds[0][rm_off(q >> 4, q & 15)]) =
-              *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint8_t *>(kp) + ub + 16 * q);
-          *reinterpret_cast<u32x4 *>(&lds[1][rm_off(q >> 4, q & 15)]) =
-              *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint8_t *>(vp) + ub + 16 * q);
-          *reinterpret_cast<u32x4 *>(&lds[2][tr_off(q >> 3, q & 7)]) =
-              *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint8_t *>(kpt) + ub + 16 * q);
-        }
-        __syncthreads();
-        if (!active) continue;
-        f16x8 db[4];
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {  // keys 32a .. 32a + 31
-          f32x16 s = f32x16{}, dp = f32x16{};
-          const int r = 32 * a + l32;
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            bf16x8 ka = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4 *>(&lds[0][rm_off(r, 2 * kk + hh)]));
-            bf16x8 va = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4 *>(&lds[1][rm_off(r, 2 * kk + hh)]));
-            s = mfma_bf16(ka, qreg[kk], s);
-            dp = mfma_bf16(va, doreg[kk], dp);
-          }
-          // lane = query, register v = key 32a + (v/4)*8 + 4hh + v%4
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[v], scale_log2e, -lse2));
-            db[2 * a + (v >> 3)][v & 7] = (_Float16)(p * (dp[v] - dlt));
-          }
-        }
-        // dQ^T[d][q] += K^T[d][keys] dS^T[keys][q]
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int d = 32 * dt + l32;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f16x8 kt = __builtin_bit_cast(
-                f16x8, *reinterpret_cast<const u32x4 *>(&lds[2][tr_off(d, 2 * g + hh)]));
-            acc[dt] = mfma_f16(kt, db[g], acc[dt]);
-          }
-        }
+      for (int e = 0; e < 12; ++e) {
+        const int j = 12 * wave + e;
+        dma16(csrc_of(j) + hb + (size_t)u * kUnit * kDB * 2 + cofs(j),
+              g_dq0.tile[j >> 4] + 1024 * (j & 15));
       }
+    };
+    auto issue1 = [&](int u) {
+#pragma unroll
+      for (int e = 0; e < 12; ++e) {
+        const int j = 12 * wave + e;
+        dma16(csrc_of(j) + hb + (size_t)u * kUnit * kDB * 2 + cofs(j),
+              g_dq1.tile[j >> 4] + 1024 * (j & 15));
+      }
+    };
+
+    __builtin_amdgcn_s_barrier();  // every wave is done with the previous tile's stages
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    issue0(cur.unit());
+    while (true) {
+      bool more = cur.next();
+      wait_copies_and_sync();
+      if (more) issue1(cur.unit());
+      if (active) dq_unit<0>(w, l32, hh, scale_log2e);
+      if (!more) break;
+      more = cur.next();
+      wait_copies_and_sync();
+      if (more) issue0(cur.unit());
+      if (active) dq_unit<1>(w, l32, hh, scale_log2e);
+      if (!more) break;
     }
     if (!active) continue;
     const int token = perm[(size_t)h * N + row0 + l32];
@@ -202,10 +286,10 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         const int d0 = 32 * dt + 8 * v4 + 4 * hh;
-        uint32_t lo = (uint32_t)f32_to_bf16(acc[dt][4 * v4] * scale) |
-                      ((uint32_t)f32_to_bf16(acc[dt][4 * v4 + 1] * scale) << 16);
-        uint32_t hi = (uint32_t)f32_to_bf16(acc[dt][4 * v4 + 2] * scale) |
-                      ((uint32_t)f32_to_bf16(acc[dt][4 * v4 + 3] * scale) << 16);
+        uint32_t lo = (uint32_t)f32_to_bf16(w.acc[dt][4 * v4] * scale) |
+                      ((uint32_t)f32_to_bf16(w.acc[dt][4 * v4 + 1] * scale) << 16);
+        uint32_t hi = (uint32_t)f32_to_bf16(w.acc[dt][4 * v4 + 2] * scale) |
+                      ((uint32_t)f32_to_bf16(w.acc[dt][4 * v4 + 3] * scale) << 16);
         *reinterpret_cast<u32x2 *>(qrow + d0) = u32x2{lo, hi};
       }
   }
@@ -354,7 +438,7 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
   const int *cols = (const int *)(ws + L.pub.csr_col);
   const int *tcnt = (const int *)(ws + L.pub.csc_count);
   const int *trows = (const int *)(ws + L.pub.csc_row);
-  float *delta = (float *)(ws + L.delta);
+  float *delta = (float *)(ws + L.delta), *lse2 = (float *)(ws + L.lse2);
   const float *lsep = (const float *)(ws + L.lsep), *o32p = (const float *)(ws + L.o32p);
   dim3 ugrid(d.U, d.heads);
   if (d.dtype == PRISM_BF16) {
@@ -362,8 +446,8 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
     {
       TraceScope tr(PRISM_STAGE_BWD_PREP, s);
       hipLaunchKernelGGL((bwd_prep_kernel<T, 128, true>), ugrid, dim3(256), 0, s, d.N, d.heads,
-                       perm, (const T *)dout, o32p, (T *)(ws + L.dop), (T *)(ws + L.dopt),
-                       delta);
+                       perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop),
+                       (T *)(ws + L.dopt), delta, lse2);
     }
     const int *counters = (const int *)(ws + L.counters);
     const float sl2e = scale * 1.4426950408889634f;
@@ -376,14 +460,14 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
     {
       TraceScope tr(PRISM_STAGE_BWD_DKDV, s);
       launch_dkdv_bf16(maxt, s, d.N, d.U, d.nb_max, d.heads, tiles, counters, qp, qpt, kp, vp,
-                       dop, dopt, lsep, delta, unit_blk, bstart, bsize, tcnt, trows, perm, scale,
+                       dop, dopt, lse2, delta, unit_blk, bstart, bsize, tcnt, trows, perm, scale,
                        sl2e, (T *)dk, (T *)dv);
     }
     {
       TraceScope tr(PRISM_STAGE_BWD_DQ, s);
       const int grid = resident_grid((const void *)attn_dq_bf16_kernel, NW * 64, maxt);
       hipLaunchKernelGGL(attn_dq_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, d.N, d.U,
-                         d.nb_max, d.heads, tiles, counters, qp, kp, kpt, vp, dop, lsep, delta,
+                         d.nb_max, d.heads, tiles, counters, qp, kp, kpt, vp, dop, lse2, delta,
                          unit_blk, bstart, bsize, cnt, cols, perm, scale, sl2e, (T *)dq);
     }
   } else {
@@ -393,7 +477,8 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
             *vp = (const T *)(ws + L.vp), *dop = (const T *)(ws + L.dop);
     if (d.D == 64) {
       hipLaunchKernelGGL((bwd_prep_kernel<T, 64, false>), ugrid, dim3(256), 0, s, d.N, d.heads,
-                         perm, (const T *)dout, o32p, (T *)(ws + L.dop), nullptr, delta);
+                         perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop), nullptr, delta,
+                         nullptr);
       hipLaunchKernelGGL((attn_dq_f32_kernel<64>), ugrid, dim3(256), 0, s, d.N, d.U, d.nb_max,
                          d.heads, qp, kp, vp, dop, lsep, delta, unit_blk, bstart, bsize, cnt,
                          cols, perm, scale, (T *)dq);
@@ -402,8 +487,8 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
                          bsize, tcnt, trows, perm, scale, (T *)dk, (T *)dv);
     } else {
       hipLaunchKernelGGL((bwd_prep_kernel<T, 128, false>), ugrid, dim3(256), 0, s, d.N,
-                         d.heads, perm, (const T *)dout, o32p, (T *)(ws + L.dop), nullptr,
-                         delta);
+                         d.heads, perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop),
+                         nullptr, delta, nullptr);
       hipLaunchKernelGGL((attn_dq_f32_kernel<128>), ugrid, dim3(256), 0, s, d.N, d.U, d.nb_max,
                          d.heads, qp, kp, vp, dop, lsep, delta, unit_blk, bstart, bsize, cnt,
                          cols, perm, scale, (T *)dq);

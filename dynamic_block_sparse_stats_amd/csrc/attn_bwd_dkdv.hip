@@ -33,38 +33,12 @@ __device__ __forceinline__ int tr_off(int d, int c) {  // [128][64] f16 tile, 8 
 // the barrier that publishes the current one and overlaps its 64 MFMAs.
 constexpr int NW = 4;
 
-struct QueryUnits {  // the 64-token units of the listed query blocks, in order
-  int idx, sub, us, nu, n;
-  const int *list, *bstart, *bsize;
-  __device__ void load() {
-    const int i = list[idx];
-    us = bstart[i] / kUnit;
-    nu = bsize[i] / kUnit;
-  }
-  __device__ void init(const int *l, int count, const int *bs, const int *bz) {
-    list = l;
-    n = count;
-    bstart = bs;
-    bsize = bz;
-    idx = sub = 0;
-    load();
-  }
-  __device__ int unit() const { return us + sub; }
-  __device__ bool next() {
-    if (++sub < nu) return true;
-    sub = 0;
-    if (++idx >= n) return false;
-    load();
-    return true;
-  }
-};
-
 // The two stages are distinct LDS objects and the unit loop is unrolled by two, so every
 // LDS read names its stage statically; the compiler can then see that the copies in flight
 // (into the other stage) do not feed the reads, and issues no wait for them.
 struct Stage {
   uint8_t tile[4][16384];  // Q, dO (row-major bf16), Q^T, dO^T (f16)
-  float vec[4][kUnit];     // lse, delta, unused, unused
+  float vec[4][kUnit];     // lse * log2(e) - 10, -delta * 2^-10, unused, unused
 };
 __shared__ __align__(16) Stage g_stage0;
 __shared__ __align__(16) Stage g_stage1;
@@ -93,28 +67,31 @@ __device__ __forceinline__ void dkdv_unit(DkdvState &w, int l32, int hh, float s
       da[kk] = __builtin_bit_cast(
           bf16x8, *reinterpret_cast<const u32x4 *>(sg.tile[1] + rm_off(r, 2 * kk + hh)));
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep the 16 reads ahead of the MFMAs below
-    f32x16 sacc = f32x16{}, dp = f32x16{};
+    // per query row of the C layout: lse * log2(e) - 10 and -delta * 2^-10
+    f32x4 l4[4], d4[4];
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int q0 = 32 * a + 8 * v4 + 4 * hh;
+      l4[v4] = *reinterpret_cast<const f32x4 *>(sg.vec[0] + q0);
+      d4[v4] = *reinterpret_cast<const f32x4 *>(sg.vec[1] + q0);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs below
+    f32x16 sacc = f32x16{}, dp;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dp[v] = d4[v >> 2][v & 3];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       sacc = mfma_bf16(qa[kk], w.kreg[kk], sacc);
       dp = mfma_bf16(da[kk], w.vreg[kk], dp);
     }
-    // C layout: lane = key l32, register v = query 32a + (v/4)*8 + 4hh + v%4
+    // C layout: lane = key l32, register v = query 32a + (v/4)*8 + 4hh + v%4;  p is
+    // P * 2^10 and dp is (dP - delta) * 2^-10
 #pragma unroll
-    for (int v4 = 0; v4 < 4; ++v4) {
-      const int q0 = 32 * a + 8 * v4 + 4 * hh;
-      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sg.vec[0] + q0);
-      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sg.vec[1] + q0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int v = 4 * v4 + e;
-        const float p =
-            __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2e, -l4[e] * 1.4426950408889634f));
-        const int g = 2 * a + (v >> 3), slot = v & 7;
-        pb[g][slot] = (_Float16)(p * kPScale);
-        db[g][slot] = (_Float16)(p * (dp[v] - d4[e]));
-      }
+    for (int v = 0; v < 16; ++v) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2e, -l4[v >> 2][v & 3]));
+      const int g = 2 * a + (v >> 3), slot = v & 7;
+      pb[g][slot] = (_Float16)p;
+      db[g][slot] = (_Float16)(p * dp[v]);
     }
   }
   // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
@@ -143,7 +120,7 @@ __global__ void __launch_bounds__(NW * 64)
                           const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
                           const uint16_t *__restrict__ qpt, const uint16_t *__restrict__ kp,
                           const uint16_t *__restrict__ vp, const uint16_t *__restrict__ dop,
-                          const uint16_t *__restrict__ dopt, const float *__restrict__ lsep,
+                          const uint16_t *__restrict__ dopt, const float *__restrict__ lse2,
                           const float *__restrict__ delta, const int *__restrict__ unit_blk,
                           const int *__restrict__ blk_start, const int *__restrict__ blk_size,
                           const int *__restrict__ csc_count, const int *__restrict__ csc_row,
@@ -154,7 +131,7 @@ __global__ void __launch_bounds__(NW * 64)
   const int ntiles = *tile_count;
   const uint8_t *tsrc = reinterpret_cast<const uint8_t *>(
       wave == 0 ? qp : (wave == 1 ? dop : (wave == 2 ? qpt : dopt)));
-  const float *vsrc = wave == 1 ? delta : lsep;
+  const float *vsrc = wave == 1 ? delta : lse2;
   // this lane's byte offset inside copy i (1 KB) of its wave's tile: rows 4i.. (row-major
   // tiles) or 8i.. (transposed tiles); the swizzle only depends on the row within 16 / 8
   auto lofs = [&](int i) {
@@ -206,8 +183,8 @@ __global__ void __launch_bounds__(NW * 64)
     __builtin_amdgcn_s_barrier();  // every wave is done with the previous tile's stages
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (nq > 0) {
-      QueryUnits cur;
-      cur.init(qlist, nq, bs, bz);
+      BlockUnits cur;
+      cur.init(qlist, nq, bs, bz, lane);
       issue0(cur.unit());
       while (true) {
         bool more = cur.next();
@@ -251,14 +228,14 @@ __global__ void __launch_bounds__(NW * 64)
 hipError_t launch_dkdv_bf16(int work_items, hipStream_t s, int N, int U, int nb_max, int heads,
                             const int2 *tiles, const int *counters, const uint16_t *qp,
                             const uint16_t *qpt, const uint16_t *kp, const uint16_t *vp,
-                            const uint16_t *dop, const uint16_t *dopt, const float *lsep,
+                            const uint16_t *dop, const uint16_t *dopt, const float *lse2,
                             const float *delta, const int *unit_blk, const int *bstart,
                             const int *bsize, const int *tcnt, const int *trows,
                             const int *perm, float scale, float sl2e, uint16_t *dk,
                             uint16_t *dv) {
   const int grid = resident_grid((const void *)attn_dkdv_bf16_kernel, NW * 64, work_items);
   hipLaunchKernelGGL(attn_dkdv_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, N, U, nb_max,
-                     heads, tiles, counters, qp, qpt, kp, vp, dop, dopt, lsep, delta, unit_blk,
+                     heads, tiles, counters, qp, qpt, kp, vp, dop, dopt, lse2, delta, unit_blk,
                      bstart, bsize, tcnt, trows, perm, scale, sl2e, dk, dv);
   return hipGetLastError();
 }

@@ -5,13 +5,15 @@
 // block 4, taken in turn; xyznot review, "Метод" item 3).
 //
 // bfloat16 path, head_dim 128, gfx950 MFMA v_mfma_f32_32x32x16_bf16:
-//   * a workgroup (4 waves) owns a query tile inside one block: 128 rows for blocks of 128
-//     or 256 tokens, 64 rows for 64-token blocks (then waves 2-3 only help stage K/V);
-//     each wave keeps its 32 query rows in registers as the B operand;
-//   * the key units of the block's selected key blocks stream through a two-stage LDS ring
-//     filled by direct global->LDS copies: K as [64 keys][128] bf16 (row-major) and V as
-//     [128][64 keys] float16 (the per-unit transposed copy written by the planner), both
-//     XOR-swizzled by 16-byte chunk so the MFMA operand reads are free of bank conflicts;
+//   * a workgroup (8 waves, two per SIMD) owns one query block: 256, 128 or 64 rows, 32
+//     per wave (waves past the block's rows only help stage K/V); each wave keeps its 32
+//     query rows in registers as the B operand; one workgroup per CU, persistent over the
+//     list of blocks;
+//   * the key units of the block's selected key blocks stream through a four-stage LDS
+//     ring (128 KB) filled by direct global->LDS copies, three units ahead of the one being
+//     computed: K as [64 keys][128] bf16 (row-major) and V as [128][64 keys] float16 (the
+//     per-unit transposed copy written by the planner), both XOR-swizzled by 16-byte chunk
+//     so the MFMA operand reads are free of bank conflicts;
 //   * the softmax weights go to the PV product as float16 scaled by 2^10 (11-bit
 //     significands where bf16 has 8: at 2K, value rows reach |v| ~ 20 and the PV sums
 //     cancel, so bf16 weights cost ~3e-2 absolute); the row sum is kept in float64;
@@ -36,50 +38,25 @@ __device__ __forceinline__ int vt_lds_off(int d, int c) {  // V^T tile: 128 rows
   return d * 128 + ((c ^ ((d >> 1) & 7)) << 4);
 }
 
-struct UnitCursor {
-  int idx, sub, us, nu, ncols;
-  const int *cols, *bstart, *bsize;
-  __device__ void load_block() {
-    int j = cols[idx];
-    us = bstart[j] / kUnit;
-    nu = bsize[j] / kUnit;
-  }
-  __device__ void init(const int *c, int n, const int *bs, const int *bz) {
-    cols = c;
-    ncols = n;
-    bstart = bs;
-    bsize = bz;
-    idx = 0;
-    sub = 0;
-    load_block();
-  }
-  __device__ int unit() const { return us + sub; }
-  // advances; false when the list is exhausted
-  __device__ bool next() {
-    if (++sub < nu) return true;
-    sub = 0;
-    if (++idx >= ncols) return false;
-    load_block();
-    return true;
-  }
-};
+constexpr int NW = 8;      // waves per workgroup: 8 x 32 = 256 query rows, one block
+constexpr int kStages = 4;  // LDS ring depth (units in flight: 3 ahead of the one computed)
+constexpr int kCpw = 32 / NW;  // 1 KB copies per wave per unit (16 for K, 16 for V^T)
 
-constexpr int NW = 4;
-
-// Two LDS stages (distinct objects, named statically by the unrolled unit loop) filled by
-// direct global->LDS copies: waves 0-1 copy the K rows, waves 2-3 the V^T rows of a unit,
-// 8 instructions of 1 KB each.
+// Four LDS stages of 32 KB (distinct objects, named statically by the unrolled unit loop)
+// filled by direct global->LDS copies: waves 0-3 copy 16 K rows each, waves 4-7 32 V^T
+// rows each, 4 instructions of 1 KB per wave and unit.
 struct FwdStage {
   uint8_t k[16384];   // [64 keys][128] bf16, swizzled
   uint8_t vt[16384];  // [128][64 keys] f16, swizzled
 };
 __shared__ __align__(16) FwdStage g_fwd0;
 __shared__ __align__(16) FwdStage g_fwd1;
+__shared__ __align__(16) FwdStage g_fwd2;
+__shared__ __align__(16) FwdStage g_fwd3;
 template <int S>
-__device__ __forceinline__ const FwdStage &fwd_stage() {
-  return S ? g_fwd1 : g_fwd0;
+__device__ __forceinline__ FwdStage &fwd_stage() {
+  return S == 0 ? g_fwd0 : (S == 1 ? g_fwd1 : (S == 2 ? g_fwd2 : g_fwd3));
 }
-
 struct FwdState {
   bf16x8 qreg[8];
   f32x16 o[4];
@@ -87,9 +64,9 @@ struct FwdState {
   double lsum;
 };
 
-template <int S>
-__device__ __forceinline__ void fwd_unit(FwdState &w, int l32, int hh, float scale_log2e) {
-  const uint8_t *Kt = fwd_stage<S>().k, *Vt = fwd_stage<S>().vt;
+__device__ __forceinline__ void fwd_unit_on(FwdState &w, const uint8_t *__restrict__ Kt,
+                                            const uint8_t *__restrict__ Vt, int l32, int hh,
+                                            float scale_log2e) {
   // S^T for keys 0-31 (a = 0) and 32-63 (a = 1): lane = query l32, 16 keys per tile
   f32x16 s[2];
 #pragma unroll
@@ -131,16 +108,20 @@ __device__ __forceinline__ void fwd_unit(FwdState &w, int l32, int hh, float sca
 #pragma unroll
       for (int v = 0; v < 16; ++v) w.o[dt][v] *= alpha;
   }
+  // the row sum adds the float16 weights the MFMA consumes (two per dot2 instruction), so
+  // the normaliser matches the weights exactly
   float psum = 0.f;
   f16x8 pb[4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+  for (int g = 0; g < 4; ++g) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[g >> 1][8 * (g & 1) + e], scale_log2e, -w.mk));
-      psum += p;
-      pb[g][e] = (_Float16)p;
-    }
+    for (int e = 0; e < 8; ++e)
+      pb[g][e] = (_Float16)__builtin_amdgcn_exp2f(
+          fmaf(s[g >> 1][8 * (g & 1) + e], scale_log2e, -w.mk));
+#pragma unroll
+    for (int e = 0; e < 8; e += 2)
+      psum = __builtin_amdgcn_fdot2(f16x2{pb[g][e], pb[g][e + 1]}, f16x2{1, 1}, psum, false);
+  }
   w.lsum += (double)psum;
   // O^T[d][q] += V^T[d][keys] P^T[keys][q]
 #pragma unroll
@@ -157,8 +138,25 @@ __device__ __forceinline__ void fwd_unit(FwdState &w, int l32, int hh, float sca
   }
 }
 
-// two waves per SIMD (2 workgroups per CU: 64 KB of LDS and <= 256 VGPRs each)
-__global__ void __launch_bounds__(NW * 64, 2)
+template <int S>
+__device__ __forceinline__ void fwd_unit(FwdState &w, int l32, int hh, float scale_log2e) {
+  fwd_unit_on(w, fwd_stage<S>().k, fwd_stage<S>().vt, l32, hh, scale_log2e);
+}
+
+// s_waitcnt vmcnt(2 kCpw) (expcnt and lgkmcnt left alone), then a workgroup barrier: every
+// wave issues exactly kCpw copies per step, so this wave's copies for the unit two steps
+// back have landed (vector memory loads complete in order), and after the barrier every
+// wave's have.  The count is the same on every path, which also lets the compiler see that
+// no further wait is needed before the LDS reads.
+__device__ __forceinline__ void wait_unit_two_behind() {
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * kCpw));
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One workgroup (8 waves, one per 32 rows; two waves per SIMD, 128 KB of LDS) per query
+// block, persistent over the block list.
+__global__ void __launch_bounds__(NW * 64)
     attn_fwd_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
                          const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
                          const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vpt,
@@ -168,31 +166,36 @@ __global__ void __launch_bounds__(NW * 64, 2)
                          float scale_log2e, uint16_t *__restrict__ out,
                          float *__restrict__ lse_out, float *__restrict__ o32p,
                          float *__restrict__ lsep) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform in the wave: in a scalar register, every branch on it (and on
+  // the block-list cursor) is a scalar branch
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   const int ntiles = *tile_count;
-  // copies of this wave: K rows 32w.. (w < 2) or V^T rows 64(w-2).. (w >= 2)
-  const uint8_t *csrc =
-      reinterpret_cast<const uint8_t *>(wave < 2 ? kp : vpt) + (wave & 1) * 8192;
-  const int cdst = (wave < 2 ? 0 : 16384) + (wave & 1) * 8192;
-  auto cofs = [&](int i) {
-    if (wave < 2) {
-      const int r = 32 * wave + 4 * i + (lane >> 4);
-      return (4 * i + (lane >> 4)) * 256 + (((lane & 15) ^ (r & 15)) << 4);
+  // copies of this wave: K rows 16w.. (w < 4) or V^T rows 32(w-4).. (w >= 4)
+  const bool kcopy = wave < NW / 2;
+  const int wq = wave & (NW / 2 - 1);
+  const uint8_t *csrc = reinterpret_cast<const uint8_t *>(kcopy ? kp : vpt);
+  const int cdst = (kcopy ? 0 : 16384) + wq * 4096;
+  auto cofs = [&](int i) {  // byte offset inside the unit of this lane's 16 bytes, copy i
+    if (kcopy) {
+      const int r = 16 * wq + 4 * i + (lane >> 4);
+      return r * 256 + (((lane & 15) ^ (r & 15)) << 4);
     }
-    const int d = 64 * (wave - 2) + 8 * i + (lane >> 3);
-    return (8 * i + (lane >> 3)) * 128 + (((lane & 7) ^ ((d >> 1) & 7)) << 4);
+    const int d = 32 * wq + 8 * i + (lane >> 3);
+    return d * 128 + (((lane & 7) ^ ((d >> 1) & 7)) << 4);
   };
 
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int2 tl = tiles[t];
-    const int h = tl.x, u0 = tl.y & (kTile64 - 1);
-    const bool active = !(tl.y & kTile64) || wave < 2;
+    const int h = __builtin_amdgcn_readfirstlane(tl.x);
+    const int ty = __builtin_amdgcn_readfirstlane(tl.y);
+    const int u0 = ty & 0xffff, rows = (ty >> 16) * kUnit;
+    const bool active = wave * 32 < rows;
     const int blk = unit_blk[(size_t)h * U + u0];
     const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
-    UnitCursor cur;
-    cur.init(csr_col + ((size_t)h * nb_max + blk) * nb_max,
-             sel_count[(size_t)h * nb_max + blk], bs, bz);
+    BlockUnits pre;  // the issuing cursor; compute only counts units
+    pre.init(csr_col + ((size_t)h * nb_max + blk) * nb_max,
+             sel_count[(size_t)h * nb_max + blk], bs, bz, lane);
 
     // this wave's 32 query rows as B operands: Q[row][16kk + 8hh .. +8]
     const int row0 = u0 * kUnit + wave * 32;
@@ -209,35 +212,51 @@ __global__ void __launch_bounds__(NW * 64, 2)
     w.mk = -INFINITY;
     w.lsum = 0.0;
 
+    // the Q rows (and the cursor's first window) have landed before any copy is issued,
+    // so no later LDS read or MFMA waits behind the copies for them
+    __builtin_amdgcn_s_waitcnt(0x0f70);
     const uint8_t *hbase = csrc + (size_t)h * N * kD * 2;
-    auto issue0 = [&](int u) {
-      const uint8_t *src = hbase + (size_t)u * kUnit * kD * 2;
+    int issued = 0;
+    bool pending = true;  // pre points at a unit not yet issued
+    // every step issues kCpw copies: past the end of the list they repeat the last unit
+    // into a stage no step reads any more (drained before the next tile)
+    auto issue = [&](FwdStage &st) {
+      const uint8_t *src = hbase + (size_t)pre.unit() * kUnit * kD * 2;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        dma16(src + cofs(i), reinterpret_cast<uint8_t *>(&g_fwd0) + cdst + 1024 * i);
-    };
-    auto issue1 = [&](int u) {
-      const uint8_t *src = hbase + (size_t)u * kUnit * kD * 2;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        dma16(src + cofs(i), reinterpret_cast<uint8_t *>(&g_fwd1) + cdst + 1024 * i);
+      for (int i = 0; i < kCpw; ++i)
+        dma16(src + cofs(i), reinterpret_cast<uint8_t *>(&st) + cdst + 1024 * i);
+      if (pending) {
+        ++issued;
+        pending = pre.next();
+      }
     };
 
     __builtin_amdgcn_s_barrier();  // every wave is done with the previous tile's stages
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    issue0(cur.unit());
-    while (true) {
-      bool more = cur.next();
-      wait_copies_and_sync();  // stage 0 has landed everywhere; stage 1 is free
-      if (more) issue1(cur.unit());
+    issue(g_fwd0);
+    issue(g_fwd1);
+    issue(g_fwd2);
+    // step i: wait for unit i (units i+1, i+2 stay in flight), refill the stage unit i-1
+    // used with unit i+3, compute unit i
+    for (int i = 0;; i += kStages) {
+      if (i >= issued) break;
+      wait_unit_two_behind();
+      issue(g_fwd3);
       if (active) fwd_unit<0>(w, l32, hh, scale_log2e);
-      if (!more) break;
-      more = cur.next();
-      wait_copies_and_sync();  // stage 1 has landed everywhere; stage 0 is free
-      if (more) issue0(cur.unit());
+      if (i + 1 >= issued) break;
+      wait_unit_two_behind();
+      issue(g_fwd0);
       if (active) fwd_unit<1>(w, l32, hh, scale_log2e);
-      if (!more) break;
+      if (i + 2 >= issued) break;
+      wait_unit_two_behind();
+      issue(g_fwd1);
+      if (active) fwd_unit<2>(w, l32, hh, scale_log2e);
+      if (i + 3 >= issued) break;
+      wait_unit_two_behind();
+      issue(g_fwd2);
+      if (active) fwd_unit<3>(w, l32, hh, scale_log2e);
     }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // the trailing repeat copies
     // epilogue
     if (!active) continue;
     const double ltot = w.lsum + __shfl_xor(w.lsum, 32, 64);  // the two half waves' keys
@@ -356,7 +375,7 @@ hipError_t launch_attn_fwd(const Dims &d, float scale, uint8_t *ws, const Layout
     const float sl2e = scale * 1.4426950408889634f;
     const int grid = resident_grid((const void *)attn_fwd_bf16_kernel, NW * 64, d.heads * d.U);
     hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, d.N, d.U,
-                       d.nb_max, d.heads, (const int2 *)(ws + L.tiles), counters,
+                       d.nb_max, d.heads, (const int2 *)(ws + L.btiles), counters + 1,
                        (const uint16_t *)(ws + L.qp), (const uint16_t *)(ws + L.kp),
                        (const uint16_t *)(ws + L.vpt), unit_blk, bstart, bsize, cnt, cols, perm,
                        sl2e, (uint16_t *)o, lse, o32p, lsep);

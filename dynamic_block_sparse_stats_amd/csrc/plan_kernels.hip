@@ -522,8 +522,9 @@ hipError_t launch_gather(const Dims &d, const void *q, const void *k, const void
 constexpr int kTileThreads = 1024;
 
 __global__ void __launch_bounds__(kTileThreads)
-    tiles_kernel(int heads, int Z, const int *__restrict__ zshape, int2 *tiles, int *counters) {
-  __shared__ int scan[kTileThreads];
+    tiles_kernel(int heads, int Z, const int *__restrict__ zshape, int2 *tiles, int2 *btiles,
+                 int *counters) {
+  __shared__ int scan[kTileThreads], bscan[kTileThreads];
   const int tid = threadIdx.x, n = heads * Z;
   const int chunk = (n + kTileThreads - 1) / kTileThreads;
   const int i0 = min(n, tid * chunk), i1 = min(n, i0 + chunk);
@@ -531,17 +532,33 @@ __global__ void __launch_bounds__(kTileThreads)
     const int code = zshape[idx];
     return ((code >> 4) & 3) + ((code >> 2) & 3) + (code & 3) >= 7 ? 4 : 8;
   };
-  int local = 0;
-  for (int i = i0; i < i1; ++i) local += ntile(i);
+  // units per block: log2 of the block volume is the sum of the log2 edges (6, 7 or 8)
+  auto bunits = [&](int idx) {
+    const int code = zshape[idx];
+    return 1 << (((code >> 4) & 3) + ((code >> 2) & 3) + (code & 3) - 6);
+  };
+  int local = 0, blocal = 0;
+  for (int i = i0; i < i1; ++i) {
+    local += ntile(i);
+    blocal += 8 / bunits(i);
+  }
   scan[tid] = local;
+  bscan[tid] = blocal;
   __syncthreads();
   for (int off = 1; off < kTileThreads; off <<= 1) {
     const int add = tid >= off ? scan[tid - off] : 0;
+    const int badd = tid >= off ? bscan[tid - off] : 0;
     __syncthreads();
     scan[tid] += add;
+    bscan[tid] += badd;
     __syncthreads();
   }
-  int at = scan[tid] - local;
+  int at = scan[tid] - local, bat = bscan[tid] - blocal;
+  for (int i = i0; i < i1; ++i) {
+    const int h = i / Z, m = i % Z, nu = bunits(i);
+    for (int b = 0; b < 8 / nu; ++b) btiles[bat + b] = make_int2(h, (8 * m + b * nu) | (nu << 16));
+    bat += 8 / nu;
+  }
   for (int i = i0; i < i1; ++i) {
     const int h = i / Z, m = i % Z;
     if (ntile(i) == 4) {
@@ -552,14 +569,17 @@ __global__ void __launch_bounds__(kTileThreads)
       at += 8;
     }
   }
-  if (tid == kTileThreads - 1) counters[0] = scan[tid];
+  if (tid == kTileThreads - 1) {
+    counters[0] = scan[tid];
+    counters[1] = bscan[tid];
+  }
 }
 
 hipError_t launch_tiles(const Dims &d, uint8_t *ws, const Layout &L, hipStream_t s) {
   TraceScope tr(PRISM_STAGE_TILES, s);
   hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(kTileThreads), 0, s, d.heads, d.Z,
                      (const int *)(ws + L.pub.zone_shape), (int2 *)(ws + L.tiles),
-                     (int *)(ws + L.counters));
+                     (int2 *)(ws + L.btiles), (int *)(ws + L.counters));
   return hipGetLastError();
 }
 

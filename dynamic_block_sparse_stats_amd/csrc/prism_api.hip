@@ -157,9 +157,11 @@ Layout make_layout(const Dims &d) {
   L.sel_bits = take(H * NB * d.words * sizeof(uint32_t));
   L.csc_bits = take(H * NB * d.words * sizeof(uint32_t));
   L.tiles = take(H * U * sizeof(int2));
+  L.btiles = take(H * U * sizeof(int2));
   L.counters = take(16 * sizeof(int));
   L.delta = take(H * N * sizeof(float));
   L.lsep = take(H * N * sizeof(float));
+  L.lse2 = take(H * N * sizeof(float));
   L.o32p = take(H * N * D * sizeof(float));
   const size_t tensor = H * N * D * d.elt;
   L.qp = take(tensor);

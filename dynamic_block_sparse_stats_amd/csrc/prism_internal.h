@@ -27,6 +27,7 @@ struct TraceScope {
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -49,11 +50,14 @@ struct Layout {
   size_t sel_bits;          // uint32 [heads][nb_max][words]
   size_t csc_bits;          // uint32 [heads][nb_max][words]
   size_t tiles;             // int2 [heads*U]: (head, first unit | kTile64) per query/key tile
-  size_t counters;          // int32 [16]: [0] = tile count
+  size_t btiles;            // int2 [heads*U]: (head, first unit | units << 16) per block
+  size_t counters;          // int32 [16]: [0] = tile count, [1] = block tile count
   size_t dop, dopt;         // bwd: gathered dout, row-major (bf16) and transposed (f16)
   size_t o32p;              // fwd: float [heads][N][D] output in permuted order
   size_t lsep;              // fwd: float [heads][N] lse in permuted order
-  size_t delta;             // bwd: float [heads][N] rowsum(dO * O) in permuted order
+  size_t delta;             // bwd: float [heads][N] in permuted order: rowsum(dO * O)
+                            //   (float32 inputs) or -rowsum(dO * O) * 2^-kPShift (bfloat16)
+  size_t lse2;              // bwd (bfloat16): float [heads][N] lse * log2(e) - kPShift
   size_t total;
 };
 
@@ -89,7 +93,7 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
 hipError_t launch_dkdv_bf16(int work_items, hipStream_t s, int N, int U, int nb_max, int heads,
                             const int2 *tiles, const int *counters, const uint16_t *qp,
                             const uint16_t *qpt, const uint16_t *kp, const uint16_t *vp,
-                            const uint16_t *dop, const uint16_t *dopt, const float *lsep,
+                            const uint16_t *dop, const uint16_t *dopt, const float *lse2,
                             const float *delta, const int *unit_blk, const int *bstart,
                             const int *bsize, const int *tcnt, const int *trows,
                             const int *perm, float scale, float sl2e, uint16_t *dk,
@@ -122,9 +126,16 @@ __device__ __forceinline__ f32x16 mfma_f16(f16x8 a, f16x8 b, f32x16 c) {
 
 // Direct global -> LDS copies (global_load_lds): lane l of one instruction writes its
 // 16 (or 4) bytes at dst + 16 * l (4 * l); dst must be uniform across the wave.
+// The LDS destination is passed on as a plain 32-bit address taken through readfirstlane
+// (it is uniform: every lane of a copy writes dst + 16 * lane): the compiler then has no
+// object to tie the copy to and adds no waits of its own before LDS reads; the kernels
+// order copies and reads themselves with s_waitcnt vmcnt and barriers.
 __device__ __forceinline__ void dma16(const void *src, void *dst) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)dst);
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                   (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+                                   (__attribute__((address_space(3))) void *)(uintptr_t)a, 16,
+                                   0, 0);
 }
 __device__ __forceinline__ void dma4(const void *src, void *dst) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
@@ -137,6 +148,51 @@ __device__ __forceinline__ void wait_copies_and_sync() {
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
+
+// The 64-token units of a list of blocks, in list order (a block of B tokens is B/64
+// consecutive units).  The list is read 64 entries at a time, one per lane, and the
+// current block is broadcast from its lane: the walk itself issues no memory operation, so
+// it never waits behind the direct-to-LDS copies in flight (loads complete in order).  The
+// members other than the window are the same in every lane.
+struct BlockUnits {
+  int base, idx, sub, us, nu, n, lane;
+  int win_us, win_nu;  // this lane's entry of the window: first unit and unit count
+  const int *list, *bstart, *bsize;
+  __device__ void fill() {  // lanes past the end repeat the last entry (never used)
+    const int j = list[min(base + lane, n - 1)];
+    win_us = bstart[j] / kUnit;
+    win_nu = bsize[j] / kUnit;
+  }
+  __device__ void load() {
+    us = __builtin_amdgcn_readlane(win_us, idx);
+    nu = __builtin_amdgcn_readlane(win_nu, idx);
+  }
+  // a list of count >= 1 blocks
+  __device__ void init(const int *l, int count, const int *bs, const int *bz, int lane_id) {
+    list = l;
+    n = __builtin_amdgcn_readfirstlane(count);
+    bstart = bs;
+    bsize = bz;
+    lane = lane_id;
+    base = idx = sub = 0;
+    fill();
+    load();
+  }
+  __device__ int unit() const { return us + sub; }
+  // advances; false once the list is exhausted
+  __device__ bool next() {
+    if (++sub < nu) return true;
+    sub = 0;
+    if (base + ++idx >= n) return false;
+    if (idx == 64) {
+      base += 64;
+      idx = 0;
+      fill();
+    }
+    load();
+    return true;
+  }
+};
 
 // bfloat16 -> float16 bits (exact inside the float16 range; saturates beyond +-65504).
 __device__ __forceinline__ uint16_t bf16_to_f16_bits(uint16_t b) {
