@@ -7,73 +7,52 @@
 // x's block, delta_x = do_x.o_x and dS_xy = P_xy (do_x.v_y - delta_x):
 //   dv_y = sum_x P_xy do_x,  dk_y = scale sum_x dS_xy q_x,  dq_x = scale sum_y dS_xy k_y.
 // Three passes, none with atomics (results are bit-reproducible):
-//   prep  -- gathers dO into the permuted layout (row-major and per-unit transposed) and
-//            forms delta from the float32 output the forward kept;  for bfloat16 it also
-//            folds the constants of the two MFMA passes into their inputs: the row-major dO
-//            copy is scaled by 2^-10 and delta stored as -delta * 2^-10 (so the dP
-//            accumulator starts at -delta and ends at (dP - delta) * 2^-10), and lse is
-//            stored as lse * log2(e) - 10 (so the exp2 gives P * 2^10 directly);
-//   dK/dV -- one workgroup per key tile (32 keys per wave, K and V rows held in registers),
-//            streaming the 64-token query units of every query block that selected the
-//            key block (the transposed selection lists);
-//   dQ    -- one workgroup per query tile (32 queries per wave, Q and dO in registers),
+//   prep  -- gathers dO into the permuted row-major layout and forms delta from the
+//            float32 output the forward kept;
+//   dK/dV -- one workgroup per key tile (pairs of waves over 32 keys, K or V rows held in
+//            registers), streaming the 64-token query units of every query block that
+//            selected the key block (the transposed selection lists);
+//   dQ    -- one workgroup per query block (32 queries per wave, Q and dO in registers),
 //            streaming the selected key units as in the forward pass.
-// Both MFMA passes recompute P from the stored lse; the products with P and dS run on the
-// float16 MFMA (P scaled by 2^10, as in the forward) against the float16 transposed copies;
-// outputs go straight to the tokens' original positions.
+// Both MFMA passes recompute P from the stored lse and run on the float16 MFMA: the
+// permuted copies are float16, the transposed operands (K^T, Q^T, dO^T) are read from
+// the row-major LDS tiles with transposing LDS reads, P is fed scaled by 2^10 (as in the
+// forward) and dS unscaled; outputs go straight to the tokens' original positions.
 #include "prism_internal.h"
 
 namespace prism {
 
 constexpr int kDB = 128;
 
-__device__ __forceinline__ int rm_off(int r, int c) {  // [64][128] bf16 tile, 16 chunks/row
-  return r * 256 + ((c ^ (r & 15)) << 4);
-}
-__device__ __forceinline__ int tr_off(int d, int c) {  // [128][64] bf16 tile, 8 chunks/row
-  return d * 128 + ((c ^ ((d >> 1) & 7)) << 4);
-}
-__device__ __forceinline__ int swap23b(int e) {
-  return (e & ~12) | ((e >> 1) & 4) | ((e << 1) & 8);
-}
 
 // ============================================================================ prep
-template <typename T, int D, bool TRANSPOSE>
+// dO gathered into the permuted row-major layout (float16 for bfloat16 inputs, the operand
+// type of the MFMA passes), delta = rowsum(dO * O) from the float32 output the forward
+// kept; for bfloat16, delta is stored negated (the dP accumulators start from it) and lse
+// as lse * log2(e) (the exp2 argument).
+template <typename T, int D, bool F16>
 __global__ void __launch_bounds__(256)
     bwd_prep_kernel(int N, int heads, const int *__restrict__ perm, const T *__restrict__ dout,
                     const float *__restrict__ o32p, const float *__restrict__ lsep,
-                    T *__restrict__ dop, T *__restrict__ dopt, float *__restrict__ delta,
-                    float *__restrict__ lse2) {
+                    T *__restrict__ dop, float *__restrict__ delta, float *__restrict__ lse2) {
   constexpr int VPC = 16 / (int)sizeof(T);
   constexpr int CH = D / VPC;
   constexpr int RG = 256 / CH;
   constexpr int RPT = kUnit / RG;
   const int u = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int c = tid % CH, rg = tid / CH;
-  __shared__ __align__(16) uint16_t tile[TRANSPOSE ? kUnit * D : 8];
   const size_t tstride = (size_t)heads * D;
 #pragma unroll
   for (int rr = 0; rr < RPT; ++rr) {
     const int row = rg + RG * rr;
     const size_t p = (size_t)u * kUnit + row;
     const int token = perm[(size_t)h * N + p];
-    u32x4 a = *reinterpret_cast<const u32x4 *>(dout + token * tstride + (size_t)h * D + c * VPC);
-    if constexpr (TRANSPOSE) {
-      // dO * 2^-kPShift: an exact power-of-two scaling of each bfloat16
-      u32x4 sc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = __uint_as_float(a[e] << 16) * (1.f / kPScale);
-        const float hi = __uint_as_float(a[e] & 0xffff0000u) * (1.f / kPScale);
-        sc[e] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-      }
-      *reinterpret_cast<u32x4 *>(dop + ((size_t)h * N + p) * D + c * VPC) = sc;
-    } else {
-      *reinterpret_cast<u32x4 *>(dop + ((size_t)h * N + p) * D + c * VPC) = a;
-    }
+    const u32x4 a =
+        *reinterpret_cast<const u32x4 *>(dout + token * tstride + (size_t)h * D + c * VPC);
     const float *orow = o32p + ((size_t)h * N + p) * D + c * VPC;
     float dot = 0.f;
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (F16) {
+      u32x4 hv;
       const f32x4 o0 = *reinterpret_cast<const f32x4 *>(orow);
       const f32x4 o1 = *reinterpret_cast<const f32x4 *>(orow + 4);
       const float ov[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
@@ -81,151 +60,151 @@ __global__ void __launch_bounds__(256)
       for (int e = 0; e < 4; ++e) {
         dot += __uint_as_float(a[e] << 16) * ov[2 * e];
         dot += __uint_as_float(a[e] & 0xffff0000u) * ov[2 * e + 1];
+        hv[e] = (uint32_t)bf16_to_f16_bits((uint16_t)(a[e] & 0xffffu)) |
+                ((uint32_t)bf16_to_f16_bits((uint16_t)(a[e] >> 16)) << 16);
       }
+      *reinterpret_cast<u32x4 *>(dop + ((size_t)h * N + p) * D + c * VPC) = hv;
     } else {
       const f32x4 o0 = *reinterpret_cast<const f32x4 *>(orow);
 #pragma unroll
       for (int e = 0; e < 4; ++e) dot += __uint_as_float(a[e]) * o0[e];
+      *reinterpret_cast<u32x4 *>(dop + ((size_t)h * N + p) * D + c * VPC) = a;
     }
 #pragma unroll
     for (int off = 1; off < CH; off <<= 1) dot += __shfl_xor(dot, off, 64);
     if (c == 0) {
-      if constexpr (TRANSPOSE) {
-        delta[(size_t)h * N + p] = -dot * (1.f / kPScale);
-        lse2[(size_t)h * N + p] = lsep[(size_t)h * N + p] * 1.4426950408889634f - kPShift;
+      if constexpr (F16) {
+        delta[(size_t)h * N + p] = -dot;
+        lse2[(size_t)h * N + p] = lsep[(size_t)h * N + p] * 1.4426950408889634f;
       } else {
         delta[(size_t)h * N + p] = dot;
       }
     }
-    if constexpr (TRANSPOSE) *reinterpret_cast<u32x4 *>(&tile[row * D + c * VPC]) = a;
-  }
-  if constexpr (TRANSPOSE) {
-    __syncthreads();
-    const int dd = tid >> 1, half = tid & 1;
-    const size_t ubase = ((size_t)h * (N / kUnit) + u) * (size_t)(D * kUnit);
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      uint32_t pk[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        int pos0 = 32 * half + 8 * cc + e;
-        int key0 = (pos0 & ~15) | swap23b(pos0 & 15);
-        int key1 = ((pos0 + 1) & ~15) | swap23b((pos0 + 1) & 15);
-        pk[e >> 1] = (uint32_t)bf16_to_f16_bits(tile[key0 * D + dd]) |
-                     ((uint32_t)bf16_to_f16_bits(tile[key1 * D + dd]) << 16);
-      }
-      *reinterpret_cast<u32x4 *>(dopt + ubase + (size_t)dd * kUnit + 32 * half + 8 * cc) =
-          u32x4{pk[0], pk[1], pk[2], pk[3]};
-    }
   }
 }
 
-constexpr int NW = 4;
-
 // ============================================================================ dQ (bf16)
-// One workgroup of four waves per query tile (32 queries per wave, Q and dO rows held as B
-// operands), streaming the selected key units through a two-stage LDS ring of direct
-// global->LDS copies as in the forward: per stage K and V row-major [64][128] bf16 and
-// K^T [128][64] f16 (48 KB); each wave issues 12 of the 48 one-kilobyte copies.
+// One workgroup of eight waves (two per SIMD) per query block (32 queries per wave, Q and
+// dO rows held as B operands), streaming the selected key units through a four-stage LDS
+// ring of direct global->LDS copies, three units ahead of the one being computed: per
+// stage K and V row-major [64][128] float16 (32 KB); waves 0-3 copy 16 K rows each, waves
+// 4-7 16 V rows, four one-kilobyte copies per wave and unit.
+constexpr int QW = 8;
+constexpr int kQStages = 4;
+constexpr int kQCpw = 32 / QW;
+constexpr int kQGroups = 4;  // K and V operand reads go in groups of 8 / kQGroups
 struct DqStage {
-  uint8_t tile[3][16384];  // K, V, K^T
+  uint8_t tile[2][16384];  // K, V
 };
 __shared__ __align__(16) DqStage g_dq0;
 __shared__ __align__(16) DqStage g_dq1;
+__shared__ __align__(16) DqStage g_dq2;
+__shared__ __align__(16) DqStage g_dq3;
 template <int S>
 __device__ __forceinline__ const DqStage &dq_stage() {
-  return S ? g_dq1 : g_dq0;
+  return S == 0 ? g_dq0 : (S == 1 ? g_dq1 : (S == 2 ? g_dq2 : g_dq3));
 }
 
 struct DqState {
-  bf16x8 qreg[8], doreg[8];
+  f16x8 qreg[8], doreg[8];
   f32x16 acc[4];
   float lse2, ndlt;
 };
 
 template <int S>
-__device__ __forceinline__ void dq_unit(DqState &w, int l32, int hh, float scale_log2e) {
-  const DqStage &sg = dq_stage<S>();
-  f16x8 db[4];
+__device__ __forceinline__ void dq_unit(DqState &w, int lane, float scale_log2e) {
+  // an opaque zero added to the stage address keeps the compiler from hoisting the per-lane
+  // swizzled addresses of all stages out of the loop (they do not fit in the registers left
+  // beside the operands)
+  int z = 0;
+  asm volatile("" : "+v"(z));
+  const DqStage &sg = *reinterpret_cast<const DqStage *>(
+      reinterpret_cast<const uint8_t *>(&dq_stage<S>()) + z);
+  const int l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {  // keys 32a .. 32a + 31
     const int r = 32 * a + l32;
-    bf16x8 ka[8], va[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      ka[kk] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4 *>(sg.tile[0] + rm_off(r, 2 * kk + hh)));
-      va[kk] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4 *>(sg.tile[1] + rm_off(r, 2 * kk + hh)));
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    // S^T = K Q^T and dP^T = V dO^T (dP started at -delta) in groups of four operand
+    // reads ahead of their MFMAs
     f32x16 s = f32x16{}, dp;
 #pragma unroll
     for (int v = 0; v < 16; ++v) dp[v] = w.ndlt;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      s = mfma_bf16(ka[kk], w.qreg[kk], s);
-      dp = mfma_bf16(va[kk], w.doreg[kk], dp);
+    for (int grp = 0; grp < 2 * kQGroups; ++grp) {
+      constexpr int GS = 8 / kQGroups;
+      const uint8_t *tile = sg.tile[grp / kQGroups];
+      f16x8 ka[GS];
+#pragma unroll
+      for (int e = 0; e < GS; ++e)
+        ka[e] = __builtin_bit_cast(
+            f16x8, *reinterpret_cast<const u32x4 *>(
+                       tile + rm_swz(r, 2 * (GS * (grp % kQGroups) + e) + hh)));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int e = 0; e < GS; ++e) {
+        const int kk = GS * (grp % kQGroups) + e;
+        if (grp < kQGroups)
+          s = mfma_f16(ka[e], w.qreg[kk], s);
+        else
+          dp = mfma_f16(ka[e], w.doreg[kk], dp);
+      }
     }
-    // lane = query, register v = key 32a + (v/4)*8 + 4hh + v%4;  P * 2^10 times
-    // (dP - delta) * 2^-10
+    // lane = query, register v = key 32a + (v/4)*8 + 4hh + v%4:  dS = P (dP - delta)
+    f16x8 db[2];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const float p = __builtin_amdgcn_exp2f(fmaf(s[v], scale_log2e, -w.lse2));
-      db[2 * a + (v >> 3)][v & 7] = (_Float16)(p * dp[v]);
+      db[v >> 3][v & 7] = (_Float16)(p * dp[v]);
     }
-  }
-  // dQ^T[d][q] += K^T[d][keys] dS^T[keys][q]
+    // dQ^T[d][q] += K^T[d][keys of this half] dS^T[keys][q], K^T read transposed
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    const int d = 32 * dt + l32;
-    f16x8 kt[4];
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      kt[g] = __builtin_bit_cast(
-          f16x8, *reinterpret_cast<const u32x4 *>(sg.tile[2] + tr_off(d, 2 * g + hh)));
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) w.acc[dt] = mfma_f16(kt[g], db[g], w.acc[dt]);
+      for (int g = 0; g < 2; ++g)
+        w.acc[dt] = mfma_f16(tr_operand(sg.tile[0], 32 * a + 16 * g, 32 * dt, lane), db[g],
+                             w.acc[dt]);
   }
 }
 
-__global__ void __launch_bounds__(NW * 64)
+// s_waitcnt vmcnt(2 kQCpw) and a workgroup barrier: every wave issues exactly kQCpw copies
+// per step, so the unit two steps behind the newest has landed everywhere
+__device__ __forceinline__ void dq_wait_two_behind() {
+  wait_and_barrier<vmcnt_imm(2 * kQCpw)>();
+}
+
+__global__ void __launch_bounds__(QW * 64)
     attn_dq_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
                         const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
-                        const uint16_t *__restrict__ kp, const uint16_t *__restrict__ kpt,
-                        const uint16_t *__restrict__ vp, const uint16_t *__restrict__ dop,
-                        const float *__restrict__ lse2, const float *__restrict__ ndelta,
-                        const int *__restrict__ unit_blk, const int *__restrict__ blk_start,
-                        const int *__restrict__ blk_size, const int *__restrict__ sel_count,
-                        const int *__restrict__ csr_col, const int *__restrict__ perm,
-                        float scale, float scale_log2e, uint16_t *__restrict__ dq) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+                        const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
+                        const uint16_t *__restrict__ dop, const float *__restrict__ lse2,
+                        const float *__restrict__ ndelta, const int *__restrict__ unit_blk,
+                        const int *__restrict__ blk_start, const int *__restrict__ blk_size,
+                        const int *__restrict__ sel_count, const int *__restrict__ csr_col,
+                        const int *__restrict__ perm, float scale, float scale_log2e,
+                        uint16_t *__restrict__ dq) {
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   const int ntiles = *tile_count;
-  // copy j in 12*wave .. 12*wave + 11 of [K (16), V (16), K^T (16)] one-kilobyte copies
-  auto csrc_of = [&](int j) -> const uint8_t * {
-    const int tsel = j >> 4;
-    return reinterpret_cast<const uint8_t *>(tsel == 0 ? kp : (tsel == 1 ? vp : kpt));
-  };
-  auto cofs = [&](int j) {
-    const int i = j & 15;
-    if (j < 32) {
-      const int r = 4 * i + (lane >> 4);
-      return r * 256 + (((lane & 15) ^ (r & 15)) << 4);
-    }
-    const int d = 8 * i + (lane >> 3);
-    return d * 128 + (((lane & 7) ^ ((d >> 1) & 7)) << 4);
+  // copies of this wave: K rows 16w.. (w < 4) or V rows 16(w-4).. (w >= 4)
+  const bool kcopy = wave < QW / 2;
+  const int wq = wave & (QW / 2 - 1);
+  const uint8_t *csrc = reinterpret_cast<const uint8_t *>(kcopy ? kp : vp);
+  const int cdst = (kcopy ? 0 : 16384) + wq * 4096;
+  auto cofs = [&](int i) {  // byte offset inside the unit of this lane's 16 bytes, copy i
+    const int r = 16 * wq + 4 * i + (lane >> 4);
+    return r * 256 + (((lane & 15) ^ (r & 15)) << 4);
   };
 
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int2 tl = tiles[t];
-    const int h = tl.x, u0 = tl.y & (kTile64 - 1);
-    const bool active = !(tl.y & kTile64) || wave < 2;
+    const int h = __builtin_amdgcn_readfirstlane(tl.x);
+    const int ty = __builtin_amdgcn_readfirstlane(tl.y);
+    const int u0 = ty & 0xffff, rows = (ty >> 16) * kUnit;
+    const bool active = wave * 32 < rows;
     const int blk = unit_blk[(size_t)h * U + u0];
     const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
-    BlockUnits cur;
-    cur.init(csr_col + ((size_t)h * nb_max + blk) * nb_max,
+    BlockUnits pre;
+    pre.init(csr_col + ((size_t)h * nb_max + blk) * nb_max,
              sel_count[(size_t)h * nb_max + blk], bs, bz, lane);
     const int row0 = u0 * kUnit + wave * 32;
     DqState w;
@@ -236,48 +215,56 @@ __global__ void __launch_bounds__(NW * 64)
       const uint16_t *dr = dop + ((size_t)h * N + row0 + l32) * kDB + 8 * hh;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        w.qreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qr + 16 * kk));
-        w.doreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(dr + 16 * kk));
+        w.qreg[kk] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(qr + 16 * kk));
+        w.doreg[kk] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(dr + 16 * kk));
       }
       w.lse2 = lse2[(size_t)h * N + row0 + l32];
       w.ndlt = ndelta[(size_t)h * N + row0 + l32];
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) w.acc[dt] = f32x16{};
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // rows and cursor window in before any copy
 
-    const size_t hb = (size_t)h * N * kDB * 2;
-    auto issue0 = [&](int u) {
+    const uint8_t *hbase = csrc + (size_t)h * N * kDB * 2;
+    int issued = 0;
+    bool pending = true;
+    // kQCpw copies per step; past the end of the list they repeat the last unit into a
+    // stage no step reads any more (drained before the next tile)
+    auto issue = [&](const DqStage &st) {
+      const uint8_t *src = hbase + (size_t)pre.unit() * kUnit * kDB * 2;
 #pragma unroll
-      for (int e = 0; e < 12; ++e) {
-        const int j = 12 * wave + e;
-        dma16(csrc_of(j) + hb + (size_t)u * kUnit * kDB * 2 + cofs(j),
-              g_dq0.tile[j >> 4] + 1024 * (j & 15));
+      for (int i = 0; i < kQCpw; ++i)
+        dma16(src + cofs(i), const_cast<uint8_t *>(reinterpret_cast<const uint8_t *>(&st)) +
+                                 cdst + 1024 * i);
+      if (pending) {
+        ++issued;
+        pending = pre.next();
       }
     };
-    auto issue1 = [&](int u) {
-#pragma unroll
-      for (int e = 0; e < 12; ++e) {
-        const int j = 12 * wave + e;
-        dma16(csrc_of(j) + hb + (size_t)u * kUnit * kDB * 2 + cofs(j),
-              g_dq1.tile[j >> 4] + 1024 * (j & 15));
-      }
-    };
 
-    __builtin_amdgcn_s_barrier();  // every wave is done with the previous tile's stages
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    issue0(cur.unit());
-    while (true) {
-      bool more = cur.next();
-      wait_copies_and_sync();
-      if (more) issue1(cur.unit());
-      if (active) dq_unit<0>(w, l32, hh, scale_log2e);
-      if (!more) break;
-      more = cur.next();
-      wait_copies_and_sync();
-      if (more) issue0(cur.unit());
-      if (active) dq_unit<1>(w, l32, hh, scale_log2e);
-      if (!more) break;
+    workgroup_barrier();  // every wave is done with the previous tile's stages
+    issue(g_dq0);
+    issue(g_dq1);
+    issue(g_dq2);
+    for (int i = 0;; i += kQStages) {
+      if (i >= issued) break;
+      dq_wait_two_behind();
+      issue(g_dq3);
+      if (active) dq_unit<0>(w, lane, scale_log2e);
+      if (i + 1 >= issued) break;
+      dq_wait_two_behind();
+      issue(g_dq0);
+      if (active) dq_unit<1>(w, lane, scale_log2e);
+      if (i + 2 >= issued) break;
+      dq_wait_two_behind();
+      issue(g_dq1);
+      if (active) dq_unit<2>(w, lane, scale_log2e);
+      if (i + 3 >= issued) break;
+      dq_wait_two_behind();
+      issue(g_dq2);
+      if (active) dq_unit<3>(w, lane, scale_log2e);
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the trailing repeat copies
     if (!active) continue;
     const int token = perm[(size_t)h * N + row0 + l32];
     uint16_t *qrow = dq + ((size_t)token * heads + h) * kDB;
@@ -446,28 +433,25 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
     {
       TraceScope tr(PRISM_STAGE_BWD_PREP, s);
       hipLaunchKernelGGL((bwd_prep_kernel<T, 128, true>), ugrid, dim3(256), 0, s, d.N, d.heads,
-                       perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop),
-                       (T *)(ws + L.dopt), delta, lse2);
+                         perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop), delta, lse2);
     }
     const int *counters = (const int *)(ws + L.counters);
     const float sl2e = scale * 1.4426950408889634f;
     const int maxt = d.heads * d.U;
     const T *qp = (const T *)(ws + L.qp), *kp = (const T *)(ws + L.kp),
-            *vp = (const T *)(ws + L.vp), *qpt = (const T *)(ws + L.qpt),
-            *kpt = (const T *)(ws + L.kpt), *dop = (const T *)(ws + L.dop),
-            *dopt = (const T *)(ws + L.dopt);
-    const int2 *tiles = (const int2 *)(ws + L.tiles);
+            *vp = (const T *)(ws + L.vp), *dop = (const T *)(ws + L.dop);
+    const int2 *tiles = (const int2 *)(ws + L.tiles), *btiles = (const int2 *)(ws + L.btiles);
     {
       TraceScope tr(PRISM_STAGE_BWD_DKDV, s);
-      launch_dkdv_bf16(maxt, s, d.N, d.U, d.nb_max, d.heads, tiles, counters, qp, qpt, kp, vp,
-                       dop, dopt, lse2, delta, unit_blk, bstart, bsize, tcnt, trows, perm, scale,
-                       sl2e, (T *)dk, (T *)dv);
+      launch_dkdv_bf16(maxt, s, d.N, d.U, d.nb_max, d.heads, tiles, counters, qp, kp, vp, dop,
+                       lse2, delta, unit_blk, bstart, bsize, tcnt, trows, perm, scale, sl2e,
+                       (T *)dk, (T *)dv);
     }
     {
       TraceScope tr(PRISM_STAGE_BWD_DQ, s);
-      const int grid = resident_grid((const void *)attn_dq_bf16_kernel, NW * 64, maxt);
-      hipLaunchKernelGGL(attn_dq_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, d.N, d.U,
-                         d.nb_max, d.heads, tiles, counters, qp, kp, kpt, vp, dop, lse2, delta,
+      const int grid = resident_grid((const void *)attn_dq_bf16_kernel, QW * 64, maxt);
+      hipLaunchKernelGGL(attn_dq_bf16_kernel, dim3(grid), dim3(QW * 64), 0, s, d.N, d.U,
+                         d.nb_max, d.heads, btiles, counters + 1, qp, kp, vp, dop, lse2, delta,
                          unit_blk, bstart, bsize, cnt, cols, perm, scale, sl2e, (T *)dq);
     }
   } else {
@@ -477,8 +461,7 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
             *vp = (const T *)(ws + L.vp), *dop = (const T *)(ws + L.dop);
     if (d.D == 64) {
       hipLaunchKernelGGL((bwd_prep_kernel<T, 64, false>), ugrid, dim3(256), 0, s, d.N, d.heads,
-                         perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop), nullptr, delta,
-                         nullptr);
+                         perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop), delta, nullptr);
       hipLaunchKernelGGL((attn_dq_f32_kernel<64>), ugrid, dim3(256), 0, s, d.N, d.U, d.nb_max,
                          d.heads, qp, kp, vp, dop, lsep, delta, unit_blk, bstart, bsize, cnt,
                          cols, perm, scale, (T *)dq);
@@ -487,8 +470,8 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
                          bsize, tcnt, trows, perm, scale, (T *)dk, (T *)dv);
     } else {
       hipLaunchKernelGGL((bwd_prep_kernel<T, 128, false>), ugrid, dim3(256), 0, s, d.N,
-                         d.heads, perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop),
-                         nullptr, delta, nullptr);
+                         d.heads, perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop), delta,
+                         nullptr);
       hipLaunchKernelGGL((attn_dq_f32_kernel<128>), ugrid, dim3(256), 0, s, d.N, d.U, d.nb_max,
                          d.heads, qp, kp, vp, dop, lsep, delta, unit_blk, bstart, bsize, cnt,
                          cols, perm, scale, (T *)dq);

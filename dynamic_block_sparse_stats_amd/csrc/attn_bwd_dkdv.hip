@@ -1,242 +1,347 @@
 // attn_bwd_dkdv.hip -- dK and dV of the block-sparse attention (bfloat16 path), key-major
 // over the transposed selection lists.  Same method as attn_bwd.hip (digest, training
 // section: the plan is constant; gradients flow only through the selected blocks), in a
-// translation unit of its own because its register budget (K and V rows plus the dK and
-// dV accumulators of 32 keys per wave) is best served by the default MFMA register form.
+// translation unit of its own because its register budget is best served by the default
+// MFMA register form.
+#include <type_traits>
+
 #include "prism_internal.h"
 
 namespace prism {
 
 namespace {
 constexpr int kDB = 128;
-
-__device__ __forceinline__ int rm_off(int r, int c) {  // [64][128] bf16 tile, 16 chunks/row
-  return r * 256 + ((c ^ (r & 15)) << 4);
-}
-__device__ __forceinline__ int tr_off(int d, int c) {  // [128][64] f16 tile, 8 chunks/row
-  return d * 128 + ((c ^ ((d >> 1) & 7)) << 4);
-}
 }  // namespace
 
 // ============================================================================ dK / dV (bf16)
-// One workgroup of four waves per key tile; each wave owns 32 keys (its K and V rows are
-// the B operands, held in registers) and accumulates dK^T and dV^T over the 64-token
-// query units of every query block that selected the key block.  A 64-key tile leaves
-// waves 2-3 idle in the arithmetic.
+// One workgroup of eight waves (two per SIMD) per 128-key tile (a 256-key block is two
+// tiles), in four pairs; pair w owns keys 32w .. 32w + 31 of the tile (a 64-key block
+// leaves pairs 2-3 idle in the arithmetic; they still help stage the units).  Over the
+// 64-token query units of every query block that selected the key block:
+//   * the P wave (w < 4) holds K as B operand, forms S = Q K^T and P = exp(S - lse),
+//     hands P to its partner through LDS (float32) and accumulates dV^T += dO^T P;
+//   * the dS wave (w >= 4) holds V as B operand, forms dP = dO V^T and accumulates
+//     dK^T += Q^T dS with dS = P (dP - delta).
+// Each wave does the same number of MFMAs and keeps one operand set and one accumulator
+// set, so two waves fit per SIMD.
 //
-// Query units stream through a two-stage LDS ring filled by direct global->LDS copies
+// Query units stream through a three-stage LDS ring filled by direct global->LDS copies
 // (global_load_lds_dwordx4: lane l of one instruction lands at +16*l, so the XOR swizzle
-// is applied by choosing which source chunk each lane fetches).  Per stage: Q and dO
-// row-major [64][128] bf16, Q^T and dO^T [128][64] f16, lse and delta [64].  Each wave
-// copies one of the four tiles (16 instructions) and one 256-byte vector, so every wave
-// has the same number of copies in flight; the copy of the next unit is issued right after
-// the barrier that publishes the current one and overlaps its 64 MFMAs.
-constexpr int NW = 4;
+// is applied by choosing which source chunk each lane fetches), two units ahead of the
+// one being computed.  Per stage: Q and dO row-major [64][128] float16 (Q^T and dO^T are
+// read from them with transposing LDS reads), lse and delta [64].  Waves 0-3 copy 16 Q
+// rows each, waves 4-7 16 dO rows (four one-kilobyte copies per unit), waves 0 and 1
+// also one 256-byte vector.  A second barrier per unit publishes P.
+constexpr int NW = 8;
+constexpr int kStages = 3;
 
-// The two stages are distinct LDS objects and the unit loop is unrolled by two, so every
-// LDS read names its stage statically; the compiler can then see that the copies in flight
-// (into the other stage) do not feed the reads, and issues no wait for them.
+// The stages are distinct LDS objects and the unit loop is unrolled by three, so every
+// LDS read names its stage statically.
 struct Stage {
-  uint8_t tile[4][16384];  // Q, dO (row-major bf16), Q^T, dO^T (f16)
-  float vec[4][kUnit];     // lse * log2(e) - 10, -delta * 2^-10, unused, unused
+  uint8_t tile[2][16384];  // Q, dO (row-major float16)
+  float vec[2][kUnit];     // lse * log2(e), -delta
 };
 __shared__ __align__(16) Stage g_stage0;
 __shared__ __align__(16) Stage g_stage1;
+__shared__ __align__(16) Stage g_stage2;
+// P (float32) of the current unit per pair, in the P wave's C layout:
+// [pair][half][register group of 4][lane]
+__shared__ __align__(16) f32x4 g_pex[4][2][4][64];
 template <int S>
 __device__ __forceinline__ Stage &stage() {
-  return S ? g_stage1 : g_stage0;
+  return S == 0 ? g_stage0 : (S == 1 ? g_stage1 : g_stage2);
 }
 
-struct DkdvState {
-  bf16x8 kreg[8], vreg[8];
-  f32x16 dkt[4], dvt[4];
-};
-
 template <int S>
-__device__ __forceinline__ void dkdv_unit(DkdvState &w, int l32, int hh, float scale_log2e) {
-  const Stage &sg = stage<S>();
-  f16x8 pb[4], db[4];
+__device__ __forceinline__ const Stage &stage_opaque() {
+  // an opaque zero added to the stage address keeps the per-lane swizzled addresses of
+  // all stages from being hoisted into registers for the whole loop
+  int z = 0;
+  asm volatile("" : "+v"(z));
+  return *reinterpret_cast<const Stage *>(reinterpret_cast<const uint8_t *>(&stage<S>()) + z);
+}
+
+// acc (C layout: lane = key l32, register v = query 32a + (v/4)*8 + 4hh + v%4) += the
+// 32 queries of half a of tile t (row-major [64][128] float16) times the wave's B operand
+__device__ __forceinline__ void half_product(f32x16 &acc, const uint8_t *tile, int a,
+                                             const f16x8 (&b)[8], int l32, int hh) {
+  const int r = 32 * a + l32;
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {  // queries 32a .. 32a + 31 of the unit
-    const int r = 32 * a + l32;
-    bf16x8 qa[8], da[8];
+  for (int grp = 0; grp < 2; ++grp) {
+    f16x8 x[4];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      qa[kk] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4 *>(sg.tile[0] + rm_off(r, 2 * kk + hh)));
-      da[kk] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4 *>(sg.tile[1] + rm_off(r, 2 * kk + hh)));
-    }
-    // per query row of the C layout: lse * log2(e) - 10 and -delta * 2^-10
-    f32x4 l4[4], d4[4];
-#pragma unroll
-    for (int v4 = 0; v4 < 4; ++v4) {
-      const int q0 = 32 * a + 8 * v4 + 4 * hh;
-      l4[v4] = *reinterpret_cast<const f32x4 *>(sg.vec[0] + q0);
-      d4[v4] = *reinterpret_cast<const f32x4 *>(sg.vec[1] + q0);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs below
-    f32x16 sacc = f32x16{}, dp;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) dp[v] = d4[v >> 2][v & 3];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      sacc = mfma_bf16(qa[kk], w.kreg[kk], sacc);
-      dp = mfma_bf16(da[kk], w.vreg[kk], dp);
-    }
-    // C layout: lane = key l32, register v = query 32a + (v/4)*8 + 4hh + v%4;  p is
-    // P * 2^10 and dp is (dP - delta) * 2^-10
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2e, -l4[v >> 2][v & 3]));
-      const int g = 2 * a + (v >> 3), slot = v & 7;
-      pb[g][slot] = (_Float16)p;
-      db[g][slot] = (_Float16)(p * dp[v]);
-    }
-  }
-  // dV^T[d][key] += dO^T[d][q] P[q][key];  dK^T[d][key] += Q^T[d][q] dS[q][key]
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    const int d = 32 * dt + l32;
-    f16x8 doa[4], qta[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      doa[g] = __builtin_bit_cast(
-          f16x8, *reinterpret_cast<const u32x4 *>(sg.tile[3] + tr_off(d, 2 * g + hh)));
-      qta[g] = __builtin_bit_cast(
-          f16x8, *reinterpret_cast<const u32x4 *>(sg.tile[2] + tr_off(d, 2 * g + hh)));
-    }
+    for (int e = 0; e < 4; ++e)
+      x[e] = __builtin_bit_cast(
+          f16x8, *reinterpret_cast<const u32x4 *>(tile + rm_swz(r, 2 * (4 * grp + e) + hh)));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      w.dvt[dt] = mfma_f16(doa[g], pb[g], w.dvt[dt]);
-      w.dkt[dt] = mfma_f16(qta[g], db[g], w.dkt[dt]);
+    for (int e = 0; e < 4; ++e) acc = mfma_f16(x[e], b[4 * grp + e], acc);
+  }
+}
+
+// acc[dt] (C layout: lane = key, register -> d) += T^T[d][queries of half a] X[q][key]
+// with T^T read transposed from the row-major tile and X the float16 B operands of the
+// half's two 16-query slices
+__device__ __forceinline__ void half_update(f32x16 (&acc)[4], const uint8_t *tile, int a,
+                                            const f16x8 (&x)[2], int lane) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    f16x8 ta[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) ta[g] = tr_operand(tile, 32 * a + 16 * g, 32 * dt, lane);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) acc[dt] = mfma_f16(ta[g], x[g], acc[dt]);
+  }
+}
+
+// The state of one wave of a pair: its B operand rows (K for the P wave, V for the dS
+// wave), its accumulators (dV^T or dK^T) and the current unit's values: P * 2^10 as
+// float16 (the operand of the dV product) [half][k-slice], or dP - delta in float32
+// [half].
+struct PState {
+  f16x8 breg[8];
+  f32x16 acc[4];
+  f16x8 x[2][2];
+};
+struct DState {
+  f16x8 breg[8];
+  f32x16 acc[4];
+  f32x16 dp[2];
+};
+
+// P wave, before the mid-unit barrier: S and P for both halves, P published
+template <int S>
+__device__ __forceinline__ void p_first(PState &w, int pair, int lane, float scale_log2e) {
+  const Stage &sg = stage_opaque<S>();
+  const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    f32x16 sacc = f32x16{};
+    half_product(sacc, sg.tile[0], a, w.breg, l32, hh);
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sg.vec[0] + 32 * a + 8 * v4 + 4 * hh);
+      f32x4 p4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * v4 + e;
+        p4[e] = __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2e, -l4[e]));
+        w.x[a][v >> 3][v & 7] = (_Float16)(p4[e] * kPScale);
+      }
+      g_pex[pair][a][v4][lane] = p4;
     }
+  }
+}
+// P wave, after the barrier: dV^T += dO^T (P * 2^10)
+template <int S>
+__device__ __forceinline__ void p_second(PState &w, int lane) {
+  const Stage &sg = stage_opaque<S>();
+#pragma unroll
+  for (int a = 0; a < 2; ++a) half_update(w.acc, sg.tile[1], a, w.x[a], lane);
+}
+// dS wave, before the barrier: dP, started at -delta
+template <int S>
+__device__ __forceinline__ void d_first(DState &w, int lane) {
+  const Stage &sg = stage_opaque<S>();
+  const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    f32x16 &dp = w.dp[a];
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sg.vec[1] + 32 * a + 8 * v4 + 4 * hh);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp[4 * v4 + e] = d4[e];
+    }
+    half_product(dp, sg.tile[1], a, w.breg, l32, hh);
+  }
+}
+// dS wave, after the barrier: dS = P (dP - delta) in float32, rounded once to float16;
+// dK^T += Q^T dS
+template <int S>
+__device__ __forceinline__ void d_second(DState &w, int pair, int lane) {
+  const Stage &sg = stage_opaque<S>();
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    f16x8 db[2];
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const f32x4 p4 = g_pex[pair][a][v4][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * v4 + e;
+        db[v >> 3][v & 7] = (_Float16)(p4[e] * w.dp[a][v]);
+      }
+    }
+    half_update(w.acc, sg.tile[0], a, db, lane);
+  }
+}
+
+// P published: the P waves' LDS writes are complete before the barrier
+__device__ __forceinline__ void publish_sync() { wait_and_barrier<kLgkm0>(); }
+
+template <bool PW>
+__device__ __forceinline__ void dkdv_waves(
+    int wave, int lane, int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
+    int ntiles, const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
+    const uint16_t *__restrict__ vp, const uint16_t *__restrict__ dop,
+    const float *__restrict__ lse2, const float *__restrict__ ndelta,
+    const int *__restrict__ unit_blk, const int *__restrict__ blk_start,
+    const int *__restrict__ blk_size, const int *__restrict__ csc_count,
+    const int *__restrict__ csc_row, const int *__restrict__ perm, float scale,
+    float scale_log2e, uint16_t *__restrict__ dk, uint16_t *__restrict__ dv) {
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int pair = wave & 3;
+  // copies of this wave: Q rows 16w.. (P waves) or dO rows 16(w-4).. (dS waves); waves 0
+  // and 1 also copy the lse and delta vectors
+  const uint8_t *tsrc = reinterpret_cast<const uint8_t *>(PW ? qp : dop);
+  const int cdst = (PW ? 0 : 16384) + pair * 4096;
+  auto cofs = [&](int i) {  // byte offset inside the unit of this lane's 16 bytes, copy i
+    const int r = 16 * pair + 4 * i + (lane >> 4);
+    return r * 256 + (((lane & 15) ^ (r & 15)) << 4);
+  };
+  const bool vcopy = wave < 2;
+  const float *vsrc = wave == 1 ? ndelta : lse2;
+
+  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int2 tl = tiles[t];
+    const int h = __builtin_amdgcn_readfirstlane(tl.x);
+    const int ty = __builtin_amdgcn_readfirstlane(tl.y);
+    // 128-key tiles (two per 256-key block), 64-key tiles for 64-key blocks
+    const int u0 = ty & (kTile64 - 1), rows = (ty & kTile64) ? kUnit : 2 * kUnit;
+    const bool active = pair * 32 < rows;
+    const int jblk = unit_blk[(size_t)h * U + u0];
+    const int nq = __builtin_amdgcn_readfirstlane(csc_count[(size_t)h * nb_max + jblk]);
+    const int *qlist = csc_row + ((size_t)h * nb_max + jblk) * nb_max;
+    const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
+    // the pair's 32 keys: K^T (P wave) or V^T (dS wave) as B operand (lane = key, 8 dims
+    // per k-step)
+    const int key0 = u0 * kUnit + pair * 32;
+    std::conditional_t<PW, PState, DState> w;
+    if (active) {
+      const uint16_t *br = (PW ? kp : vp) + ((size_t)h * N + key0 + l32) * kDB + 8 * hh;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        w.breg[kk] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(br + 16 * kk));
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) w.acc[dt] = f32x16{};
+
+    const size_t hb = (size_t)h * N;
+    int issued = 0;
+    bool pending = true;
+    BlockUnits pre;
+    // every step issues this wave's copies: past the end of the list they repeat the last
+    // unit into a stage no step reads any more (drained before the next tile)
+    auto issue = [&](Stage &st) {
+      const int u = pre.unit();
+      const uint8_t *src = tsrc + (hb + (size_t)u * kUnit) * kDB * 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dma16(src + cofs(i), reinterpret_cast<uint8_t *>(&st) + cdst + 1024 * i);
+      if (vcopy) dma4(vsrc + hb + (size_t)u * kUnit + lane, st.vec[wave]);
+      if (pending) {
+        ++issued;
+        pending = pre.next();
+      }
+    };
+    // this wave's copies of the unit one step behind the newest have landed everywhere
+    auto wait_one_behind = [&]() {
+      if (vcopy)
+        wait_and_barrier<vmcnt_imm(5)>();
+      else
+        wait_and_barrier<vmcnt_imm(4)>();
+    };
+    auto unit = [&](auto stage_tag) {
+      constexpr int S = decltype(stage_tag)::value;
+      if constexpr (PW) {
+        if (active) p_first<S>(w, pair, lane, scale_log2e);
+        publish_sync();
+        if (active) p_second<S>(w, lane);
+      } else {
+        if (active) d_first<S>(w, lane);
+        publish_sync();
+        if (active) d_second<S>(w, pair, lane);
+      }
+    };
+
+    workgroup_barrier();  // every wave is done with the previous tile's stages
+    if (nq > 0) {
+      pre.init(qlist, nq, bs, bz, lane);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // K or V rows and the cursor window are in
+      issue(g_stage0);
+      issue(g_stage1);
+      for (int i = 0;; i += kStages) {
+        if (i >= issued) break;
+        wait_one_behind();
+        issue(g_stage2);
+        unit(std::integral_constant<int, 0>{});
+        if (i + 1 >= issued) break;
+        wait_one_behind();
+        issue(g_stage0);
+        unit(std::integral_constant<int, 1>{});
+        if (i + 2 >= issued) break;
+        wait_one_behind();
+        issue(g_stage1);
+        unit(std::integral_constant<int, 2>{});
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the trailing repeat copies
+    }
+    // epilogue: C layout lane = key l32, register v -> d = 32dt + (v/4)*8 + 4hh + v%4; the
+    // P wave writes dV (P carried 2^10), the dS wave dK (times the softmax scale)
+    if (!active) continue;
+    const int token = perm[(size_t)h * N + key0 + l32];
+    uint16_t *orow = (PW ? dv : dk) + ((size_t)token * heads + h) * kDB;
+    const float mul = PW ? 1.f / kPScale : scale;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int d0 = 32 * dt + 8 * v4 + 4 * hh;
+        const f32x16 &A = w.acc[dt];
+        uint32_t x0 = (uint32_t)f32_to_bf16(A[4 * v4] * mul) |
+                      ((uint32_t)f32_to_bf16(A[4 * v4 + 1] * mul) << 16);
+        uint32_t x1 = (uint32_t)f32_to_bf16(A[4 * v4 + 2] * mul) |
+                      ((uint32_t)f32_to_bf16(A[4 * v4 + 3] * mul) << 16);
+        *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{x0, x1};
+      }
   }
 }
 
 __global__ void __launch_bounds__(NW * 64)
     attn_dkdv_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
                           const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
-                          const uint16_t *__restrict__ qpt, const uint16_t *__restrict__ kp,
-                          const uint16_t *__restrict__ vp, const uint16_t *__restrict__ dop,
-                          const uint16_t *__restrict__ dopt, const float *__restrict__ lse2,
-                          const float *__restrict__ delta, const int *__restrict__ unit_blk,
+                          const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
+                          const uint16_t *__restrict__ dop, const float *__restrict__ lse2,
+                          const float *__restrict__ ndelta, const int *__restrict__ unit_blk,
                           const int *__restrict__ blk_start, const int *__restrict__ blk_size,
                           const int *__restrict__ csc_count, const int *__restrict__ csc_row,
                           const int *__restrict__ perm, float scale, float scale_log2e,
                           uint16_t *__restrict__ dk, uint16_t *__restrict__ dv) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l32 = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int ntiles = *tile_count;
-  const uint8_t *tsrc = reinterpret_cast<const uint8_t *>(
-      wave == 0 ? qp : (wave == 1 ? dop : (wave == 2 ? qpt : dopt)));
-  const float *vsrc = wave == 1 ? delta : lse2;
-  // this lane's byte offset inside copy i (1 KB) of its wave's tile: rows 4i.. (row-major
-  // tiles) or 8i.. (transposed tiles); the swizzle only depends on the row within 16 / 8
-  auto lofs = [&](int i) {
-    if (wave < 2) {
-      const int r = 4 * i + (lane >> 4);
-      return r * 256 + (((lane & 15) ^ (r & 15)) << 4);
-    }
-    const int d = 8 * i + (lane >> 3);
-    return d * 128 + (((lane & 7) ^ ((d >> 1) & 7)) << 4);
-  };
-
-  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int2 tl = tiles[t];
-    const int h = tl.x, u0 = tl.y & (kTile64 - 1);
-    const bool active = !(tl.y & kTile64) || wave < 2;
-    const int jblk = unit_blk[(size_t)h * U + u0];
-    const int nq = csc_count[(size_t)h * nb_max + jblk];
-    const int *qlist = csc_row + ((size_t)h * nb_max + jblk) * nb_max;
-    const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
-    // this wave's 32 keys: K^T and V^T as B operands (lane = key, 8 dims per k-step)
-    const int key0 = u0 * kUnit + wave * 32;
-    DkdvState w;
-    if (active) {
-      const uint16_t *kr = kp + ((size_t)h * N + key0 + l32) * kDB + 8 * hh;
-      const uint16_t *vr = vp + ((size_t)h * N + key0 + l32) * kDB + 8 * hh;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        w.kreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kr + 16 * kk));
-        w.vreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(vr + 16 * kk));
-      }
-    }
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) w.dkt[dt] = w.dvt[dt] = f32x16{};
-
-    const size_t hb = (size_t)h * N;
-    auto issue0 = [&](int u) {
-      const uint8_t *src = tsrc + (hb + (size_t)u * kUnit) * kDB * 2;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dma16(src + lofs(i), g_stage0.tile[wave] + 1024 * i);
-      dma4(vsrc + hb + (size_t)u * kUnit + lane, g_stage0.vec[wave]);
-    };
-    auto issue1 = [&](int u) {
-      const uint8_t *src = tsrc + (hb + (size_t)u * kUnit) * kDB * 2;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dma16(src + lofs(i), g_stage1.tile[wave] + 1024 * i);
-      dma4(vsrc + hb + (size_t)u * kUnit + lane, g_stage1.vec[wave]);
-    };
-
-    __builtin_amdgcn_s_barrier();  // every wave is done with the previous tile's stages
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (nq > 0) {
-      BlockUnits cur;
-      cur.init(qlist, nq, bs, bz, lane);
-      issue0(cur.unit());
-      while (true) {
-        bool more = cur.next();
-        wait_copies_and_sync();  // stage 0 has landed everywhere; stage 1 is free
-        if (more) issue1(cur.unit());
-        if (active) dkdv_unit<0>(w, l32, hh, scale_log2e);
-        if (!more) break;
-        more = cur.next();
-        wait_copies_and_sync();  // stage 1 has landed everywhere; stage 0 is free
-        if (more) issue0(cur.unit());
-        if (active) dkdv_unit<1>(w, l32, hh, scale_log2e);
-        if (!more) break;
-      }
-    }
-    // epilogue: C layout lane = key l32, register v -> d = 32dt + (v/4)*8 + 4hh + v%4
-    if (!active) continue;
-    const int token = perm[(size_t)h * N + key0 + l32];
-    uint16_t *krow = dk + ((size_t)token * heads + h) * kDB;
-    uint16_t *vrow = dv + ((size_t)token * heads + h) * kDB;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const int d0 = 32 * dt + 8 * v4 + 4 * hh;
-        const f32x16 &K = w.dkt[dt], &V = w.dvt[dt];
-        uint32_t k0 = (uint32_t)f32_to_bf16(K[4 * v4] * scale) |
-                      ((uint32_t)f32_to_bf16(K[4 * v4 + 1] * scale) << 16);
-        uint32_t k1 = (uint32_t)f32_to_bf16(K[4 * v4 + 2] * scale) |
-                      ((uint32_t)f32_to_bf16(K[4 * v4 + 3] * scale) << 16);
-        const float vs = 1.f / kPScale;
-        uint32_t w0 = (uint32_t)f32_to_bf16(V[4 * v4] * vs) |
-                      ((uint32_t)f32_to_bf16(V[4 * v4 + 1] * vs) << 16);
-        uint32_t w1 = (uint32_t)f32_to_bf16(V[4 * v4 + 2] * vs) |
-                      ((uint32_t)f32_to_bf16(V[4 * v4 + 3] * vs) << 16);
-        *reinterpret_cast<u32x2 *>(krow + d0) = u32x2{k0, k1};
-        *reinterpret_cast<u32x2 *>(vrow + d0) = u32x2{w0, w1};
-      }
-  }
+  // the two roles run the same sequence of barriers and copies
+  if (wave < 4)
+    dkdv_waves<true>(wave, lane, N, U, nb_max, heads, tiles, ntiles, qp, kp, vp, dop, lse2,
+                     ndelta, unit_blk, blk_start, blk_size, csc_count, csc_row, perm, scale,
+                     scale_log2e, dk, dv);
+  else
+    dkdv_waves<false>(wave, lane, N, U, nb_max, heads, tiles, ntiles, qp, kp, vp, dop, lse2,
+                      ndelta, unit_blk, blk_start, blk_size, csc_count, csc_row, perm, scale,
+                      scale_log2e, dk, dv);
 }
 
 hipError_t launch_dkdv_bf16(int work_items, hipStream_t s, int N, int U, int nb_max, int heads,
                             const int2 *tiles, const int *counters, const uint16_t *qp,
-                            const uint16_t *qpt, const uint16_t *kp, const uint16_t *vp,
-                            const uint16_t *dop, const uint16_t *dopt, const float *lse2,
-                            const float *delta, const int *unit_blk, const int *bstart,
-                            const int *bsize, const int *tcnt, const int *trows,
-                            const int *perm, float scale, float sl2e, uint16_t *dk,
-                            uint16_t *dv) {
+                            const uint16_t *kp, const uint16_t *vp, const uint16_t *dop,
+                            const float *lse2, const float *ndelta, const int *unit_blk,
+                            const int *bstart, const int *bsize, const int *tcnt,
+                            const int *trows, const int *perm, float scale, float sl2e,
+                            uint16_t *dk, uint16_t *dv) {
   const int grid = resident_grid((const void *)attn_dkdv_bf16_kernel, NW * 64, work_items);
   hipLaunchKernelGGL(attn_dkdv_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, N, U, nb_max,
-                     heads, tiles, counters, qp, qpt, kp, vp, dop, dopt, lse2, delta, unit_blk,
-                     bstart, bsize, tcnt, trows, perm, scale, sl2e, dk, dv);
+                     heads, tiles, counters, qp, kp, vp, dop, lse2, ndelta, unit_blk, bstart,
+                     bsize, tcnt, trows, perm, scale, sl2e, dk, dv);
   return hipGetLastError();
 }
 

@@ -4,19 +4,20 @@
 // training section: 64-token atomic units, a 128-token block is 2 units and a 256-token
 // block 4, taken in turn; xyznot review, "Метод" item 3).
 //
-// bfloat16 path, head_dim 128, gfx950 MFMA v_mfma_f32_32x32x16_bf16:
+// bfloat16 path, head_dim 128, gfx950 MFMA v_mfma_f32_32x32x16_f16 (the planner stores
+// the permuted Q, K, V as float16: exact for bfloat16 values inside the float16 range):
 //   * a workgroup (8 waves, two per SIMD) owns one query block: 256, 128 or 64 rows, 32
 //     per wave (waves past the block's rows only help stage K/V); each wave keeps its 32
 //     query rows in registers as the B operand; one workgroup per CU, persistent over the
 //     list of blocks;
 //   * the key units of the block's selected key blocks stream through a four-stage LDS
 //     ring (128 KB) filled by direct global->LDS copies, three units ahead of the one being
-//     computed: K as [64 keys][128] bf16 (row-major) and V as [128][64 keys] float16 (the
-//     per-unit transposed copy written by the planner), both XOR-swizzled by 16-byte chunk
-//     so the MFMA operand reads are free of bank conflicts;
+//     computed: K and V as [64 keys][128] float16, XOR-swizzled by 16-byte chunk; K rows
+//     are read directly, V^T with transposing LDS reads (ds_read_b64_tr_b16);
 //   * the softmax weights go to the PV product as float16 scaled by 2^10 (11-bit
 //     significands where bf16 has 8: at 2K, value rows reach |v| ~ 20 and the PV sums
-//     cancel, so bf16 weights cost ~3e-2 absolute); the row sum is kept in float64;
+//     cancel, so bf16 weights cost ~3e-2 absolute); the row sum adds the same float16
+//     weights and is kept in float64;
 //   * S^T = K Q^T (keys x queries) leaves each query's scores in one lane pair, so the
 //     online-softmax max and sum are lane-local plus one exchange across the two half
 //     waves; O^T += V^T P^T keeps the output with the same lane-per-query layout, so the
@@ -31,23 +32,16 @@ namespace prism {
 
 constexpr int kD = 128;
 
-__device__ __forceinline__ int k_lds_off(int r, int c) {  // K tile: 64 rows x 16 chunks
-  return r * 256 + ((c ^ (r & 15)) << 4);
-}
-__device__ __forceinline__ int vt_lds_off(int d, int c) {  // V^T tile: 128 rows x 8 chunks
-  return d * 128 + ((c ^ ((d >> 1) & 7)) << 4);
-}
-
 constexpr int NW = 8;      // waves per workgroup: 8 x 32 = 256 query rows, one block
 constexpr int kStages = 4;  // LDS ring depth (units in flight: 3 ahead of the one computed)
-constexpr int kCpw = 32 / NW;  // 1 KB copies per wave per unit (16 for K, 16 for V^T)
+constexpr int kCpw = 32 / NW;  // 1 KB copies per wave per unit (16 for K, 16 for V)
 
 // Four LDS stages of 32 KB (distinct objects, named statically by the unrolled unit loop)
-// filled by direct global->LDS copies: waves 0-3 copy 16 K rows each, waves 4-7 32 V^T
-// rows each, 4 instructions of 1 KB per wave and unit.
+// filled by direct global->LDS copies: waves 0-3 copy 16 K rows each, waves 4-7 16 V rows
+// each, 4 instructions of 1 KB per wave and unit.
 struct FwdStage {
-  uint8_t k[16384];   // [64 keys][128] bf16, swizzled
-  uint8_t vt[16384];  // [128][64 keys] f16, swizzled
+  uint8_t k[16384];  // [64 keys][128] float16, swizzled
+  uint8_t v[16384];  // [64 keys][128] float16, swizzled (read transposed)
 };
 __shared__ __align__(16) FwdStage g_fwd0;
 __shared__ __align__(16) FwdStage g_fwd1;
@@ -58,29 +52,30 @@ __device__ __forceinline__ FwdStage &fwd_stage() {
   return S == 0 ? g_fwd0 : (S == 1 ? g_fwd1 : (S == 2 ? g_fwd2 : g_fwd3));
 }
 struct FwdState {
-  bf16x8 qreg[8];
+  f16x8 qreg[8];
   f32x16 o[4];
   float m, mk;
   double lsum;
 };
 
 __device__ __forceinline__ void fwd_unit_on(FwdState &w, const uint8_t *__restrict__ Kt,
-                                            const uint8_t *__restrict__ Vt, int l32, int hh,
+                                            const uint8_t *__restrict__ Vt, int lane,
                                             float scale_log2e) {
+  const int l32 = lane & 31, hh = lane >> 5;
   // S^T for keys 0-31 (a = 0) and 32-63 (a = 1): lane = query l32, 16 keys per tile
   f32x16 s[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int r = 32 * a + l32;
-    bf16x8 ka[8];
+    f16x8 ka[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
       ka[kk] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4 *>(Kt + k_lds_off(r, 2 * kk + hh)));
+          f16x8, *reinterpret_cast<const u32x4 *>(Kt + rm_swz(r, 2 * kk + hh)));
     __builtin_amdgcn_sched_barrier(0);
     s[a] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) s[a] = mfma_bf16(ka[kk], w.qreg[kk], s[a]);
+    for (int kk = 0; kk < 8; ++kk) s[a] = mfma_f16(ka[kk], w.qreg[kk], s[a]);
   }
   // online softmax (log2 domain) with lazy rescaling: the running max only moves when a
   // query's new maximum exceeds it by more than 2^kLazy, so the float16 weights
@@ -123,15 +118,12 @@ __device__ __forceinline__ void fwd_unit_on(FwdState &w, const uint8_t *__restri
       psum = __builtin_amdgcn_fdot2(f16x2{pb[g][e], pb[g][e + 1]}, f16x2{1, 1}, psum, false);
   }
   w.lsum += (double)psum;
-  // O^T[d][q] += V^T[d][keys] P^T[keys][q]
+  // O^T[d][q] += V^T[d][keys] P^T[keys][q], V^T read transposed from the row-major tile
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
-    const int d = 32 * dt + l32;
     f16x8 va[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      va[g] = __builtin_bit_cast(
-          f16x8, *reinterpret_cast<const u32x4 *>(Vt + vt_lds_off(d, 2 * g + hh)));
+    for (int g = 0; g < 4; ++g) va[g] = tr_operand(Vt, 16 * g, 32 * dt, lane);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < 4; ++g) w.o[dt] = mfma_f16(va[g], pb[g], w.o[dt]);
@@ -139,8 +131,14 @@ __device__ __forceinline__ void fwd_unit_on(FwdState &w, const uint8_t *__restri
 }
 
 template <int S>
-__device__ __forceinline__ void fwd_unit(FwdState &w, int l32, int hh, float scale_log2e) {
-  fwd_unit_on(w, fwd_stage<S>().k, fwd_stage<S>().vt, l32, hh, scale_log2e);
+__device__ __forceinline__ void fwd_unit(FwdState &w, int lane, float scale_log2e) {
+  // an opaque zero added to the stage address keeps the compiler from hoisting the per-lane
+  // swizzled addresses of all four stages into registers for the whole loop
+  int z = 0;
+  asm volatile("" : "+v"(z));
+  const FwdStage &st = *reinterpret_cast<const FwdStage *>(
+      reinterpret_cast<const uint8_t *>(&fwd_stage<S>()) + z);
+  fwd_unit_on(w, st.k, st.v, lane, scale_log2e);
 }
 
 // s_waitcnt vmcnt(2 kCpw) (expcnt and lgkmcnt left alone), then a workgroup barrier: every
@@ -149,9 +147,7 @@ __device__ __forceinline__ void fwd_unit(FwdState &w, int l32, int hh, float sca
 // wave's have.  The count is the same on every path, which also lets the compiler see that
 // no further wait is needed before the LDS reads.
 __device__ __forceinline__ void wait_unit_two_behind() {
-  __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * kCpw));
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  wait_and_barrier<vmcnt_imm(2 * kCpw)>();
 }
 
 // One workgroup (8 waves, one per 32 rows; two waves per SIMD, 128 KB of LDS) per query
@@ -159,7 +155,7 @@ __device__ __forceinline__ void wait_unit_two_behind() {
 __global__ void __launch_bounds__(NW * 64)
     attn_fwd_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
                          const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
-                         const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vpt,
+                         const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
                          const int *__restrict__ unit_blk, const int *__restrict__ blk_start,
                          const int *__restrict__ blk_size, const int *__restrict__ sel_count,
                          const int *__restrict__ csr_col, const int *__restrict__ perm,
@@ -171,18 +167,14 @@ __global__ void __launch_bounds__(NW * 64)
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   const int ntiles = *tile_count;
-  // copies of this wave: K rows 16w.. (w < 4) or V^T rows 32(w-4).. (w >= 4)
+  // copies of this wave: K rows 16w.. (w < 4) or V rows 16(w-4).. (w >= 4)
   const bool kcopy = wave < NW / 2;
   const int wq = wave & (NW / 2 - 1);
-  const uint8_t *csrc = reinterpret_cast<const uint8_t *>(kcopy ? kp : vpt);
+  const uint8_t *csrc = reinterpret_cast<const uint8_t *>(kcopy ? kp : vp);
   const int cdst = (kcopy ? 0 : 16384) + wq * 4096;
   auto cofs = [&](int i) {  // byte offset inside the unit of this lane's 16 bytes, copy i
-    if (kcopy) {
-      const int r = 16 * wq + 4 * i + (lane >> 4);
-      return r * 256 + (((lane & 15) ^ (r & 15)) << 4);
-    }
-    const int d = 32 * wq + 8 * i + (lane >> 3);
-    return d * 128 + (((lane & 7) ^ ((d >> 1) & 7)) << 4);
+    const int r = 16 * wq + 4 * i + (lane >> 4);
+    return r * 256 + (((lane & 15) ^ (r & 15)) << 4);
   };
 
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
@@ -204,7 +196,7 @@ __global__ void __launch_bounds__(NW * 64)
       const uint16_t *qrow = qp + ((size_t)h * N + row0 + l32) * kD + 8 * hh;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
-        w.qreg[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 16 * kk));
+        w.qreg[kk] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(qrow + 16 * kk));
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) w.o[dt] = f32x16{};
@@ -214,7 +206,7 @@ __global__ void __launch_bounds__(NW * 64)
 
     // the Q rows (and the cursor's first window) have landed before any copy is issued,
     // so no later LDS read or MFMA waits behind the copies for them
-    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     const uint8_t *hbase = csrc + (size_t)h * N * kD * 2;
     int issued = 0;
     bool pending = true;  // pre points at a unit not yet issued
@@ -231,8 +223,7 @@ __global__ void __launch_bounds__(NW * 64)
       }
     };
 
-    __builtin_amdgcn_s_barrier();  // every wave is done with the previous tile's stages
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    workgroup_barrier();  // every wave is done with the previous tile's stages
     issue(g_fwd0);
     issue(g_fwd1);
     issue(g_fwd2);
@@ -242,21 +233,21 @@ __global__ void __launch_bounds__(NW * 64)
       if (i >= issued) break;
       wait_unit_two_behind();
       issue(g_fwd3);
-      if (active) fwd_unit<0>(w, l32, hh, scale_log2e);
+      if (active) fwd_unit<0>(w, lane, scale_log2e);
       if (i + 1 >= issued) break;
       wait_unit_two_behind();
       issue(g_fwd0);
-      if (active) fwd_unit<1>(w, l32, hh, scale_log2e);
+      if (active) fwd_unit<1>(w, lane, scale_log2e);
       if (i + 2 >= issued) break;
       wait_unit_two_behind();
       issue(g_fwd1);
-      if (active) fwd_unit<2>(w, l32, hh, scale_log2e);
+      if (active) fwd_unit<2>(w, lane, scale_log2e);
       if (i + 3 >= issued) break;
       wait_unit_two_behind();
       issue(g_fwd2);
-      if (active) fwd_unit<3>(w, l32, hh, scale_log2e);
+      if (active) fwd_unit<3>(w, lane, scale_log2e);
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // the trailing repeat copies
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the trailing repeat copies
     // epilogue
     if (!active) continue;
     const double ltot = w.lsum + __shfl_xor(w.lsum, 32, 64);  // the two half waves' keys
@@ -377,7 +368,7 @@ hipError_t launch_attn_fwd(const Dims &d, float scale, uint8_t *ws, const Layout
     hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, d.N, d.U,
                        d.nb_max, d.heads, (const int2 *)(ws + L.btiles), counters + 1,
                        (const uint16_t *)(ws + L.qp), (const uint16_t *)(ws + L.kp),
-                       (const uint16_t *)(ws + L.vpt), unit_blk, bstart, bsize, cnt, cols, perm,
+                       (const uint16_t *)(ws + L.vp), unit_blk, bstart, bsize, cnt, cols, perm,
                        sl2e, (uint16_t *)o, lse, o32p, lsep);
   } else {
     dim3 grid(d.U, d.heads);

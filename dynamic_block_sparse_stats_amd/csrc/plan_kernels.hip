@@ -348,25 +348,17 @@ hipError_t launch_quantize(const Dims &d, const prism_config *cfg, const double 
 // block is contiguous, with one partition shared by Q, K and V): zones in raster order,
 // blocks inside a zone in raster order of block coordinates, tokens inside a block in
 // raster order.  One workgroup per (zone, head) writes perm / inv_perm, copies the zone's
-// 512 rows of Q, K, V into the permuted row-major layout (and, for bfloat16, into a
-// per-64-token-unit transposed float16 layout [D][64] used as the key-major MFMA operand
-// against float16 softmax weights), and
-// forms the float32 block means of Q and K (digest obstacles and selection sections).
-//
-// Transposed layout: within each group of 16 keys the stored order is
-// 0-3, 8-11, 4-7, 12-15 (bits 2 and 3 of the key index swapped), which makes the 8 keys a
-// lane feeds to one 32x32x16 MFMA step contiguous.
-__device__ __forceinline__ int swap23(int e) {
-  return (e & ~12) | ((e >> 1) & 4) | ((e << 1) & 8);
-}
-
-template <typename T, int D, bool TRANSPOSE>
+// 512 rows of Q, K, V into the permuted row-major layout (bfloat16 inputs are stored as
+// float16, the operand type of the attention MFMAs, saturated to the float16 range), and
+// forms the float32 block means of Q and K from the input values (digest obstacles and
+// selection sections).
+template <typename T, int D, bool F16>
 __global__ void __launch_bounds__(256)
     gather_kernel(int H, int W, int heads, int nzh, int nzw, int N, int nb_max, const T *q,
                   const T *k, const T *v, const int *__restrict__ zshape,
                   const int *__restrict__ zblock, int *__restrict__ perm,
-                  int *__restrict__ inv, T *qp, T *kp, T *vp, T *qpt, T *kpt, T *vpt,
-                  float *__restrict__ qbar, float *__restrict__ kbar, int Z) {
+                  int *__restrict__ inv, T *qp, T *kp, T *vp, float *__restrict__ qbar,
+                  float *__restrict__ kbar, int Z) {
   constexpr int VPC = 16 / (int)sizeof(T);  // values per 16-byte chunk
   constexpr int CH = D / VPC;               // chunks per row
   constexpr int RG = 256 / CH;              // rows per pass
@@ -381,7 +373,6 @@ __global__ void __launch_bounds__(256)
 
   __shared__ int tok[kZoneTok];
   __shared__ float psum[RG][D];
-  __shared__ __align__(16) uint16_t tile[TRANSPOSE ? kUnit * D : 8];
 
   for (int p = tid; p < kZoneTok; p += 256) {
     int beta = p / B, r = p % B;
@@ -399,7 +390,6 @@ __global__ void __launch_bounds__(256)
   const int c = tid % CH, rg = tid / CH;
   const T *src[3] = {q, k, v};
   T *dst[3] = {qp, kp, vp};
-  T *dstt[3] = {qpt, kpt, vpt};
   float *bar[2] = {qbar, kbar};
   const size_t tstride = (size_t)heads * D;
   for (int x = 0; x < 3; ++x) {
@@ -417,8 +407,15 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
       for (int rr = 0; rr < RPT; ++rr) {
         int p = s * kUnit + rg + RG * rr;
+        u32x4 out = buf[rr];
+        if constexpr (F16) {  // the attention kernels read float16 copies
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            out[e] = (uint32_t)bf16_to_f16_bits((uint16_t)(buf[rr][e] & 0xffffu)) |
+                     ((uint32_t)bf16_to_f16_bits((uint16_t)(buf[rr][e] >> 16)) << 16);
+        }
         *reinterpret_cast<u32x4 *>(dst[x] + ((size_t)h * N + kZoneTok * m + p) * D + c * VPC) =
-            buf[rr];
+            out;
         if (x < 2) {
           if constexpr (sizeof(T) == 2) {
             const uint32_t *w32 = reinterpret_cast<const uint32_t *>(&buf[rr]);
@@ -433,31 +430,6 @@ __global__ void __launch_bounds__(256)
             for (int e = 0; e < VPC; ++e) acc[e] += f[e];
           }
         }
-        if constexpr (TRANSPOSE) {
-          int row = rg + RG * rr;
-          *reinterpret_cast<u32x4 *>(&tile[row * D + c * VPC]) = buf[rr];
-        }
-      }
-      if constexpr (TRANSPOSE) {
-        __syncthreads();
-        // [D][64] for this unit: thread -> (d, half of the 64 keys)
-        const int dd = tid >> 1, half = tid & 1;
-        const size_t ubase = ((size_t)h * (N / kUnit) + (size_t)m * 8 + s) * (size_t)(D * kUnit);
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          uint32_t pk[4];
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            int pos0 = 32 * half + 8 * cc + e;
-            int key0 = (pos0 & ~15) | swap23(pos0 & 15);
-            int key1 = ((pos0 + 1) & ~15) | swap23((pos0 + 1) & 15);
-            pk[e >> 1] = (uint32_t)bf16_to_f16_bits(tile[key0 * D + dd]) |
-                         ((uint32_t)bf16_to_f16_bits(tile[key1 * D + dd]) << 16);
-          }
-          *reinterpret_cast<u32x4 *>(dstt[x] + ubase + (size_t)dd * kUnit + 32 * half + 8 * cc) =
-              u32x4{pk[0], pk[1], pk[2], pk[3]};
-        }
-        __syncthreads();
       }
       // block boundary: reduce the pooled sums over the row groups
       if (x < 2 && ((s + 1) * kUnit) % B == 0) {
@@ -491,21 +463,19 @@ hipError_t launch_gather(const Dims &d, const void *q, const void *k, const void
     hipLaunchKernelGGL((gather_kernel<T, 128, true>), grid, dim3(256), 0, s, d.H, d.W, d.heads,
                        d.nzh, d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k, (const T *)v,
                        zshape, zblock, perm, inv, (T *)(ws + L.qp), (T *)(ws + L.kp),
-                       (T *)(ws + L.vp), (T *)(ws + L.qpt), (T *)(ws + L.kpt),
-                       (T *)(ws + L.vpt), qbar, kbar, d.Z);
+                       (T *)(ws + L.vp), qbar, kbar, d.Z);
   } else if (d.D == 64) {
     typedef float T;
     hipLaunchKernelGGL((gather_kernel<T, 64, false>), grid, dim3(256), 0, s, d.H, d.W, d.heads,
                        d.nzh, d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k, (const T *)v,
                        zshape, zblock, perm, inv, (T *)(ws + L.qp), (T *)(ws + L.kp),
-                       (T *)(ws + L.vp), nullptr, nullptr, nullptr, qbar, kbar, d.Z);
+                       (T *)(ws + L.vp), qbar, kbar, d.Z);
   } else {
     typedef float T;
     hipLaunchKernelGGL((gather_kernel<T, 128, false>), grid, dim3(256), 0, s, d.H, d.W,
                        d.heads, d.nzh, d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k,
                        (const T *)v, zshape, zblock, perm, inv, (T *)(ws + L.qp),
-                       (T *)(ws + L.kp), (T *)(ws + L.vp), nullptr, nullptr, nullptr, qbar,
-                       kbar, d.Z);
+                       (T *)(ws + L.kp), (T *)(ws + L.vp), qbar, kbar, d.Z);
   }
   return hipGetLastError();
 }

@@ -168,12 +168,6 @@ Layout make_layout(const Dims &d) {
   L.kp = take(tensor);
   L.vp = take(tensor);
   L.dop = take(tensor);
-  if (d.dtype == PRISM_BF16) {
-    L.qpt = take(tensor);
-    L.kpt = take(tensor);
-    L.vpt = take(tensor);
-    L.dopt = take(tensor);
-  }
   L.total = off;
   L.pub.total = off;
   L.pub.N = d.N;

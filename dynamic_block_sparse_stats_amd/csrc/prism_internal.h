@@ -28,7 +28,9 @@ struct TraceScope {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -45,19 +47,19 @@ struct Dims {
 // Internal workspace layout: the public arrays of prism_layout plus scratch.
 struct Layout {
   prism_layout pub;
-  size_t qp, kp, vp;        // permuted copies, row-major [heads][N][D]
-  size_t qpt, kpt, vpt;     // bf16 path only: per-unit transposed float16 [heads][U][D][64]
+  size_t qp, kp, vp;        // permuted copies, row-major [heads][N][D] (float16 for
+                            //   bfloat16 inputs, float32 for float32 inputs)
   size_t sel_bits;          // uint32 [heads][nb_max][words]
   size_t csc_bits;          // uint32 [heads][nb_max][words]
   size_t tiles;             // int2 [heads*U]: (head, first unit | kTile64) per query/key tile
   size_t btiles;            // int2 [heads*U]: (head, first unit | units << 16) per block
   size_t counters;          // int32 [16]: [0] = tile count, [1] = block tile count
-  size_t dop, dopt;         // bwd: gathered dout, row-major (bf16) and transposed (f16)
+  size_t dop;               // bwd: gathered dout, row-major [heads][N][D] (as qp)
   size_t o32p;              // fwd: float [heads][N][D] output in permuted order
   size_t lsep;              // fwd: float [heads][N] lse in permuted order
   size_t delta;             // bwd: float [heads][N] in permuted order: rowsum(dO * O)
-                            //   (float32 inputs) or -rowsum(dO * O) * 2^-kPShift (bfloat16)
-  size_t lse2;              // bwd (bfloat16): float [heads][N] lse * log2(e) - kPShift
+                            //   (float32 inputs) or -rowsum(dO * O) (bfloat16)
+  size_t lse2;              // bwd (bfloat16): float [heads][N] lse * log2(e)
   size_t total;
 };
 
@@ -92,12 +94,11 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
 // attn_bwd_dkdv.hip
 hipError_t launch_dkdv_bf16(int work_items, hipStream_t s, int N, int U, int nb_max, int heads,
                             const int2 *tiles, const int *counters, const uint16_t *qp,
-                            const uint16_t *qpt, const uint16_t *kp, const uint16_t *vp,
-                            const uint16_t *dop, const uint16_t *dopt, const float *lse2,
-                            const float *delta, const int *unit_blk, const int *bstart,
-                            const int *bsize, const int *tcnt, const int *trows,
-                            const int *perm, float scale, float sl2e, uint16_t *dk,
-                            uint16_t *dv);
+                            const uint16_t *kp, const uint16_t *vp, const uint16_t *dop,
+                            const float *lse2, const float *ndelta, const int *unit_blk,
+                            const int *bstart, const int *bsize, const int *tcnt,
+                            const int *trows, const int *perm, float scale, float sl2e,
+                            uint16_t *dk, uint16_t *dv);
 
 // Workgroups of `kernel` (block size `block`) that fit on the current device at once: the
 // grid of the persistent attention kernels.
@@ -112,6 +113,34 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+// Row-major [64][128] 16-bit LDS tile: 16 chunks of 16 bytes per row, chunk c of row r
+// stored at chunk c ^ (r % 16), so that 16-byte reads of one chunk column by 16 rows, and
+// the transposed reads below, spread over all banks.
+__device__ __forceinline__ int rm_swz(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+
+// The A operand of a 32x32x16 float16 MFMA taken transposed from a row-major float16 tile
+// X[k][d] with ds_read_b64_tr_b16 (in each 16-lane group, lane i receives element i % 4 of
+// the 8-byte pieces addressed by lanes 4j + i / 4, j = 0..3).  Lane l gets, in register e,
+// X[kb + 8 (e / 4) + 4 (l / 32) + e % 4][db + l % 32]: row l % 32 of the transposed tile
+// and the same key order as a B operand taken from a C tile (register v of a C tile holds
+// row (v / 4) * 8 + 4 (l / 32) + v % 4).  kb is a multiple of 16, db of 32.
+__device__ __forceinline__ f16x8 tr_operand(const uint8_t *tile, int kb, int db, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int col = db + 16 * (g & 1) + 4 * (s & 3);
+  f16x8 r;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int row = kb + 8 * m + 4 * (g >> 1) + (s >> 2);
+    const fp16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+        (__attribute__((address_space(3))) fp16x4_t *)(tile + rm_swz(row, col >> 3) +
+                                                       (col & 7) * 2));
+    const f16x4 w = __builtin_bit_cast(f16x4, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[4 * m + e] = w[e];
+  }
+  return r;
 }
 
 // Typed MFMA wrappers: the builtins accept any 8-element 16-bit vector silently, these do
@@ -141,10 +170,27 @@ __device__ __forceinline__ void dma4(const void *src, void *dst) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
                                    (__attribute__((address_space(3))) void *)dst, 4, 0, 0);
 }
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone), then a workgroup barrier that the
-// compiler may not move memory operations across.
-__device__ __forceinline__ void wait_copies_and_sync() {
-  __builtin_amdgcn_s_waitcnt(0x0070 | 0x0f00);
+// s_waitcnt with the given immediate, then a workgroup barrier.  The compiler fences on
+// both sides keep every memory operation of this wave in program order around the pair:
+// LDS writes issued before it are covered by the wait (s_barrier itself does not order
+// memory for the compiler).
+template <int IMM>
+__device__ __forceinline__ void wait_and_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(IMM);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8): wait for this wave's vector memory operations down to n outstanding, or for its
+// LDS operations
+constexpr int vmcnt_imm(int n) { return 0x0f70 | n; }
+constexpr int kLgkm0 = 0xc07f;
+// every copy of this wave has landed, then a workgroup barrier
+__device__ __forceinline__ void wait_copies_and_sync() { wait_and_barrier<vmcnt_imm(0)>(); }
+// a workgroup barrier that the compiler may not move memory operations across
+__device__ __forceinline__ void workgroup_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
