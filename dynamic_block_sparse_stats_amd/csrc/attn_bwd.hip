@@ -192,7 +192,7 @@ __global__ void __launch_bounds__(QW * 64)
   const int cdst = (kcopy ? 0 : 16384) + wq * 4096;
   auto cofs = [&](int i) {  // byte offset inside the unit of this lane's 16 bytes, copy i
     const int r = 16 * wq + 4 * i + (lane >> 4);
-    return r * 256 + (((lane & 15) ^ (r & 15)) << 4);
+    return r * 256 + (((lane & 15) ^ swz(r)) << 4);
   };
 
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {

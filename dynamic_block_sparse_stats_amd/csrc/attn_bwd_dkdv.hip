@@ -198,7 +198,7 @@ __device__ __forceinline__ void dkdv_waves(
   const int cdst = (PW ? 0 : 16384) + pair * 4096;
   auto cofs = [&](int i) {  // byte offset inside the unit of this lane's 16 bytes, copy i
     const int r = 16 * pair + 4 * i + (lane >> 4);
-    return r * 256 + (((lane & 15) ^ (r & 15)) << 4);
+    return r * 256 + (((lane & 15) ^ swz(r)) << 4);
   };
   const bool vcopy = wave < 2;
   const float *vsrc = wave == 1 ? ndelta : lse2;

@@ -115,10 +115,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Row-major [64][128] 16-bit LDS tile: 16 chunks of 16 bytes per row, chunk c of row r
-// stored at chunk c ^ (r % 16), so that 16-byte reads of one chunk column by 16 rows, and
-// the transposed reads below, spread over all banks.
-__device__ __forceinline__ int rm_swz(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+// Row-major [64][128] 16-bit LDS tile: 16 chunks of 16 bytes per row (one row spans the 64
+// banks once), chunk c of row r stored at chunk c ^ swz(r), swz(r) = 4 (r % 4) + (r / 4) % 4.
+// swz is a bijection on r % 16, so 16-byte reads of one chunk by 16 consecutive rows hit
+// 16 different chunk positions; and four consecutive rows (r % 4 = 0..3, same (r / 4) % 4)
+// spread a group of four aligned chunks over four different quarters of the banks, which
+// keeps the 8-byte transposed reads below (4 rows x 4 chunks x 2 halves per 32 lanes)
+// free of bank conflicts too.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int rm_swz(int r, int c) { return r * 256 + ((c ^ swz(r)) << 4); }
 
 // The A operand of a 32x32x16 float16 MFMA taken transposed from a row-major float16 tile
 // X[k][d] with ds_read_b64_tr_b16 (in each 16-lane group, lane i receives element i % 4 of
