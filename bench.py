@@ -29,6 +29,36 @@ import numpy as np
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# HBM bytes per launch of the attention kernels on the 2K training workload, from two
+# rocprofv3 counter passes over one step (FETCH_SIZE x 2 x 1024 + WRITE_SIZE x 1024 bytes;
+# the scales come from a 1 GiB device copy measured in the same runs), together with the
+# hash of the kernel sources they were taken with: a kernel changed since reports null.
+KERNEL_SOURCES = {"attn_fwd": "attn_fwd.hip", "bwd_dkdv": "attn_bwd_dkdv.hip",
+                  "bwd_dq": "attn_bwd.hip"}
+MEASURED_TRAFFIC = {
+    ("attn_fwd", "2k-train-64x104x128"): ("4bda8980806984e3", 30.775e12),
+    ("bwd_dkdv", "2k-train-64x104x128"): ("5d17afab71d7506a", 60.964e12),
+    ("bwd_dq", "2k-train-64x104x128"): ("d54ce15834e6145c", 30.771e12),
+}
+
+
+def kernel_source_hash(kernel):
+    import hashlib
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "dynamic_block_sparse_stats_amd", "csrc")
+    m = hashlib.sha1()
+    for f in (KERNEL_SOURCES[kernel], "prism_internal.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            m.update(fh.read())
+    return m.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    entry = MEASURED_TRAFFIC.get((kernel, workload))
+    if entry is None or kernel_source_hash(kernel) != entry[0]:
+        return None
+    return entry[1]
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -42,6 +72,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run one plain device-to-device copy of MIB mebibytes (a "
+                         "kernel of known traffic for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -181,6 +214,16 @@ def main():
 
     wl = synth.workload(args.workload)
     dev = "cuda"
+    if args.copy_calibration:
+        n = args.copy_calibration << 18  # float32 elements
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# calibration copy of {args.copy_calibration} MiB done", file=sys.stderr,
+              flush=True)
+        del src, dst
     backward = wl.backward
     t0 = time.perf_counter()
     inp = synth.make_inputs(wl, device=dev, with_dout=True)
@@ -239,8 +282,12 @@ def main():
     achieved = kernel_flops[dom] / (per_launch_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom, wl.name),
                 "launch_ms": round(per_launch_ms, 3)}
+    if roofline["traffic"] is not None:
+        roofline["traffic_note"] = ("HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                    "scaled by a 1 GiB copy)")
 
     # dense comparators on a subset of heads, scaled by the head count
     dense = {}
