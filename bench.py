@@ -72,6 +72,17 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--policy", default=None,
+                    help="selection policy of the pages' sparsity ablation, replacing the "
+                         "workload's Top-k/Top-p: pages (k = 5%% of blocks + p 0.2), topk75, "
+                         "topk85, topk95, topp0.1, topp0.2, topp0.3, topk95+p0.1, topk95+p0.3")
+    ap.add_argument("--fixed-shape", default=None, metavar="TxHxW",
+                    help="fixed-shape baseline: every zone cut into blocks of this shape")
+    ap.add_argument("--map-exponent", type=float, default=0.0,
+                    help="mapping ablation: exponent a of b_d ~ g_d^-a (default 1/2)")
+    ap.add_argument("--density-mode", type=int, default=0,
+                    help="density ablation: 0 spatial+temporal, 1 spatial, 2 temporal, "
+                         "3 A2V intensity")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device-to-device copy of MIB mebibytes (a "
                          "kernel of known traffic for scaling hardware byte counters)")
@@ -144,7 +155,7 @@ def time_dense_own(P, wl, inp, heads, backward, steps=2):
     return min(ts)
 
 
-def cpu_baseline(wl, inp, budget_s):
+def cpu_baseline(wl, cfg, inp, budget_s):
     """The CPU oracle as it stands on a bounded sample of the workload: the full plan of
     head 0, then the forward and backward of a seeded sample of head-0 query rows."""
     import oracle
@@ -156,8 +167,11 @@ def cpu_baseline(wl, inp, budget_s):
     a = inp["a2v"].double().cpu().numpy()
     do = inp["dout"][:, h].double().cpu().numpy() if wl.backward else None
     t0 = time.perf_counter()
-    op = oracle.plan_head(wl.T, wl.H, wl.W, q, k, v, a, top_k=wl.top_k, top_p=wl.top_p,
-                          min_edge_log2=wl.min_edge_log2)
+    op = oracle.plan_head(wl.T, wl.H, wl.W, q, k, v, a, top_k=cfg.top_k, top_p=cfg.top_p,
+                          min_edge_log2=wl.min_edge_log2, top_k_frac=cfg.top_k_frac,
+                          fixed_shape=cfg.fixed_shape,
+                          map_exponent=cfg.map_exponent if cfg.map_exponent > 0 else 0.5,
+                          density_mode=cfg.density_mode)
     t_plan = time.perf_counter() - t0
     tok_blk = np.empty(wl.N, dtype=np.int64)
     tok_blk[op.perm] = op.bof
@@ -230,7 +244,16 @@ def main():
     torch.cuda.synchronize()
     print(f"# inputs {wl.name} ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
           flush=True)
-    cfg = P.config_for(wl)
+    over = {}
+    if args.policy:
+        over.update(P.POLICIES[args.policy])
+    if args.fixed_shape:
+        over["fixed_shape"] = P.shape_code(*[int(x) for x in args.fixed_shape.split("x")])
+    if args.map_exponent > 0:
+        over["map_exponent"] = args.map_exponent
+    if args.density_mode:
+        over["density_mode"] = args.density_mode
+    cfg = P.config_for(wl, **over)
     att = P.PrismAttention(cfg)
 
     def step():
@@ -316,7 +339,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         try:
-            cpu = cpu_baseline(wl, inp, args.cpu_seconds)
+            cpu = cpu_baseline(wl, cfg, inp, args.cpu_seconds)
         except Exception as e:  # noqa: BLE001
             cpu = {"error": repr(e)[:300]}
 
@@ -331,7 +354,10 @@ def main():
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded smooth field + moving blobs; no dataset)",
         "config": {"workload": wl.name, "tokens": N, "heads": Hh, "head_dim": D,
-                   "top_k": wl.top_k, "top_p": wl.top_p, "backward": backward,
+                   "top_k": cfg.top_k, "top_k_frac": round(cfg.top_k_frac, 6),
+                   "top_p": round(cfg.top_p, 6), "policy": args.policy or "workload",
+                   "fixed_shape": args.fixed_shape, "map_exponent": cfg.map_exponent or 0.5,
+                   "density_mode": cfg.density_mode, "backward": backward,
                    "parallelism": "single GPU (heads in one call)"},
         "stage_ms": {k: round(v, 3) for k, v in stage_ms.items()},
         "plan_ms": round(plan_ms, 3), "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),

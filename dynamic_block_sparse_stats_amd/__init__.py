@@ -34,7 +34,9 @@ class PrismConfig(ctypes.Structure):
                 ("top_k", ctypes.c_int), ("top_p", ctypes.c_float),
                 ("tau128", ctypes.c_float), ("tau256", ctypes.c_float),
                 ("eps", ctypes.c_double), ("score_scale", ctypes.c_float),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("top_k_frac", ctypes.c_float),
+                ("fixed_shape", ctypes.c_int), ("map_exponent", ctypes.c_float),
+                ("density_mode", ctypes.c_int)]
 
     @property
     def N(self) -> int:
@@ -102,12 +104,38 @@ def lib():
 
 def make_config(T, H, W, num_heads, head_dim, dtype="bf16", min_edge_log2=1, top_k=8,
                 top_p=0.9, tau128=0.5, tau256=0.25, eps=1e-6, score_scale=0.0,
-                softmax_scale=0.0) -> PrismConfig:
+                softmax_scale=0.0, top_k_frac=0.0, fixed_shape=0, map_exponent=0.0,
+                density_mode=0) -> PrismConfig:
     dt = {"f32": F32, "bf16": BF16, F32: F32, BF16: BF16, torch.float32: F32,
           torch.bfloat16: BF16}[dtype]
     return PrismConfig(T, H, W, num_heads, head_dim, dt, min_edge_log2, int(top_k),
                        float(top_p), float(tau128), float(tau256), float(eps),
-                       float(score_scale), float(softmax_scale))
+                       float(score_scale), float(softmax_scale), float(top_k_frac),
+                       int(fixed_shape), float(map_exponent), int(density_mode))
+
+
+def shape_code(bT: int, bH: int, bW: int) -> int:
+    """The packed shape code (log2 edges, lT*16 + lH*4 + lW) of a block of bT x bH x bW."""
+    lg = [int(x).bit_length() - 1 for x in (bT, bH, bW)]
+    if any(1 << l != x for l, x in zip(lg, (bT, bH, bW))):
+        raise ValueError("block edges must be powers of two")
+    return lg[0] * 16 + lg[1] * 4 + lg[2]
+
+
+# Selection policies of the pages' sparsity ablation (digest, ablation table of per-query
+# sparsity strategies): Top-k as a sparsity (k = ceil((1 - s) * Nb)), Top-p thresholds,
+# and their union; "pages" is the default configuration (95% + 0.2).
+POLICIES = {
+    "pages": dict(top_k=0, top_k_frac=0.05, top_p=0.2),
+    "topk75": dict(top_k=0, top_k_frac=0.25, top_p=0.0),
+    "topk85": dict(top_k=0, top_k_frac=0.15, top_p=0.0),
+    "topk95": dict(top_k=0, top_k_frac=0.05, top_p=0.0),
+    "topp0.1": dict(top_k=0, top_k_frac=0.0, top_p=0.1),
+    "topp0.2": dict(top_k=0, top_k_frac=0.0, top_p=0.2),
+    "topp0.3": dict(top_k=0, top_k_frac=0.0, top_p=0.3),
+    "topk95+p0.1": dict(top_k=0, top_k_frac=0.05, top_p=0.1),
+    "topk95+p0.3": dict(top_k=0, top_k_frac=0.05, top_p=0.3),
+}
 
 
 def config_for(wl, **over) -> PrismConfig:

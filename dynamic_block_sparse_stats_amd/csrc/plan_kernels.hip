@@ -66,7 +66,7 @@ hipError_t launch_audio_stats(const Dims &d, const float *a2v, double *astat, hi
 // the zone mean, averaged over channels (review item 1), and rho_raw = channel-mean
 // spatial variance about the per-frame mean plus the channel-mean squared frame-to-frame
 // difference of the frame profile over Z_T - 1 pairs (digest, density section, Eq.
-// rho_raw).  One wave per (zone, head): the wave reads the zone's 512 token rows of this
+// rho_raw; the density ablation can keep one of the two terms).  One wave per (zone, head): the wave reads the zone's 512 token rows of this
 // head (each a contiguous D-element row, so every load instruction covers one row), and
 // every lane accumulates raw float64 sums of its channels: frame sums, h-row sums, w-column
 // sums and the sum of squares, all shifted by the zone's first token to keep the variance
@@ -74,7 +74,8 @@ hipError_t launch_audio_stats(const Dims &d, const float *a2v, double *astat, hi
 template <typename T, int D>
 __global__ void __launch_bounds__(64) zone_stats_kernel(int H, int W, int heads, int nzh,
                                                         int nzw, const T *__restrict__ v,
-                                                        double *__restrict__ out, int Z) {
+                                                        int dmode, double *__restrict__ out,
+                                                        int Z) {
   constexpr int CPL = D / 64;  // channels per lane
   const int m = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const int zw = m % nzw, zh = (m / nzw) % nzh, zt = m / (nzw * nzh);
@@ -154,7 +155,8 @@ __global__ void __launch_bounds__(64) zone_stats_kernel(int H, int W, int heads,
     acc[0] += vt / kZone;
     acc[1] += vh / kZone;
     acc[2] += vw / kZone;
-    acc[3] += spatial + td / (kZone - 1);
+    // density ablation: dmode 1 keeps only the spatial term, 2 only the temporal one
+    acc[3] += (dmode == 2 ? 0.0 : spatial) + (dmode == 1 ? 0.0 : td / (kZone - 1));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1)
@@ -169,18 +171,19 @@ __global__ void __launch_bounds__(64) zone_stats_kernel(int H, int W, int heads,
   }
 }
 
-hipError_t launch_zone_stats(const Dims &d, const void *v, double *zstat, hipStream_t s) {
+hipError_t launch_zone_stats(const Dims &d, const void *v, int dmode, double *zstat,
+                             hipStream_t s) {
   TraceScope tr(PRISM_STAGE_ZONE_STATS, s);
   dim3 grid(d.Z, d.heads);
   if (d.dtype == PRISM_BF16) {
     hipLaunchKernelGGL((zone_stats_kernel<uint16_t, 128>), grid, dim3(64), 0, s, d.H, d.W,
-                       d.heads, d.nzh, d.nzw, (const uint16_t *)v, zstat, d.Z);
+                       d.heads, d.nzh, d.nzw, (const uint16_t *)v, dmode, zstat, d.Z);
   } else if (d.D == 64) {
     hipLaunchKernelGGL((zone_stats_kernel<float, 64>), grid, dim3(64), 0, s, d.H, d.W, d.heads,
-                       d.nzh, d.nzw, (const float *)v, zstat, d.Z);
+                       d.nzh, d.nzw, (const float *)v, dmode, zstat, d.Z);
   } else {
     hipLaunchKernelGGL((zone_stats_kernel<float, 128>), grid, dim3(64), 0, s, d.H, d.W, d.heads,
-                       d.nzh, d.nzw, (const float *)v, zstat, d.Z);
+                       d.nzh, d.nzw, (const float *)v, dmode, zstat, d.Z);
   }
   return hipGetLastError();
 }
@@ -198,9 +201,12 @@ hipError_t launch_zone_stats(const Dims &d, const void *v, double *zstat, hipStr
 // arithmetic is written without fused multiply-adds so that each decision is taken on the
 // same float64 values a plain evaluation of these formulas gives.  Then the per-zone block
 // counts are scanned into the block table.
+// Ablation settings (digest, ablation section): alpha replaces the 1/2 of the mapping
+// b_d ~ g_d^-1/2; fixed > 0 gives every zone that packed shape (no shape decision, margin
+// 1e300); dmode 3 takes the volume tier from a_bar instead of rho.
 __device__ void shape_of_zone(const double *vs, const double *as, double rho_max, double a_max,
-                              double tau128, double tau256, double eps, int mel, int *code_out,
-                              int *S_out, double *diag) {
+                              double tau128, double tau256, double eps, int mel, double alpha,
+                              int fixed, int dmode, int *code_out, int *S_out, double *diag) {
 #pragma clang fp contract(off)
   double rho = rho_max > 0 ? vs[3] / rho_max : 0.0;
   double vsum = vs[0] + vs[1] + vs[2];
@@ -211,6 +217,7 @@ __device__ void shape_of_zone(const double *vs, const double *as, double rho_max
     double asum = as[1] + as[2] + as[3];
     for (int dd = 0; dd < 3; ++dd) va[dd] = asum > 0 ? as[1 + dd] / asum : 0.0;
   }
+  if (dmode == 3) rho = abar;
   double g[3], lg[3], ls[3];
   for (int dd = 0; dd < 3; ++dd) {
     double t = abar * va[dd];
@@ -220,19 +227,20 @@ __device__ void shape_of_zone(const double *vs, const double *as, double rho_max
   int S = rho >= tau128 ? 6 : (rho >= tau256 ? 7 : 8);
   for (int dd = 0; dd < 3; ++dd) lg[dd] = log2(g[dd]);
   double hs = (double)S;
-  hs = hs + 0.5 * lg[0];
-  hs = hs + 0.5 * lg[1];
-  hs = hs + 0.5 * lg[2];
+  hs = hs + alpha * lg[0];
+  hs = hs + alpha * lg[1];
+  hs = hs + alpha * lg[2];
   hs = hs / 3.0;
-  for (int dd = 0; dd < 3; ++dd) ls[dd] = -0.5 * lg[dd] + hs;
+  for (int dd = 0; dd < 3; ++dd) ls[dd] = -alpha * lg[dd] + hs;
   double dist[19];
   int cand[19];
   int nc = 0;
   double best = INFINITY;
+  if (fixed > 0) S = ((fixed >> 4) & 3) + ((fixed >> 2) & 3) + (fixed & 3);
   for (int a = mel; a <= 3; ++a)
     for (int b = mel; b <= 3; ++b)
       for (int c = mel; c <= 3; ++c)
-        if (a + b + c == S) {
+        if (a + b + c == S && (fixed <= 0 || a * 16 + b * 4 + c == fixed)) {
           double e0 = ls[0] - a, e1 = ls[1] - b, e2 = ls[2] - c;
           double dsum = e0 * e0;
           dsum = dsum + e1 * e1;
@@ -256,7 +264,7 @@ __device__ void shape_of_zone(const double *vs, const double *as, double rho_max
   double tm = fabs(rho - tau128), tm2 = fabs(rho - tau256);
   diag[0] = rho;
   diag[1] = tm < tm2 ? tm : tm2;
-  diag[2] = second - best;
+  diag[2] = fixed > 0 ? 1e300 : second - best;
   diag[3] = best;
 }
 
@@ -265,7 +273,8 @@ constexpr int kQuantThreads = 1024;
 __global__ void __launch_bounds__(kQuantThreads)
     quantize_kernel(int Z, int nb_max, const double *__restrict__ zstat,
                     const double *__restrict__ astat, int have_audio, double tau128,
-                    double tau256, double eps, int mel, int *__restrict__ zshape,
+                    double tau256, double eps, int mel, double alpha, int fixed, int dmode,
+                    int *__restrict__ zshape,
                     int *__restrict__ zblock, double *__restrict__ zdiag,
                     int *__restrict__ blk_start, int *__restrict__ blk_size,
                     int *__restrict__ unit_blk) {
@@ -300,7 +309,7 @@ __global__ void __launch_bounds__(kQuantThreads)
   for (int m = m0; m < m1; ++m) {
     int code, S;
     shape_of_zone(zs + 4 * m, have_audio ? astat + 4 * m : nullptr, rmax, amax, tau128, tau256,
-                  eps, mel, &code, &S, zdiag + ((size_t)h * Z + m) * 4);
+                  eps, mel, alpha, fixed, dmode, &code, &S, zdiag + ((size_t)h * Z + m) * 4);
     zshape[(size_t)h * Z + m] = code;
     local += kZoneTok >> S;
   }
@@ -337,7 +346,8 @@ hipError_t launch_quantize(const Dims &d, const prism_config *cfg, const double 
   hipLaunchKernelGGL(quantize_kernel, dim3(d.heads), dim3(kQuantThreads), 0, s, d.Z, d.nb_max,
                      zstat, astat, have_audio ? 1 : 0, (double)cfg->tau128,
                      (double)cfg->tau256, cfg->eps, cfg->min_edge_log2,
-                     (int *)(ws + L.pub.zone_shape), (int *)(ws + L.pub.zone_block),
+                     cfg->map_exponent > 0.f ? (double)cfg->map_exponent : 0.5,
+                     cfg->fixed_shape, cfg->density_mode, (int *)(ws + L.pub.zone_shape), (int *)(ws + L.pub.zone_block),
                      (double *)(ws + L.pub.zone_diag), (int *)(ws + L.pub.block_start),
                      (int *)(ws + L.pub.block_size), (int *)(ws + L.pub.unit_block));
   return hipGetLastError();

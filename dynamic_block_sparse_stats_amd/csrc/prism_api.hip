@@ -100,6 +100,19 @@ prism_status check_config(const prism_config *cfg, Dims *d, const char **why) {
     *why = "top_k, top_p, tau, eps and scales must be finite and non-negative";
     return PRISM_ERR_ARG;
   }
+  if (!(cfg->top_k_frac >= 0.f && cfg->top_k_frac <= 1.f) || !isfinite(cfg->map_exponent) ||
+      cfg->density_mode < 0 || cfg->density_mode > 3) {
+    *why = "top_k_frac must be in [0, 1], map_exponent finite, density_mode 0..3";
+    return PRISM_ERR_ARG;
+  }
+  if (cfg->fixed_shape > 0) {
+    const int f = cfg->fixed_shape, a = (f >> 4) & 3, b = (f >> 2) & 3, c = f & 3;
+    if (f > 63 || a < cfg->min_edge_log2 || b < cfg->min_edge_log2 ||
+        c < cfg->min_edge_log2 || a + b + c < 6 || a + b + c > 8) {
+      *why = "fixed_shape must pack log2 edges >= min_edge_log2 with volume 64, 128 or 256";
+      return PRISM_ERR_ARG;
+    }
+  }
   if (cfg->num_heads > 4096) {
     *why = "too many heads in one call";
     return PRISM_ERR_UNSUPPORTED;
@@ -244,7 +257,8 @@ prism_status prism_plan(const prism_config *cfg, const void *q, const void *k, c
   if (a2v_norm) {
     if ((st = launched(launch_audio_stats(d, a2v_norm, astat, s), "audio stats"))) return st;
   }
-  if ((st = launched(launch_zone_stats(d, v, zstat, s), "zone stats"))) return st;
+  if ((st = launched(launch_zone_stats(d, v, cfg->density_mode, zstat, s), "zone stats")))
+    return st;
   if ((st = launched(launch_quantize(d, cfg, zstat, astat, a2v_norm != nullptr, ws, L, s),
                      "quantiser")))
     return st;

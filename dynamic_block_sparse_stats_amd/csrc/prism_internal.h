@@ -74,7 +74,8 @@ Scales scales_of(const prism_config *cfg, const Dims &d);
 // ---------------------------------------------------------------------------- launchers
 // plan_kernels.hip
 hipError_t launch_audio_stats(const Dims &d, const float *a2v, double *astat, hipStream_t s);
-hipError_t launch_zone_stats(const Dims &d, const void *v, double *zstat, hipStream_t s);
+hipError_t launch_zone_stats(const Dims &d, const void *v, int dmode, double *zstat,
+                             hipStream_t s);
 hipError_t launch_quantize(const Dims &d, const prism_config *cfg, const double *zstat,
                            const double *astat, bool have_audio, uint8_t *ws, const Layout &L,
                            hipStream_t s);

@@ -153,10 +153,12 @@ __device__ __forceinline__ uint32_t fkey(float f) {
 template <int NT, int WPT>
 __global__ void __launch_bounds__(NT)
     select_kernel(int nb_max, int words, const int *__restrict__ nb_ptr,
-                  const float *__restrict__ scores, int top_k, float top_p,
+                  const float *__restrict__ scores, int top_k, float top_k_frac, float top_p,
                   uint32_t *__restrict__ bits, int *__restrict__ count,
                   int *__restrict__ cols) {
   const int nb = *nb_ptr;
+  // Top-k as a fraction of this head's blocks (the pages' sparsity form), else a count
+  if (top_k_frac > 0.f) top_k = (int)ceil((double)top_k_frac * (double)nb);
   __shared__ float redf[NT / 64];
   __shared__ int redi[NT / 64];
   __shared__ int scanbuf[NT / 64];
@@ -390,10 +392,12 @@ hipError_t launch_scores_select(const Dims &d, const prism_config *cfg, float sc
     TraceScope tr(PRISM_STAGE_SELECT, s);
     if (small) {
       hipLaunchKernelGGL((select_kernel<256, 2>), dim3(sel_grid), dim3(256), 0, s, d.nb_max,
-                         d.words, nbp, scores, cfg->top_k, cfg->top_p, bits, cnt, cols);
+                         d.words, nbp, scores, cfg->top_k, cfg->top_k_frac, cfg->top_p, bits,
+                         cnt, cols);
     } else {
       hipLaunchKernelGGL((select_kernel<1024, 2>), dim3(sel_grid), dim3(1024), 0, s, d.nb_max,
-                         d.words, nbp, scores, cfg->top_k, cfg->top_p, bits, cnt, cols);
+                         d.words, nbp, scores, cfg->top_k, cfg->top_k_frac, cfg->top_p, bits,
+                         cnt, cols);
     }
     hipLaunchKernelGGL(transpose_bits_kernel, dim3(1024), dim3(256), 0, s, d.words, nbp, bits,
                        tbits);

@@ -69,6 +69,19 @@ typedef struct prism_config {
     double eps;           /* epsilon in g_d (pages give no value; default 1e-6) */
     float score_scale;    /* block-score logit scale; <= 0 selects 1/sqrt(D) */
     float softmax_scale;  /* attention logit scale; <= 0 selects 1/sqrt(D) */
+    /* Operating-point and ablation settings (digest, selection section and the sparsity,
+     * shape, density and mapping ablations).  All-zero values keep the method as above. */
+    float top_k_frac;     /* > 0: Top-k = ceil(top_k_frac * Nb) key blocks for each head
+                             (Nb = that head's block count), replacing top_k; the pages'
+                             "Top-k at 95% sparsity" is 0.05.  Range [0, 1] */
+    int fixed_shape;      /* > 0: every zone takes this packed shape (lT*16 + lH*4 + lW;
+                             each log2 edge in [min_edge_log2, 3], volume 64, 128 or 256)
+                             instead of the adaptive one: the fixed-shape baseline */
+    float map_exponent;   /* exponent a of the shape mapping b_d ~ g_d^-a (the Lagrange
+                             optimum of J is 1/2); <= 0 selects 1/2 */
+    int density_mode;     /* information density driving the volume tier: 0 spatial plus
+                             temporal terms of rho_raw (the method), 1 spatial term only,
+                             2 temporal term only, 3 the normalised A2V intensity a_bar */
 } prism_config;
 
 /* Offsets (bytes from the workspace base) and element types of the plan's arrays, for

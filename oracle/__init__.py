@@ -75,13 +75,13 @@ def _f64(x):
     return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
 
 
-def zone_stats(T, H, W, v):
+def zone_stats(T, H, W, v, density_mode=0):
     v = _f64(v)
     N, D = v.shape
     assert N == T * H * W
     Z = N // ZONE ** 3
     out = np.zeros((Z, 4))
-    rc = _load().orc_zone_stats(T, H, W, D, _dp(v), _dp(out))
+    rc = _load().orc_zone_stats(T, H, W, D, _dp(v), int(density_mode), _dp(out))
     if rc:
         raise ValueError("grid not divisible by the zone edge")
     return out
@@ -103,11 +103,13 @@ def shape_pool(S, min_edge_log2):
     return cand[:n].copy()
 
 
-def zone_plan(vstats, astats=None, tau128=0.5, tau256=0.25, eps=1e-6, min_edge_log2=1):
+def zone_plan(vstats, astats=None, tau128=0.5, tau256=0.25, eps=1e-6, min_edge_log2=1,
+              map_exponent=0.5, fixed_shape=0, density_mode=0):
     lib = _load()
     lib.orc_zone_plan.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_double, ctypes.c_double, ctypes.c_double,
-                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+                                  ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_void_p]
     vstats = np.ascontiguousarray(vstats, dtype=np.float64)
     Z = vstats.shape[0]
     shape = np.zeros(Z, dtype=np.int32)
@@ -117,6 +119,7 @@ def zone_plan(vstats, astats=None, tau128=0.5, tau256=0.25, eps=1e-6, min_edge_l
         astats = np.ascontiguousarray(astats, dtype=np.float64)
         ap = astats.ctypes.data
     rc = lib.orc_zone_plan(Z, vstats.ctypes.data, ap, tau128, tau256, eps, min_edge_log2,
+                           float(map_exponent), int(fixed_shape), int(density_mode),
                            shape.ctypes.data, diag.ctypes.data)
     if rc:
         raise ValueError("bad zone_plan arguments")
@@ -209,22 +212,32 @@ class HeadPlan:
         return [self.cols[i, :self.count[i]].copy() for i in range(self.nb)]
 
 
+def topk_of(nb, top_k, top_k_frac):
+    """Top-k of a head with nb blocks: ceil(frac * nb) when a fraction is given (the
+    fraction taken as the float32 the library receives), else the count."""
+    if top_k_frac and top_k_frac > 0:
+        return int(np.ceil(float(np.float32(top_k_frac)) * nb))
+    return int(top_k)
+
+
 def plan_head(T, H, W, q, k, v, a=None, top_k=8, top_p=0.9, tau128=0.5, tau256=0.25,
-              eps=1e-6, min_edge_log2=1, score_scale=None, astats=None):
+              eps=1e-6, min_edge_log2=1, score_scale=None, astats=None, top_k_frac=0.0,
+              map_exponent=0.5, fixed_shape=0, density_mode=0):
     """The full plan for one head: q, k, v are [N, D] for that head; a is [N] or None."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     D = q.shape[1]
     if score_scale is None:
         score_scale = 1.0 / np.sqrt(D)
-    vs = zone_stats(T, H, W, v)
+    vs = zone_stats(T, H, W, v, density_mode)
     if astats is None and a is not None:
         astats = audio_stats(T, H, W, a)
-    shape, zd = zone_plan(vs, astats, tau128, tau256, eps, min_edge_log2)
+    shape, zd = zone_plan(vs, astats, tau128, tau256, eps, min_edge_log2, map_exponent,
+                          fixed_shape, density_mode)
     perm, inv, bstart, bsize, bof = permutation(T, H, W, shape)
     qbar = block_means(q, perm, bstart, bsize)
     kbar = block_means(k, perm, bstart, bsize)
     s, P = block_probs(qbar, kbar, score_scale)
-    count, cols, sd = select(P, top_k, top_p)
+    count, cols, sd = select(P, topk_of(len(bsize), top_k, top_k_frac), top_p)
     return HeadPlan(shape, zd, vs, perm, inv, bstart, bsize, bof, qbar, kbar, s, P, count,
                     cols, sd)
 

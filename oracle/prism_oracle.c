@@ -47,8 +47,10 @@ static int idx_token(int H, int W, int t, int h, int w) { return (t * H + h) * W
  * Zone statistics of V for one head ([review] item 1, sigma^2_{v,d};
  * [digest] density section, Eq. rho_raw).
  * v: [N][D] float64.  out: [Z][4] = sigma2_T, sigma2_H, sigma2_W, rho_raw.
+ * dmode selects the terms of rho_raw for the density ablation ([digest] ablation
+ * section: spatial only or temporal only): 1 spatial, 2 temporal, otherwise both.
  * ---------------------------------------------------------------------------------- */
-int orc_zone_stats(int T, int H, int W, int D, const double *v, double *out)
+int orc_zone_stats(int T, int H, int W, int D, const double *v, int dmode, double *out)
 {
     if (T % ZE || H % ZE || W % ZE || D <= 0) return -1;
     int nzt = T / ZE, nzh = H / ZE, nzw = W / ZE;
@@ -107,7 +109,7 @@ int orc_zone_stats(int T, int H, int W, int D, const double *v, double *out)
                 out[4 * m + 0] = s2[0] / D;
                 out[4 * m + 1] = s2[1] / D;
                 out[4 * m + 2] = s2[2] / D;
-                out[4 * m + 3] = spatial / D + temporal / D;
+                out[4 * m + 3] = (dmode == 2 ? 0.0 : spatial / D) + (dmode == 1 ? 0.0 : temporal / D);
             }
     free(pt);
     free(ph);
@@ -186,11 +188,22 @@ int orc_shape_pool(int S, int min_edge_log2, int *cand /* [..][3] log2 edges */)
  *   (first layer: no cached A2V norm, video guidance only).
  *   shape_out [Z]: packed log2 edges.  diag [Z][12] (optional): rho, abar, g_T, g_H, g_W,
  *   l*_T, l*_H, l*_W, B, tier margin, shape margin, best distance.
+ * Ablation settings ([digest] ablation section): alpha is the exponent of the mapping
+ * b_d ~ g_d^-alpha (the Lagrange optimum of J gives 1/2); fixed > 0 gives every zone that
+ * packed shape (the fixed-shape baseline; no shape decision, margin reported as 1e300);
+ * dmode 3 takes the volume tier from the normalised A2V intensity a_bar instead of rho.
  * ---------------------------------------------------------------------------------- */
 int orc_zone_plan(int Z, const double *vstats, const double *astats, double tau128,
-                  double tau256, double eps, int min_edge_log2, int *shape_out, double *diag)
+                  double tau256, double eps, int min_edge_log2, double alpha, int fixed,
+                  int dmode, int *shape_out, double *diag)
 {
     if (Z <= 0 || min_edge_log2 < 0 || min_edge_log2 > 2) return -1;
+    if (fixed > 0) {
+        int fa = (fixed >> 4) & 3, fb = (fixed >> 2) & 3, fc = fixed & 3, fs = fa + fb + fc;
+        if (fixed > 63 || fa < min_edge_log2 || fb < min_edge_log2 || fc < min_edge_log2 ||
+            fs < 6 || fs > 8)
+            return -1;
+    }
     double rho_max = 0, a_max = 0;
     for (int m = 0; m < Z; ++m) {
         if (vstats[4 * m + 3] > rho_max) rho_max = vstats[4 * m + 3];
@@ -210,6 +223,7 @@ int orc_zone_plan(int Z, const double *vstats, const double *astats, double tau1
             double asum = as[1] + as[2] + as[3];
             for (int d = 0; d < 3; ++d) va[d] = asum > 0 ? as[1 + d] / asum : 0.0;
         }
+        if (dmode == 3) rho = abar;
         double g[3];
         for (int d = 0; d < 3; ++d) g[d] = r[d] + abar * va[d] + eps;
 
@@ -222,9 +236,18 @@ int orc_zone_plan(int Z, const double *vstats, const double *astats, double tau1
         for (int d = 0; d < 3; ++d) lg[d] = log2(g[d]);
         double lstar[3];
         for (int d = 0; d < 3; ++d)
-            lstar[d] = -0.5 * lg[d] + (S + 0.5 * lg[0] + 0.5 * lg[1] + 0.5 * lg[2]) / 3.0;
+            lstar[d] = -alpha * lg[d] + (S + alpha * lg[0] + alpha * lg[1] + alpha * lg[2]) / 3.0;
 
-        int nc = orc_shape_pool(S, min_edge_log2, cand);
+        int nc;
+        if (fixed > 0) {
+            S = ((fixed >> 4) & 3) + ((fixed >> 2) & 3) + (fixed & 3);
+            cand[0] = (fixed >> 4) & 3;
+            cand[1] = (fixed >> 2) & 3;
+            cand[2] = fixed & 3;
+            nc = 1;
+        } else {
+            nc = orc_shape_pool(S, min_edge_log2, cand);
+        }
         double dist[64], best = INFINITY;
         for (int c = 0; c < nc; ++c) {
             double e0 = lstar[0] - cand[3 * c + 0];
@@ -256,7 +279,7 @@ int orc_zone_plan(int Z, const double *vstats, const double *astats, double tau1
             o[8] = (double)(1 << S);
             double tm = fabs(rho - tau128), tm2 = fabs(rho - tau256);
             o[9] = tm < tm2 ? tm : tm2;
-            o[10] = second - best;
+            o[10] = fixed > 0 ? 1e300 : second - best;
             o[11] = best;
         }
     }

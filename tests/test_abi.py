@@ -46,11 +46,17 @@ def test_layout_and_workspace(lib):
     (dict(T=12), -2), (dict(H=0), -1), (dict(head_dim=96), -2), (dict(dtype=7), -2),
     (dict(min_edge_log2=2), -1), (dict(top_k=-1), -1), (dict(top_p=float("nan")), -1),
     (dict(T=4096, H=1024, W=1024), -2),
+    (dict(top_k_frac=1.5), -1), (dict(top_k_frac=-0.1), -1), (dict(density_mode=4), -1),
+    (dict(map_exponent=float("inf")), -1),
+    (dict(fixed_shape=(1 << 4) | (1 << 2) | 1), -1),     # 2x2x2: 8 tokens
+    (dict(fixed_shape=(3 << 4) | (3 << 2) | 3), -1),     # 8x8x8: 512 tokens
+    (dict(fixed_shape=(0 << 4) | (3 << 2) | 3), -1),     # edge 1 with min_edge_log2 = 1
 ])
 def test_rejected_configs(lib, over, code):
     base = dict(T=8, H=16, W=16, num_heads=2, head_dim=128, dtype=P.BF16, min_edge_log2=1,
                 top_k=8, top_p=0.9, tau128=0.5, tau256=0.25, eps=1e-6, score_scale=0.0,
-                softmax_scale=0.0)
+                softmax_scale=0.0, top_k_frac=0.0, fixed_shape=0, map_exponent=0.0,
+                density_mode=0)
     base.update(over)
     cfg = P.PrismConfig(**base)
     assert lib.prism_workspace_bytes(ctypes.byref(cfg)) == 0
@@ -74,3 +80,11 @@ def test_null_and_small_workspace(lib):
     assert lib.prism_attn_bwd(ctypes.byref(cfg), d, need, d, d, None, d, None) == -1
     assert lib.prism_attn_bwd(ctypes.byref(cfg), d, need - 1, d, d, d, d, None) == -3
     assert lib.prism_status_string(-3) == b"workspace too small"
+
+
+def test_accepted_ablation_configs(lib):
+    for over in (dict(top_k_frac=0.05, top_p=0.2), dict(fixed_shape=P.shape_code(4, 8, 8)),
+                 dict(fixed_shape=P.shape_code(4, 4, 4)), dict(map_exponent=1.0),
+                 dict(density_mode=3)):
+        cfg = P.make_config(8, 16, 16, 2, 128, "bf16", **over)
+        assert lib.prism_workspace_bytes(ctypes.byref(cfg)) > 0, over

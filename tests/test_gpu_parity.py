@@ -169,3 +169,34 @@ def test_deterministic_rerun():
             what = names[i] if i < len(names) else f"selection list {i - len(names)}"
             raise AssertionError(f"{what} differs between runs at {bad.shape[0]} places "
                                  f"(first {bad[:4].tolist()}), max difference {d:.3e}")
+
+
+# The pages' operating point and sparsity policies, the fixed-shape baseline and the mapping
+# and density ablation settings: plan, selection and forward against the oracle.
+SETTINGS = [
+    ("pages", P.POLICIES["pages"]),
+    ("topk85", P.POLICIES["topk85"]),
+    ("topp0.3", P.POLICIES["topp0.3"]),
+    ("fixed-4x8x8", dict(fixed_shape=P.shape_code(4, 8, 8))),
+    ("fixed-4x4x4", dict(fixed_shape=P.shape_code(4, 4, 4))),
+    ("map-1.0", dict(map_exponent=1.0)),
+    ("map-0.3", dict(map_exponent=0.3)),
+    ("density-spatial", dict(density_mode=1)),
+    ("density-temporal", dict(density_mode=2)),
+    ("density-audio", dict(density_mode=3)),
+]
+
+
+@pytest.mark.parametrize("name,over", SETTINGS, ids=[s[0] for s in SETTINGS])
+def test_bf16_settings(name, over):
+    wl = synth.custom(8, 24, 40, 2, 128, "bf16", seed=11)
+    inp_cpu, inp = _inputs(wl)
+    cfg = P.config_for(wl, **over)
+    att = run_plan(cfg, inp)
+    o, lse = att.forward()
+    torch.cuda.synchronize()
+    oover = dict(over)
+    if "map_exponent" in oover:  # the library receives a float32
+        oover["map_exponent"] = float(np.float32(oover["map_exponent"]))
+    for h in range(wl.heads):
+        _check_head(wl, cfg, att, inp_cpu, h, o, lse, **oover)

@@ -399,3 +399,102 @@ def test_attn_bwd_rows_subset():
     # sum over keys of dV equals the sum of dO; dK sums to zero
     np.testing.assert_allclose(full[2].sum(0), do.sum(0), atol=1e-10)
     np.testing.assert_allclose(full[1].sum(0), 0, atol=1e-10)
+
+
+# ----------------------------------------------------------------------------- ablation settings
+
+def test_density_terms_separable():
+    """Density ablation: mode 1 keeps Var(g) + Var(u) (spatial spread at a fixed time),
+    mode 2 the mean squared frame step of f, mode 0 their sum (same separable field as
+    test_zone_stats_separable, closed forms from numpy)."""
+    T, H, W, D = 8, 8, 8, 3
+    f = rng0.normal(size=(T, D))
+    g = rng0.normal(size=(H, D))
+    u = rng0.normal(size=(W, D))
+    t, h, w = coords(T, H, W)
+    v = f[t] + g[h] + u[w]
+    spatial = np.mean(np.var(g, axis=0)) + np.mean(np.var(u, axis=0))
+    temporal = np.mean(np.sum(np.diff(f, axis=0) ** 2, axis=0) / 7.0)
+    for mode, exp in ((0, spatial + temporal), (1, spatial), (2, temporal)):
+        st = oracle.zone_stats(T, H, W, v, density_mode=mode)
+        assert st[0, 3] == pytest.approx(exp, rel=1e-12)
+        # the directional variances do not depend on the density terms
+        np.testing.assert_allclose(st[0, :3], oracle.zone_stats(T, H, W, v)[0, :3], rtol=0)
+
+
+def test_density_from_audio_intensity():
+    """Density mode 3: the tier follows the zone-mean A2V intensity normalised by its maximum
+    (1.0 -> 64, 0.4 -> 128, 0.1 -> 256 with the pages' thresholds 0.5 and 0.25), whatever
+    rho_raw says."""
+    vs = np.array([[1.0, 1.0, 1.0, 0.0], [1.0, 1.0, 1.0, 5.0], [1.0, 1.0, 1.0, 1.0]])
+    ast = np.array([[2.0, 0, 0, 0], [0.8, 0, 0, 0], [0.2, 0, 0, 0]])
+    shape, diag = oracle.zone_plan(vs, ast, density_mode=3)
+    assert list(diag[:, 8]) == [64.0, 128.0, 256.0]
+    np.testing.assert_allclose(diag[:, 0], [1.0, 0.4, 0.1], rtol=1e-15)
+
+
+@pytest.mark.parametrize("alpha", [0.25, 0.5, 1.0, 2.0])
+def test_mapping_exponent(alpha):
+    """Mapping ablation b_d ~ g_d^-alpha: sum_d l*_d = S for every alpha, and
+    l*_d - l*_d' = -alpha log2(g_d / g_d')."""
+    vs = np.array([[0.6, 0.3, 0.1, 0.2]])   # shares r = (0.6, 0.3, 0.1), rho = 1 -> B = 64
+    shape, diag = oracle.zone_plan(vs, None, eps=0.0, map_exponent=alpha)
+    ls = diag[0, 5:8]
+    assert ls.sum() == pytest.approx(6.0, abs=1e-12)
+    assert ls[0] - ls[1] == pytest.approx(-alpha * math.log2(0.6 / 0.3), abs=1e-12)
+    assert ls[1] - ls[2] == pytest.approx(-alpha * math.log2(0.3 / 0.1), abs=1e-12)
+
+
+def test_mapping_exponent_extremes():
+    """A vanishing exponent maps every zone to the isotropic optimum S/3 per axis, so a
+    64-token block is 4 x 4 x 4; a large one drives the fast axis to the shortest edge."""
+    vs = np.array([[0.9, 0.05, 0.05, 1.0]])
+    shape, diag = oracle.zone_plan(vs, None, eps=0.0, map_exponent=1e-9)
+    assert list(oracle.unpack_shape(shape)[0]) == [2, 2, 2]
+    shape, _ = oracle.zone_plan(vs, None, eps=0.0, map_exponent=4.0)
+    assert oracle.unpack_shape(shape)[0][0] == 1          # T edge 2, the pool's minimum
+
+
+@pytest.mark.parametrize("edges", [(4, 8, 8), (4, 4, 4), (2, 8, 8), (8, 4, 4)])
+def test_fixed_shape(edges):
+    """Fixed-shape baseline: every zone takes the given shape; the permutation is then the
+    regular tiling of each zone into bT x bH x bW boxes."""
+    T, H, W = 16, 16, 8
+    code = (int(math.log2(edges[0])) << 4) | (int(math.log2(edges[1])) << 2) | int(
+        math.log2(edges[2]))
+    v = rng0.normal(size=(T * H * W, 4))
+    vs = oracle.zone_stats(T, H, W, v)
+    shape, diag = oracle.zone_plan(vs, None, fixed_shape=code)
+    assert np.all(shape == code)
+    assert np.all(diag[:, 10] == 1e300)
+    perm, inv, bstart, bsize, bof = oracle.permutation(T, H, W, shape)
+    B = edges[0] * edges[1] * edges[2]
+    assert np.all(bsize == B) and len(bsize) == T * H * W // B
+    t, h, w = coords(T, H, W)
+    for b in range(len(bsize)):
+        toks = perm[bstart[b]:bstart[b] + B]
+        for ax, e in zip((t, h, w), edges):
+            c = ax[toks]
+            assert c.max() - c.min() == e - 1 and c.min() % e == 0
+
+
+def test_fixed_shape_rejects_bad_codes():
+    vs = np.ones((1, 4))
+    for bad in ((1 << 4) | (1 << 2) | 1, (3 << 4) | (3 << 2) | 3):   # 8 tokens; 512 tokens
+        with pytest.raises(ValueError):
+            oracle.zone_plan(vs, None, fixed_shape=bad)
+
+
+@pytest.mark.parametrize("frac", [0.05, 0.15, 0.25])
+def test_topk_as_fraction(frac):
+    """Top-k as a sparsity: with p = 0 every row keeps exactly ceil(frac * Nb) blocks, the
+    ones a brute-force sort ranks first (relevance descending, index ascending)."""
+    nb = 57
+    P = rng0.dirichlet(np.ones(nb), size=nb)
+    k = oracle.topk_of(nb, 0, frac)
+    assert k == math.ceil(np.float32(frac) * nb)
+    count, cols, _ = oracle.select(P, k, 0.0)
+    for i in range(nb):
+        order = sorted(range(nb), key=lambda j: (-P[i, j], j))
+        assert count[i] == k
+        assert sorted(cols[i, :k]) == sorted(order[:k])
