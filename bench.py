@@ -69,6 +69,8 @@ def parse():
                     "3: 2K fwd, 4: 2K fwd+bwd (default)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense comparators")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-a2v-norm", action="store_true",
+                    help="skip timing the A2V norm producer")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
@@ -312,6 +314,28 @@ def main():
         roofline["traffic_note"] = ("HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                     "scaled by a 1 GiB copy)")
 
+    # the A2V norm producer (the field the next layer's plan reads) on a synthetic
+    # cross-attention output of hidden width heads x D: an HBM-bound row reduction
+    a2v_norm = None
+    if not args.no_a2v_norm:
+        x = synth.a2v_output(inp["a2v"], Hh * D, "bf16" if wl.dtype == "bf16" else "f32")
+        out = P.a2v_norm(x)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(5):
+            P.a2v_norm(x, out=out)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms_n = ev0.elapsed_time(ev1) / 5
+        nbytes = x.numel() * x.element_size() + 4 * N
+        a2v_norm = {"ms": round(ms_n, 4), "bytes": nbytes,
+                    "GB/s": round(nbytes / (ms_n * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(nbytes / (ms_n * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "shape": [N, Hh * D]}
+        del x, out
+        torch.cuda.empty_cache()
+
     # dense comparators on a subset of heads, scaled by the head count
     dense = {}
     if not args.no_dense:
@@ -369,6 +393,7 @@ def main():
         "zones_B64_B128_B256": [int((vol == 64).sum()), int((vol == 128).sum()),
                                 int((vol == 256).sum())],
         "dense": dense,
+        "a2v_norm": a2v_norm,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -63,8 +63,8 @@ class PrismError(RuntimeError):
 
 _lib = None
 EXPORTS = ["prism_workspace_bytes", "prism_plan_layout", "prism_plan", "prism_attn_fwd",
-           "prism_attn_bwd", "prism_status_string", "prism_last_error", "prism_trace_enable",
-           "prism_trace_read", "prism_stage_name"]
+           "prism_attn_bwd", "prism_a2v_norm", "prism_status_string", "prism_last_error",
+           "prism_trace_enable", "prism_trace_read", "prism_stage_name"]
 STAGES = ["audio_stats", "zone_stats", "quantize", "gather", "tiles", "scores", "select",
           "attn_fwd", "bwd_prep", "bwd_dkdv", "bwd_dq"]
 
@@ -88,6 +88,9 @@ def lib():
         L.prism_attn_fwd.restype = ctypes.c_int
         L.prism_attn_bwd.argtypes = [cfgp, vp, ctypes.c_size_t, vp, vp, vp, vp, vp]
         L.prism_attn_bwd.restype = ctypes.c_int
+        L.prism_a2v_norm.argtypes = [vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
+                                     ctypes.c_int, vp, vp]
+        L.prism_a2v_norm.restype = ctypes.c_int
         L.prism_status_string.argtypes = [ctypes.c_int]
         L.prism_status_string.restype = ctypes.c_char_p
         L.prism_last_error.argtypes = []
@@ -209,6 +212,24 @@ def attn_bwd(cfg, ws, dout, dq, dk, dv, stream=None):
     _check(lib().prism_attn_bwd(ctypes.byref(cfg), _ptr(ws), ws.numel() * ws.element_size(),
                                 _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)),
            "prism_attn_bwd")
+
+
+def a2v_norm(x, out=None, stream=None):
+    """The A2V norm field of an audio-to-video cross-attention output x [N, C] (float32 or
+    bfloat16, rows 16-byte aligned): out[n] = ||x[n, :]||_2 as float32 [N]."""
+    if x.dim() != 2 or x.dtype not in (torch.float32, torch.bfloat16) or not x.is_cuda:
+        raise ValueError("x: expected a CUDA float32 or bfloat16 [N, C] tensor")
+    if x.stride(1) != 1:
+        raise ValueError("x: rows must be contiguous")
+    n = x.shape[0]
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=x.device)
+    if out.shape != (n,) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out: expected float32 [N]")
+    dt = BF16 if x.dtype == torch.bfloat16 else F32
+    _check(lib().prism_a2v_norm(_ptr(x), n, x.shape[1], x.stride(0), dt, _ptr(out),
+                                _stream(stream)), "prism_a2v_norm")
+    return out
 
 
 def trace_enable(on: bool = True):

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libprism.so")
 SOURCES = ["plan_kernels.hip", "select_kernels.hip", "attn_fwd.hip", "attn_bwd.hip",
-           "attn_bwd_dkdv.hip", "prism_api.hip"]
+           "attn_bwd_dkdv.hip", "a2v_norm.hip", "prism_api.hip"]
 # The attention kernels never see NaN inputs; without IEEE-mode NaN quieting the compiler
 # can feed MFMA results straight into v_max instead of canonicalising each one first.
 # The forward and dQ kernels also keep their MFMA accumulators in ordinary VGPRs (no

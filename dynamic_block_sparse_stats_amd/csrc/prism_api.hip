@@ -347,4 +347,21 @@ const char *prism_stage_name(int stage) {
   return stage >= 0 && stage < PRISM_STAGE_COUNT ? names[stage] : "unknown";
 }
 
+prism_status prism_a2v_norm(const void *x, int64_t n_tokens, int channels, int64_t ld,
+                            int dtype, float *a2v_norm, void *stream) {
+  if (!x || !a2v_norm) return fail(PRISM_ERR_ARG, "null tensor");
+  if (n_tokens <= 0 || channels <= 0 || ld < channels)
+    return fail(PRISM_ERR_ARG, "n_tokens and channels must be positive, ld >= channels");
+  if (dtype != PRISM_F32 && dtype != PRISM_BF16)
+    return fail(PRISM_ERR_UNSUPPORTED, "dtype must be PRISM_F32 or PRISM_BF16");
+  const int vpc = dtype == PRISM_BF16 ? 8 : 4;
+  if (ld % vpc || ((uintptr_t)x) % 16)
+    return fail(PRISM_ERR_ARG, "rows must start on 16-byte boundaries (x aligned, ld * size "
+                               "a multiple of 16)");
+  if ((n_tokens + 3) / 4 > 0x7fffffffLL) return fail(PRISM_ERR_UNSUPPORTED, "too many tokens");
+  return launched(prism::launch_a2v_norm(x, n_tokens, channels, ld, dtype, a2v_norm,
+                                         (hipStream_t)stream),
+                  "a2v norm");
+}
+
 }  // extern "C"

@@ -101,6 +101,10 @@ hipError_t launch_dkdv_bf16(int work_items, hipStream_t s, int N, int U, int nb_
                             const int *trows, const int *perm, float scale, float sl2e,
                             uint16_t *dk, uint16_t *dv);
 
+// a2v_norm.hip
+hipError_t launch_a2v_norm(const void *x, long long n_tokens, int channels, long long ld,
+                           int dtype, float *out, hipStream_t s);
+
 // Workgroups of `kernel` (block size `block`) that fit on the current device at once: the
 // grid of the persistent attention kernels.
 int resident_grid(const void *kernel, int block, int work_items);

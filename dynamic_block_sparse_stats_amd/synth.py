@@ -216,3 +216,20 @@ def make_inputs(wl: Workload, device="cpu", with_dout: bool | None = None, seed_
         gdo.manual_seed(int(c_do.generate_state(1)[0]))
         out["dout"] = torch.randn(N, Hh, D, generator=gdo, device=dev).to(tdt)
     return out
+
+
+def a2v_output(a2v, channels: int, dtype: str = "bf16", seed: int = 0):
+    """A synthetic audio-to-video cross-attention output [N, channels] whose rows are seeded
+    random directions scaled by the A2V intensity field a2v [N]: each row has length a2v[n]
+    (up to the rounding of the stored dtype).  Stands in for the previous layer's output,
+    which needs the model; the norm producer reads it back into an A2V field."""
+    dev = a2v.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(BASE_SEED + 31 * seed + 17)
+    out = torch.empty(a2v.shape[0], channels, dtype=_torch_dtype(dtype), device=dev)
+    step = max(1, (1 << 28) // max(channels, 1))
+    for i0 in range(0, a2v.shape[0], step):
+        u = torch.randn(min(step, a2v.shape[0] - i0), channels, generator=g, device=dev)
+        u = u / u.norm(dim=1, keepdim=True).clamp_min(1e-30)
+        out[i0:i0 + u.shape[0]] = (u * a2v[i0:i0 + u.shape[0], None]).to(out.dtype)
+    return out

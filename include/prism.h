@@ -132,6 +132,17 @@ prism_status prism_plan(const prism_config *cfg, const void *q, const void *k, c
 prism_status prism_attn_fwd(const prism_config *cfg, void *workspace, size_t workspace_bytes,
                             void *o, float *lse, void *stream);
 
+/* The A2V norm field a later layer's prism_plan consumes (digest, guidance section: the
+ * audio injection strength of a video position is the vector length of its output of the
+ * audio-to-video cross-attention, cached from the previous layer):
+ *   a2v_norm[n] = sqrt(sum_c x[n][c]^2), c < channels,
+ * x: n_tokens rows of `channels` values in dtype (prism_dtype), row n starting at element
+ * n * ld (ld >= channels; x 16-byte aligned and ld * element size a multiple of 16);
+ * a2v_norm: [n_tokens] float32 (overwritten).  Sums in float64.  PRISM_ERR_ARG on null
+ * pointers or bad sizes, PRISM_ERR_UNSUPPORTED on an unknown dtype. */
+prism_status prism_a2v_norm(const void *x, int64_t n_tokens, int channels, int64_t ld,
+                            int dtype, float *a2v_norm, void *stream);
+
 /* Sparse attention backward with the plan held constant (digest, training section): given
  * dout [N][heads][D], writes dq, dk, dv [N][heads][D] (overwritten, token order).  Reads
  * the float32 copy of the output and the lse that prism_attn_fwd left in workspace, so

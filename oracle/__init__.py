@@ -19,6 +19,7 @@ Parity status of each function (what pins it; see tests/test_oracle_pins.py):
   attn_fwd                 -- Top-k = all equals textbook dense attention; any plan equals
                               dense attention under the plan's block mask
   attn_bwd                 -- central finite differences of attn_fwd
+  row_norms                -- closed forms (unit vectors, constant rows, Pythagorean rows)
 """
 from __future__ import annotations
 
@@ -286,3 +287,17 @@ def attn_bwd(plan: HeadPlan, q, k, v, dout, scale=None, rows=None):
                      0 if rws is None else len(rws), dq.ctypes.data, dk.ctypes.data,
                      dv.ctypes.data)
     return dq, dk, dv
+
+
+def row_norms(x, rows=None):
+    """The A2V norm field sqrt(sum_c x[n, c]^2) of rows `rows` (default: all) of x [N, C]."""
+    x = _f64(x)
+    N, C = x.shape
+    rows = np.arange(N, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.zeros(len(rows))
+    lib = _load()
+    lib.orc_row_norms.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p]
+    if lib.orc_row_norms(C, x.ctypes.data, rows.ctypes.data, len(rows), out.ctypes.data):
+        raise ValueError("bad row_norms arguments")
+    return out

@@ -542,3 +542,20 @@ int orc_attn_bwd(int N, int D, const double *q, const double *k, const double *v
     free(o);
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------
+ * The A2V norm field ([digest] guidance section: the audio injection strength of a video
+ * position is the vector length of its audio-to-video cross-attention output):
+ *   out[i] = sqrt(sum_c x[rows[i]][c]^2), x: [N][C] float64, rows: the n row indices.
+ * ---------------------------------------------------------------------------------- */
+int orc_row_norms(int C, const double *x, const int64_t *rows, int n, double *out)
+{
+    if (C <= 0 || n < 0) return -1;
+    for (int i = 0; i < n; ++i) {
+        const double *r = x + (size_t)rows[i] * C;
+        double s = 0;
+        for (int c = 0; c < C; ++c) s += r[c] * r[c];
+        out[i] = sqrt(s);
+    }
+    return 0;
+}

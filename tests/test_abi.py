@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     src = open(os.path.join(ROOT, "include", "prism.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(prism_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(prism_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -88,3 +88,13 @@ def test_accepted_ablation_configs(lib):
                  dict(density_mode=3)):
         cfg = P.make_config(8, 16, 16, 2, 128, "bf16", **over)
         assert lib.prism_workspace_bytes(ctypes.byref(cfg)) > 0, over
+
+
+def test_a2v_norm_rejects_bad_arguments(lib):
+    d = ctypes.c_void_p(256)
+    assert lib.prism_a2v_norm(None, 10, 8, 8, P.BF16, d, None) == -1
+    assert lib.prism_a2v_norm(d, 0, 8, 8, P.BF16, d, None) == -1
+    assert lib.prism_a2v_norm(d, 10, 8, 4, P.BF16, d, None) == -1      # ld < channels
+    assert lib.prism_a2v_norm(d, 10, 8, 12, P.BF16, d, None) == -1     # rows not 16-B aligned
+    assert lib.prism_a2v_norm(ctypes.c_void_p(8), 10, 8, 8, P.BF16, d, None) == -1
+    assert lib.prism_a2v_norm(d, 10, 8, 8, 5, d, None) == -2

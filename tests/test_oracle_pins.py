@@ -498,3 +498,18 @@ def test_topk_as_fraction(frac):
         order = sorted(range(nb), key=lambda j: (-P[i, j], j))
         assert count[i] == k
         assert sorted(cols[i, :k]) == sorted(order[:k])
+
+
+# ----------------------------------------------------------------------------- A2V norm field
+
+def test_row_norms_closed_forms():
+    C = 12
+    x = np.zeros((4, C))
+    x[0, 5] = -2.5                       # one nonzero entry: its magnitude
+    x[1, :] = 3.0                        # constant row: |c| sqrt(C)
+    x[2, 0], x[2, 7] = 3.0, 4.0          # Pythagorean pair
+    u = rng0.normal(size=C)
+    x[3] = 7.0 * u / np.sqrt(np.sum(u * u))  # scaled unit vector
+    np.testing.assert_allclose(oracle.row_norms(x), [2.5, 3.0 * math.sqrt(C), 5.0, 7.0],
+                               rtol=1e-14)
+    np.testing.assert_allclose(oracle.row_norms(x, rows=[2, 0]), [5.0, 2.5], rtol=1e-14)
