@@ -11,9 +11,13 @@
 //     query rows in registers as the B operand; one workgroup per CU, persistent over the
 //     list of blocks;
 //   * the key units of the block's selected key blocks stream through a four-stage LDS
-//     ring (128 KB) filled by direct global->LDS copies, three units ahead of the one being
-//     computed: K and V as [64 keys][128] float16, XOR-swizzled by 16-byte chunk; K rows
-//     are read directly, V^T with transposing LDS reads (ds_read_b64_tr_b16);
+//     ring (128 KB) filled by direct global->LDS copies, two units ahead of the one being
+//     computed (the fourth stage is still being read by the late waves, below): K and V as
+//     [64 keys][128] float16, XOR-swizzled by 16-byte chunk; K rows are read directly, V^T
+//     with transposing LDS reads (ds_read_b64_tr_b16);
+//   * the two waves of a SIMD run half a unit apart (the late one finishes the previous
+//     unit's PV product while the early one forms its scores), and each wave reads the
+//     operands of its next group of MFMAs while the current group runs;
 //   * the softmax weights go to the PV product as float16 scaled by 2^10 (11-bit
 //     significands where bf16 has 8: at 2K, value rows reach |v| ~ 20 and the PV sums
 //     cancel, so bf16 weights cost ~3e-2 absolute); the row sum adds the same float16
@@ -33,7 +37,7 @@ namespace prism {
 constexpr int kD = 128;
 
 constexpr int NW = 8;      // waves per workgroup: 8 x 32 = 256 query rows, one block
-constexpr int kStages = 4;  // LDS ring depth (units in flight: 3 ahead of the one computed)
+constexpr int kStages = 4;  // LDS ring depth (copies run 2 units ahead of the one computed)
 constexpr int kCpw = 32 / NW;  // 1 KB copies per wave per unit (16 for K, 16 for V)
 
 // Four LDS stages of 32 KB (distinct objects, named statically by the unrolled unit loop)
@@ -43,10 +47,10 @@ struct FwdStage {
   uint8_t k[16384];  // [64 keys][128] float16, swizzled
   uint8_t v[16384];  // [64 keys][128] float16, swizzled (read transposed)
 };
-__shared__ __align__(16) FwdStage g_fwd0;
-__shared__ __align__(16) FwdStage g_fwd1;
-__shared__ __align__(16) FwdStage g_fwd2;
-__shared__ __align__(16) FwdStage g_fwd3;
+__shared__ __align__(256) FwdStage g_fwd0;
+__shared__ __align__(256) FwdStage g_fwd1;
+__shared__ __align__(256) FwdStage g_fwd2;
+__shared__ __align__(256) FwdStage g_fwd3;
 template <int S>
 __device__ __forceinline__ FwdStage &fwd_stage() {
   return S == 0 ? g_fwd0 : (S == 1 ? g_fwd1 : (S == 2 ? g_fwd2 : g_fwd3));
@@ -54,28 +58,39 @@ __device__ __forceinline__ FwdStage &fwd_stage() {
 struct FwdState {
   f16x8 qreg[8];
   f32x16 o[4];
+  f16x8 pb[4];  // the current unit's softmax weights, float16 (B operand of the PV product)
   float m, mk;
   double lsum;
 };
 
-__device__ __forceinline__ void fwd_unit_on(FwdState &w, const uint8_t *__restrict__ Kt,
-                                            const uint8_t *__restrict__ Vt, int lane,
-                                            float scale_log2e) {
+// S^T = K Q^T for the unit, the online-softmax update (which rescales O) and the unit's
+// float16 weights; kt is the LDS address of the unit's K tile
+__device__ __forceinline__ void fwd_scores(FwdState &w, uint32_t kt, int lane,
+                                           float scale_log2e) {
   const int l32 = lane & 31, hh = lane >> 5;
-  // S^T for keys 0-31 (a = 0) and 32-63 (a = 1): lane = query l32, 16 keys per tile
-  f32x16 s[2];
+  // chunk 2kk + hh of key row l32 (a = 0) at kr ^ (kk << 5), of row 32 + l32 8 KB further
+  const uint32_t kr = row_base(kt, l32) ^ (uint32_t)(hh << 4);
+  // S^T for keys 0-31 (a = 0) and 32-63 (a = 1): lane = query l32, 16 keys per tile.  The
+  // operands of the next group of four MFMAs are read while the current group runs.
+  f32x16 s[2] = {f32x16{}, f32x16{}};
+  f16x8 ka[2][2][2];  // [buffer][a][e]
+  auto load = [&](int buf, int grp) {
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int r = 32 * a + l32;
-    f16x8 ka[8];
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      ka[kk] = __builtin_bit_cast(
-          f16x8, *reinterpret_cast<const u32x4 *>(Kt + rm_swz(r, 2 * kk + hh)));
+      for (int e = 0; e < 2; ++e)
+        ka[buf][a][e] = lds_row16((kr ^ (uint32_t)((2 * grp + e) << 5)) + 8192u * a);
+  };
+  load(0, 0);
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) {
+    if (grp < 3) load((grp + 1) & 1, grp + 1);
     __builtin_amdgcn_sched_barrier(0);
-    s[a] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) s[a] = mfma_f16(ka[kk], w.qreg[kk], s[a]);
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) s[a] = mfma_f16(ka[grp & 1][a][e], w.qreg[2 * grp + e], s[a]);
+    __builtin_amdgcn_sched_barrier(0);
   }
   // online softmax (log2 domain) with lazy rescaling: the running max only moves when a
   // query's new maximum exceeds it by more than 2^kLazy, so the float16 weights
@@ -105,6 +120,7 @@ __device__ __forceinline__ void fwd_unit_on(FwdState &w, const uint8_t *__restri
   }
   // the row sum adds the float16 weights the MFMA consumes (two per dot2 instruction), so
   // the normaliser matches the weights exactly
+  // (built in a fresh variable: the previous unit's weights are dead from here on)
   float psum = 0.f;
   f16x8 pb[4];
 #pragma unroll
@@ -118,60 +134,67 @@ __device__ __forceinline__ void fwd_unit_on(FwdState &w, const uint8_t *__restri
       psum = __builtin_amdgcn_fdot2(f16x2{pb[g][e], pb[g][e + 1]}, f16x2{1, 1}, psum, false);
   }
   w.lsum += (double)psum;
-  // O^T[d][q] += V^T[d][keys] P^T[keys][q], V^T read transposed from the row-major tile
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    f16x8 va[4];
+  for (int g = 0; g < 4; ++g) w.pb[g] = pb[g];
+}
+
+// O^T[d][q] += V^T[d][keys] P^T[keys][q] with the weights of the last fwd_scores, V^T read
+// transposed from the row-major tile at LDS address vt; per 16-key slice the four d-tiles'
+// accumulators are independent
+__device__ __forceinline__ void fwd_values(FwdState &w, uint32_t vt, int lane) {
+  const TrBase vb = tr_base(vt, lane);
+  f16x8 va[2][4];  // [buffer][dt]: the next slice's operands are read while one runs
 #pragma unroll
-    for (int g = 0; g < 4; ++g) va[g] = tr_operand(Vt, 16 * g, 32 * dt, lane);
+  for (int dt = 0; dt < 4; ++dt) va[0][dt] = tr_read(vb, 0, 32 * dt);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    if (g < 3)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) va[(g + 1) & 1][dt] = tr_read(vb, 16 * (g + 1), 32 * dt);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) w.o[dt] = mfma_f16(va[g], pb[g], w.o[dt]);
+    for (int dt = 0; dt < 4; ++dt) w.o[dt] = mfma_f16(va[g & 1][dt], w.pb[g], w.o[dt]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
+// The LDS address of stage S plus an opaque zero: it keeps the compiler from hoisting the
+// per-lane addresses of all four stages into registers for the whole loop
 template <int S>
-__device__ __forceinline__ void fwd_unit(FwdState &w, int lane, float scale_log2e) {
-  // an opaque zero added to the stage address keeps the compiler from hoisting the per-lane
-  // swizzled addresses of all four stages into registers for the whole loop
+__device__ __forceinline__ uint32_t fwd_stage_addr() {
   int z = 0;
   asm volatile("" : "+v"(z));
-  const FwdStage &st = *reinterpret_cast<const FwdStage *>(
-      reinterpret_cast<const uint8_t *>(&fwd_stage<S>()) + z);
-  fwd_unit_on(w, st.k, st.v, lane, scale_log2e);
+  return lds_addr(&fwd_stage<S>()) + (uint32_t)z;
 }
 
-// s_waitcnt vmcnt(2 kCpw) (expcnt and lgkmcnt left alone), then a workgroup barrier: every
-// wave issues exactly kCpw copies per step, so this wave's copies for the unit two steps
+// s_waitcnt vmcnt(kCpw) (expcnt and lgkmcnt left alone), then a workgroup barrier: every
+// wave issues exactly kCpw copies per step, so this wave's copies for the unit one step
 // back have landed (vector memory loads complete in order), and after the barrier every
 // wave's have.  The count is the same on every path, which also lets the compiler see that
 // no further wait is needed before the LDS reads.
-__device__ __forceinline__ void wait_unit_two_behind() {
-  wait_and_barrier<vmcnt_imm(2 * kCpw)>();
+__device__ __forceinline__ void wait_unit_one_behind() {
+  wait_and_barrier<vmcnt_imm(kCpw)>();
 }
 
-// One workgroup (8 waves, one per 32 rows; two waves per SIMD, 128 KB of LDS) per query
-// block, persistent over the block list.
-__global__ void __launch_bounds__(NW * 64)
-    attn_fwd_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
-                         const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
-                         const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
-                         const int *__restrict__ unit_blk, const int *__restrict__ blk_start,
-                         const int *__restrict__ blk_size, const int *__restrict__ sel_count,
-                         const int *__restrict__ csr_col, const int *__restrict__ perm,
-                         float scale_log2e, uint16_t *__restrict__ out,
-                         float *__restrict__ lse_out, float *__restrict__ o32p,
-                         float *__restrict__ lsep) {
-  // the wave index is uniform in the wave: in a scalar register, every branch on it (and on
-  // the block-list cursor) is a scalar branch
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+// The waves of one role.  The two waves of a SIMD (w and w + 4) run half a unit apart so
+// that one's softmax arithmetic overlaps the other's MFMAs: after the barrier of step u the
+// early wave (w < 4) forms the scores of unit u, then its PV product; the late wave first
+// finishes the PV product of unit u - 1, then forms the scores of unit u, and carries their
+// weights across the next barrier.
+template <bool LATE>
+__device__ __forceinline__ void fwd_waves(
+    int wave, int lane, int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
+    int ntiles, const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
+    const uint16_t *__restrict__ vp, const int *__restrict__ unit_blk,
+    const int *__restrict__ blk_start, const int *__restrict__ blk_size,
+    const int *__restrict__ sel_count, const int *__restrict__ csr_col,
+    const int *__restrict__ perm, float scale_log2e, uint16_t *__restrict__ out,
+    float *__restrict__ lse_out, float *__restrict__ o32p, float *__restrict__ lsep) {
   const int l32 = lane & 31, hh = lane >> 5;
-  const int ntiles = *tile_count;
-  // copies of this wave: K rows 16w.. (w < 4) or V rows 16(w-4).. (w >= 4)
-  const bool kcopy = wave < NW / 2;
+  // copies of this wave: K rows 16w.. (early waves) or V rows 16(w-4).. (late waves)
   const int wq = wave & (NW / 2 - 1);
-  const uint8_t *csrc = reinterpret_cast<const uint8_t *>(kcopy ? kp : vp);
-  const int cdst = (kcopy ? 0 : 16384) + wq * 4096;
+  const uint8_t *csrc = reinterpret_cast<const uint8_t *>(LATE ? vp : kp);
+  const int cdst = (LATE ? 16384 : 0) + wq * 4096;
   auto cofs = [&](int i) {  // byte offset inside the unit of this lane's 16 bytes, copy i
     const int r = 16 * wq + 4 * i + (lane >> 4);
     return r * 256 + (((lane & 15) ^ swz(r)) << 4);
@@ -222,30 +245,42 @@ __global__ void __launch_bounds__(NW * 64)
         pending = pre.next();
       }
     };
+    // step u (stage S = u mod 4): wait for unit u (unit u + 1 stays in flight), refill the
+    // stage of unit u - 2 (no wave reads it any more) with unit u + 2, compute.  One step
+    // past the last unit finishes the late wave's PV product; the late wave's product in
+    // the first step multiplies unit 0's V by zero weights (adds nothing).  Returns whether
+    // unit u existed.
+    auto step = [&](auto stage_tag, int u) {
+      constexpr int S = decltype(stage_tag)::value;
+      wait_unit_one_behind();
+      issue(fwd_stage<(S + 2) % kStages>());
+      const bool unit_u = u < issued;
+      if (active) {
+        const uint32_t st = fwd_stage_addr<S>();
+        if constexpr (LATE) {
+          const uint32_t prev = fwd_stage_addr<(S + kStages - 1) % kStages>();
+          fwd_values(w, (u == 0 ? st : prev) + 16384, lane);
+          if (!unit_u) return false;
+          fwd_scores(w, st, lane, scale_log2e);
+        } else {
+          if (!unit_u) return false;
+          fwd_scores(w, st, lane, scale_log2e);
+          fwd_values(w, st + 16384, lane);
+        }
+      }
+      return unit_u;
+    };
+#pragma unroll
+    for (int g = 0; g < 4; ++g) w.pb[g] = f16x8{};
 
     workgroup_barrier();  // every wave is done with the previous tile's stages
     issue(g_fwd0);
     issue(g_fwd1);
-    issue(g_fwd2);
-    // step i: wait for unit i (units i+1, i+2 stay in flight), refill the stage unit i-1
-    // used with unit i+3, compute unit i
     for (int i = 0;; i += kStages) {
-      if (i >= issued) break;
-      wait_unit_two_behind();
-      issue(g_fwd3);
-      if (active) fwd_unit<0>(w, lane, scale_log2e);
-      if (i + 1 >= issued) break;
-      wait_unit_two_behind();
-      issue(g_fwd0);
-      if (active) fwd_unit<1>(w, lane, scale_log2e);
-      if (i + 2 >= issued) break;
-      wait_unit_two_behind();
-      issue(g_fwd1);
-      if (active) fwd_unit<2>(w, lane, scale_log2e);
-      if (i + 3 >= issued) break;
-      wait_unit_two_behind();
-      issue(g_fwd2);
-      if (active) fwd_unit<3>(w, lane, scale_log2e);
+      if (!step(std::integral_constant<int, 0>{}, i)) break;
+      if (!step(std::integral_constant<int, 1>{}, i + 1)) break;
+      if (!step(std::integral_constant<int, 2>{}, i + 2)) break;
+      if (!step(std::integral_constant<int, 3>{}, i + 3)) break;
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the trailing repeat copies
     // epilogue
@@ -274,6 +309,33 @@ __global__ void __launch_bounds__(NW * 64)
       lsep[(size_t)h * N + prow] = lse;
     }
   }
+}
+
+// One workgroup (8 waves, one per 32 rows; two waves per SIMD, 128 KB of LDS) per query
+// block, persistent over the block list.
+__global__ void __launch_bounds__(NW * 64)
+    attn_fwd_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
+                         const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
+                         const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
+                         const int *__restrict__ unit_blk, const int *__restrict__ blk_start,
+                         const int *__restrict__ blk_size, const int *__restrict__ sel_count,
+                         const int *__restrict__ csr_col, const int *__restrict__ perm,
+                         float scale_log2e, uint16_t *__restrict__ out,
+                         float *__restrict__ lse_out, float *__restrict__ o32p,
+                         float *__restrict__ lsep) {
+  // the wave index is uniform in the wave: in a scalar register, every branch on it (and on
+  // the block-list cursor) is a scalar branch
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int ntiles = *tile_count;
+  // the two roles run the same sequence of barriers and copies
+  if (wave < NW / 2)
+    fwd_waves<false>(wave, lane, N, U, nb_max, heads, tiles, ntiles, qp, kp, vp, unit_blk,
+                     blk_start, blk_size, sel_count, csr_col, perm, scale_log2e, out, lse_out,
+                     o32p, lsep);
+  else
+    fwd_waves<true>(wave, lane, N, U, nb_max, heads, tiles, ntiles, qp, kp, vp, unit_blk,
+                    blk_start, blk_size, sel_count, csr_col, perm, scale_log2e, out, lse_out,
+                    o32p, lsep);
 }
 
 // ---------------------------------------------------------------------------- float32

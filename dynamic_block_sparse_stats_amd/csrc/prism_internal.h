@@ -153,6 +153,47 @@ __device__ __forceinline__ f16x8 tr_operand(const uint8_t *tile, int kb, int db,
   return r;
 }
 
+// The same reads with the per-lane address arithmetic hoisted: in a 256-byte aligned tile the
+// swizzle and the chunk index only touch address bits 4-7, so chunk c of row r lies at
+// row_base(r) ^ (c << 4); and a transposed piece (kb, db) lies at tr_base ^ (2 db) + 256 kb
+// (kb a multiple of 16 leaves swz unchanged, db a multiple of 32 flips chunk bits 2-3 only).
+// A wave then keeps one or two base registers per tile instead of one address per read.
+// Addresses are 32-bit LDS byte addresses.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+__device__ __forceinline__ uint32_t row_base(uint32_t tile, int r) {
+  return tile + (uint32_t)(r * 256 + (swz(r) << 4));
+}
+__device__ __forceinline__ f16x8 lds_row16(uint32_t addr) {
+  return __builtin_bit_cast(
+      f16x8, *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)addr);
+}
+struct TrBase {
+  uint32_t m0, m1;  // the lane's 8-byte piece of rows 0-7 and 8-15 at kb = 0, db = 0
+};
+__device__ __forceinline__ TrBase tr_base(uint32_t tile, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int col = 16 * (g & 1) + 4 * (s & 3);
+  const int row = 4 * (g >> 1) + (s >> 2);
+  const uint32_t t = tile + (uint32_t)((col & 7) * 2);
+  return {t + (uint32_t)rm_swz(row, col >> 3), t + (uint32_t)rm_swz(row + 8, col >> 3)};
+}
+// tr_operand(tile, kb, db, lane) from tr_base(tile, lane)
+__device__ __forceinline__ f16x8 tr_read(const TrBase &b, int kb, int db) {
+  f16x8 r;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const uint32_t a = ((m ? b.m1 : b.m0) ^ (uint32_t)(2 * db)) + (uint32_t)(256 * kb);
+    const fp16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+        (__attribute__((address_space(3))) fp16x4_t *)(uintptr_t)a);
+    const f16x4 w = __builtin_bit_cast(f16x4, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[4 * m + e] = w[e];
+  }
+  return r;
+}
+
 // Typed MFMA wrappers: the builtins accept any 8-element 16-bit vector silently, these do
 // not (32x32 output tile, K = 16; C/D layout: lane -> column lane % 32, register v -> row
 // (v / 4) * 8 + 4 * (lane / 32) + v % 4).
@@ -164,22 +205,33 @@ __device__ __forceinline__ f32x16 mfma_f16(f16x8 a, f16x8 b, f32x16 c) {
 }
 
 // Direct global -> LDS copies (global_load_lds): lane l of one instruction writes its
-// 16 (or 4) bytes at dst + 16 * l (4 * l); dst must be uniform across the wave.
-// The LDS destination is passed on as a plain 32-bit address taken through readfirstlane
-// (it is uniform: every lane of a copy writes dst + 16 * lane): the compiler then has no
-// object to tie the copy to and adds no waits of its own before LDS reads; the kernels
-// order copies and reads themselves with s_waitcnt vmcnt and barriers.
-__device__ __forceinline__ void dma16(const void *src, void *dst) {
-  const uint32_t a = __builtin_amdgcn_readfirstlane(
+// 16 (or 4) bytes at dst + 16 * l (4 * l); dst must be uniform across the wave and is
+// passed in M0.  They are written as inline assembly on purpose: the compiler classes the
+// instruction as a flat access that may touch LDS, and while one is outstanding on vmcnt
+// (in these kernels: always) it makes every wait for an LDS read wait for all of them
+// (lgkmcnt(0)), which stops any LDS read from overlapping the MFMAs before it.  The
+// hardware counts these copies on vmcnt only.  Hidden from the compiler, they are ordered
+// by the kernels themselves: explicit s_waitcnt vmcnt before the barrier that publishes a
+// stage, and the "memory" clobber, which keeps the compiler from moving LDS accesses across
+// a copy.  (Loads the compiler issues itself stay correct: copies it does not know of only
+// make its vmcnt waits stricter.)  M0 is written only here in these kernels.
+__device__ __forceinline__ uint32_t lds_dst(void *dst) {
+  return __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)dst);
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                   (__attribute__((address_space(3))) void *)(uintptr_t)a, 16,
-                                   0, 0);
+}
+__device__ __forceinline__ void dma16(const void *src, void *dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_dst(dst))
+               : "memory");
 }
 __device__ __forceinline__ void dma4(const void *src, void *dst) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                   (__attribute__((address_space(3))) void *)dst, 4, 0, 0);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(lds_dst(dst))
+               : "memory");
 }
+
 // s_waitcnt with the given immediate, then a workgroup barrier.  The compiler fences on
 // both sides keep every memory operation of this wave in program order around the pair:
 // LDS writes issued before it are covered by the wait (s_barrier itself does not order
