@@ -22,28 +22,35 @@ constexpr int kDB = 128;
 //     hands P to its partner through LDS (float32) and accumulates dV^T += dO^T P;
 //   * the dS wave (w >= 4) holds V as B operand, forms dP = dO V^T and accumulates
 //     dK^T += Q^T dS with dS = P (dP - delta).
-// Each wave does the same number of MFMAs and keeps one operand set and one accumulator
-// set, so two waves fit per SIMD.
+// The two waves of a pair share a SIMD.  Each unit has two barriers: after the first the
+// P wave forms S and P while the dS wave forms dP and then the dK product of the previous
+// unit (so the P wave's exponentials overlap MFMAs); after the second (P published) the P
+// wave runs its dV product while the dS wave forms dS, which it keeps for the next unit.
+// One step past the last unit finishes the last dK product.
 //
 // Query units stream through a three-stage LDS ring filled by direct global->LDS copies
 // (global_load_lds_dwordx4: lane l of one instruction lands at +16*l, so the XOR swizzle
-// is applied by choosing which source chunk each lane fetches), two units ahead of the
-// one being computed.  Per stage: Q and dO row-major [64][128] float16 (Q^T and dO^T are
-// read from them with transposing LDS reads), lse and delta [64].  Waves 0-3 copy 16 Q
-// rows each, waves 4-7 16 dO rows (four one-kilobyte copies per unit), waves 0 and 1
-// also one 256-byte vector.  A second barrier per unit publishes P.
+// is applied by choosing which source chunk each lane fetches).  The copies of unit u + 2
+// are issued after the second barrier of unit u, once the dS wave is done with the stage
+// of unit u - 1.  Per stage: Q and dO row-major [64][128] float16 (Q^T and dO^T are read
+// from them with transposing LDS reads), lse and delta [64].  Waves 0-3 copy 16 Q rows
+// each, waves 4-7 16 dO rows (four one-kilobyte copies per unit), waves 0 and 1 also one
+// 256-byte vector.
 constexpr int NW = 8;
 constexpr int kStages = 3;
+constexpr uint32_t kDOTile = 16384;  // byte offset of the dO tile in a stage
+constexpr uint32_t kVecs = 32768;    // byte offset of the lse and delta vectors
 
 // The stages are distinct LDS objects and the unit loop is unrolled by three, so every
-// LDS read names its stage statically.
+// LDS read names its stage statically.  256-byte alignment lets the swizzled addresses be
+// formed by XOR (row_base, tr_base).
 struct Stage {
   uint8_t tile[2][16384];  // Q, dO (row-major float16)
   float vec[2][kUnit];     // lse * log2(e), -delta
 };
-__shared__ __align__(16) Stage g_stage0;
-__shared__ __align__(16) Stage g_stage1;
-__shared__ __align__(16) Stage g_stage2;
+__shared__ __align__(256) Stage g_stage0;
+__shared__ __align__(256) Stage g_stage1;
+__shared__ __align__(256) Stage g_stage2;
 // P (float32) of the current unit per pair, in the P wave's C layout:
 // [pair][half][register group of 4][lane]
 __shared__ __align__(16) f32x4 g_pex[4][2][4][64];
@@ -51,53 +58,74 @@ template <int S>
 __device__ __forceinline__ Stage &stage() {
   return S == 0 ? g_stage0 : (S == 1 ? g_stage1 : g_stage2);
 }
-
+// The LDS address of stage S plus an opaque zero: it keeps the per-lane addresses of all
+// stages from being hoisted into registers for the whole loop
 template <int S>
-__device__ __forceinline__ const Stage &stage_opaque() {
-  // an opaque zero added to the stage address keeps the per-lane swizzled addresses of
-  // all stages from being hoisted into registers for the whole loop
+__device__ __forceinline__ uint32_t stage_addr() {
   int z = 0;
   asm volatile("" : "+v"(z));
-  return *reinterpret_cast<const Stage *>(reinterpret_cast<const uint8_t *>(&stage<S>()) + z);
+  return lds_addr(&stage<S>()) + (uint32_t)z;
+}
+__device__ __forceinline__ f32x4 lds_f32x4(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) f32x4 *)(uintptr_t)addr;
 }
 
-// acc (C layout: lane = key l32, register v = query 32a + (v/4)*8 + 4hh + v%4) += the
-// 32 queries of half a of tile t (row-major [64][128] float16) times the wave's B operand
-__device__ __forceinline__ void half_product(f32x16 &acc, const uint8_t *tile, int a,
-                                             const f16x8 (&b)[8], int l32, int hh) {
-  const int r = 32 * a + l32;
+// acc[a] (C layout: lane = key l32, register v = query 32a + (v/4)*8 + 4hh + v%4) += the
+// 32 queries of half a of the row-major [64][128] float16 tile at LDS address t times the
+// wave's B operand, for both halves: the two accumulators alternate, and the operands of
+// the next group of four MFMAs are read while the current group runs
+__device__ __forceinline__ void both_halves_product(f32x16 (&acc)[2], uint32_t t,
+                                                    const f16x8 (&b)[8], int l32, int hh) {
+  // chunk 2kk + hh of row l32 at r ^ (kk << 5); row 32 + l32 8 KB further
+  const uint32_t r = row_base(t, l32) ^ (uint32_t)(hh << 4);
+  f16x8 x[2][2][2];  // [buffer][a][e]
+  auto load = [&](int buf, int grp) {
 #pragma unroll
-  for (int grp = 0; grp < 2; ++grp) {
-    f16x8 x[4];
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      x[e] = __builtin_bit_cast(
-          f16x8, *reinterpret_cast<const u32x4 *>(tile + rm_swz(r, 2 * (4 * grp + e) + hh)));
+      for (int e = 0; e < 2; ++e)
+        x[buf][a][e] = lds_row16((r ^ (uint32_t)((2 * grp + e) << 5)) + 8192u * a);
+  };
+  load(0, 0);
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) {
+    if (grp < 3) load((grp + 1) & 1, grp + 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc = mfma_f16(x[e], b[4 * grp + e], acc);
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) acc[a] = mfma_f16(x[grp & 1][a][e], b[2 * grp + e], acc[a]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// acc[dt] (C layout: lane = key, register -> d) += T^T[d][queries of half a] X[q][key]
-// with T^T read transposed from the row-major tile and X the float16 B operands of the
-// half's two 16-query slices
-__device__ __forceinline__ void half_update(f32x16 (&acc)[4], const uint8_t *tile, int a,
-                                            const f16x8 (&x)[2], int lane) {
+// acc[dt] (C layout: lane = key, register -> d) += T^T[d][q] X[q][key] over the unit's 64
+// queries, T^T read transposed from the row-major tile whose transposed-read base is tb,
+// X the float16 B operands of the four 16-query slices ([half][slice]); per slice the
+// four d-tiles' accumulators are independent, and the next slice's operands are read
+// while one runs
+__device__ __forceinline__ void unit_update(f32x16 (&acc)[4], const TrBase &tb,
+                                            const f16x8 (&x)[2][2]) {
+  f16x8 ta[2][4];  // [buffer][dt]
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    f16x8 ta[2];
+  for (int dt = 0; dt < 4; ++dt) ta[0][dt] = tr_read(tb, 0, 32 * dt);
 #pragma unroll
-    for (int g = 0; g < 2; ++g) ta[g] = tr_operand(tile, 32 * a + 16 * g, 32 * dt, lane);
+  for (int sl = 0; sl < 4; ++sl) {
+    if (sl < 3)
 #pragma unroll
-    for (int g = 0; g < 2; ++g) acc[dt] = mfma_f16(ta[g], x[g], acc[dt]);
+      for (int dt = 0; dt < 4; ++dt) ta[(sl + 1) & 1][dt] = tr_read(tb, 16 * (sl + 1), 32 * dt);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      acc[dt] = mfma_f16(ta[sl & 1][dt], x[sl >> 1][sl & 1], acc[dt]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // The state of one wave of a pair: its B operand rows (K for the P wave, V for the dS
-// wave), its accumulators (dV^T or dK^T) and the current unit's values: P * 2^10 as
-// float16 (the operand of the dV product) [half][k-slice], or dP - delta in float32
-// [half].
+// wave), its accumulators (dV^T or dK^T) and the values it carries: the P wave P * 2^10
+// as float16 (the operand of the dV product) [half][slice]; the dS wave dP - delta in
+// float32 [half] and the previous unit's dS as float16 [half][slice].
 struct PState {
   f16x8 breg[8];
   f32x16 acc[4];
@@ -107,74 +135,76 @@ struct DState {
   f16x8 breg[8];
   f32x16 acc[4];
   f32x16 dp[2];
+  f16x8 db[2][2];
 };
 
-// P wave, before the mid-unit barrier: S and P for both halves, P published
-template <int S>
-__device__ __forceinline__ void p_first(PState &w, int pair, int lane, float scale_log2e) {
-  const Stage &sg = stage_opaque<S>();
+// P wave, before the mid-unit barrier: S and P for both halves, P published; st is the
+// stage's LDS address
+__device__ __forceinline__ void p_first(PState &w, uint32_t st, int pair, int lane,
+                                        float scale_log2e) {
   const int l32 = lane & 31, hh = lane >> 5;
+  f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  both_halves_product(sacc, st, w.breg, l32, hh);
+  f16x8 x[2][2];  // built fresh: the previous unit's weights are dead here
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
-    f32x16 sacc = f32x16{};
-    half_product(sacc, sg.tile[0], a, w.breg, l32, hh);
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sg.vec[0] + 32 * a + 8 * v4 + 4 * hh);
+      const f32x4 l4 = lds_f32x4(st + kVecs + 4u * (32 * a + 8 * v4 + 4 * hh));
       f32x4 p4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int v = 4 * v4 + e;
-        p4[e] = __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2e, -l4[e]));
-        w.x[a][v >> 3][v & 7] = (_Float16)(p4[e] * kPScale);
+        p4[e] = __builtin_amdgcn_exp2f(fmaf(sacc[a][v], scale_log2e, -l4[e]));
+        x[a][v >> 3][v & 7] = (_Float16)(p4[e] * kPScale);
       }
       g_pex[pair][a][v4][lane] = p4;
     }
   }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) w.x[a][g] = x[a][g];
 }
 // P wave, after the barrier: dV^T += dO^T (P * 2^10)
-template <int S>
-__device__ __forceinline__ void p_second(PState &w, int lane) {
-  const Stage &sg = stage_opaque<S>();
-#pragma unroll
-  for (int a = 0; a < 2; ++a) half_update(w.acc, sg.tile[1], a, w.x[a], lane);
+__device__ __forceinline__ void p_second(PState &w, uint32_t st, int lane) {
+  unit_update(w.acc, tr_base(st + kDOTile, lane), w.x);
 }
 // dS wave, before the barrier: dP, started at -delta
-template <int S>
-__device__ __forceinline__ void d_first(DState &w, int lane) {
-  const Stage &sg = stage_opaque<S>();
+__device__ __forceinline__ void d_dp(DState &w, uint32_t st, int lane) {
   const int l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    f32x16 &dp = w.dp[a];
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4) {
-      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sg.vec[1] + 32 * a + 8 * v4 + 4 * hh);
+      const f32x4 d4 = lds_f32x4(st + kVecs + 4u * (kUnit + 32 * a + 8 * v4 + 4 * hh));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dp[4 * v4 + e] = d4[e];
+      for (int e = 0; e < 4; ++e) w.dp[a][4 * v4 + e] = d4[e];
     }
-    half_product(dp, sg.tile[1], a, w.breg, l32, hh);
-  }
+  both_halves_product(w.dp, st + kDOTile, w.breg, l32, hh);
 }
-// dS wave, after the barrier: dS = P (dP - delta) in float32, rounded once to float16;
-// dK^T += Q^T dS
-template <int S>
-__device__ __forceinline__ void d_second(DState &w, int pair, int lane) {
-  const Stage &sg = stage_opaque<S>();
+// dS wave: dK^T += Q^T dS with the carried dS, Q^T read from the Q tile of stage st
+__device__ __forceinline__ void d_dk(DState &w, uint32_t st, int lane) {
+  unit_update(w.acc, tr_base(st, lane), w.db);
+}
+// dS wave, after the barrier: dS = P (dP - delta) in float32, rounded once to float16
+__device__ __forceinline__ void d_ds(DState &w, int pair, int lane) {
+  f16x8 db[2][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    f16x8 db[2];
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4) {
       const f32x4 p4 = g_pex[pair][a][v4][lane];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int v = 4 * v4 + e;
-        db[v >> 3][v & 7] = (_Float16)(p4[e] * w.dp[a][v]);
+        db[a][v >> 3][v & 7] = (_Float16)(p4[e] * w.dp[a][v]);
       }
     }
-    half_update(w.acc, sg.tile[0], a, db, lane);
-  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) w.db[a][g] = db[a][g];
 }
 
 // P published: the P waves' LDS writes are complete before the barrier
@@ -226,13 +256,21 @@ __device__ __forceinline__ void dkdv_waves(
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) w.acc[dt] = f32x16{};
+    if constexpr (!PW) {
+      // the dK product of the first step multiplies by zero (there is no previous unit)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) w.db[a][g] = f16x8{};
+    }
 
     const size_t hb = (size_t)h * N;
     int issued = 0;
     bool pending = true;
     BlockUnits pre;
     // every step issues this wave's copies: past the end of the list they repeat the last
-    // unit into a stage no step reads any more (drained before the next tile)
+    // unit (finite data) into a stage no step reads any more, or reads only for a result
+    // it discards (drained before the next tile)
     auto issue = [&](Stage &st) {
       const int u = pre.unit();
       const uint8_t *src = tsrc + (hb + (size_t)u * kUnit) * kDB * 2;
@@ -252,17 +290,33 @@ __device__ __forceinline__ void dkdv_waves(
       else
         wait_and_barrier<vmcnt_imm(4)>();
     };
-    auto unit = [&](auto stage_tag) {
+    // step u (stage S = u mod 3): wait for unit u; first half; barrier (P published);
+    // refill the stage of unit u - 1 with unit u + 2; second half.  Returns whether unit
+    // u existed.  The step after the last unit only runs the dS wave's last dK product
+    // (its dP there reads the repeated copy of the last unit and is discarded).
+    auto step = [&](auto stage_tag, int u) {
       constexpr int S = decltype(stage_tag)::value;
+      wait_one_behind();
+      const bool unit_u = u < issued;
+      const uint32_t st = stage_addr<S>();
       if constexpr (PW) {
-        if (active) p_first<S>(w, pair, lane, scale_log2e);
+        if (!unit_u) return false;
+        if (active) p_first(w, st, pair, lane, scale_log2e);
         publish_sync();
-        if (active) p_second<S>(w, lane);
+        issue(stage<(S + 2) % kStages>());
+        if (active) p_second(w, st, lane);
       } else {
-        if (active) d_first<S>(w, lane);
+        if (active) {
+          d_dp(w, st, lane);
+          const uint32_t prev = stage_addr<(S + kStages - 1) % kStages>();
+          d_dk(w, u == 0 ? st : prev, lane);
+        }
+        if (!unit_u) return false;
         publish_sync();
-        if (active) d_second<S>(w, pair, lane);
+        issue(stage<(S + 2) % kStages>());
+        if (active) d_ds(w, pair, lane);
       }
+      return true;
     };
 
     workgroup_barrier();  // every wave is done with the previous tile's stages
@@ -272,18 +326,9 @@ __device__ __forceinline__ void dkdv_waves(
       issue(g_stage0);
       issue(g_stage1);
       for (int i = 0;; i += kStages) {
-        if (i >= issued) break;
-        wait_one_behind();
-        issue(g_stage2);
-        unit(std::integral_constant<int, 0>{});
-        if (i + 1 >= issued) break;
-        wait_one_behind();
-        issue(g_stage0);
-        unit(std::integral_constant<int, 1>{});
-        if (i + 2 >= issued) break;
-        wait_one_behind();
-        issue(g_stage1);
-        unit(std::integral_constant<int, 2>{});
+        if (!step(std::integral_constant<int, 0>{}, i)) break;
+        if (!step(std::integral_constant<int, 1>{}, i + 1)) break;
+        if (!step(std::integral_constant<int, 2>{}, i + 2)) break;
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the trailing repeat copies
     }
