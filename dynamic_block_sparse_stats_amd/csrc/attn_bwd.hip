@@ -86,110 +86,113 @@ __global__ void __launch_bounds__(256)
 // ============================================================================ dQ (bf16)
 // One workgroup of eight waves (two per SIMD) per query block (32 queries per wave, Q and
 // dO rows held as B operands), streaming the selected key units through a four-stage LDS
-// ring of direct global->LDS copies, three units ahead of the one being computed: per
-// stage K and V row-major [64][128] float16 (32 KB); waves 0-3 copy 16 K rows each, waves
-// 4-7 16 V rows, four one-kilobyte copies per wave and unit.
+// ring of direct global->LDS copies, two units ahead of the one being computed: per stage
+// K and V row-major [64][128] float16 (32 KB); waves 0-3 copy 16 K rows each, waves 4-7
+// 16 V rows, four one-kilobyte copies per wave and unit.  Per unit a wave forms S^T and
+// dP^T (K and V rows read directly), dS = P (dP - delta) as float16, and dQ^T += K^T dS^T
+// (K^T through transposing reads).  As in the forward, the two waves of a SIMD run half a
+// unit apart: the late wave (w >= 4) runs the dQ product of the previous unit before the
+// scores of the current one, carrying dS across the barrier, so one wave's exponentials
+// overlap the other's MFMAs.
 constexpr int QW = 8;
 constexpr int kQStages = 4;
 constexpr int kQCpw = 32 / QW;
-constexpr int kQGroups = 4;  // K and V operand reads go in groups of 8 / kQGroups
 struct DqStage {
   uint8_t tile[2][16384];  // K, V
 };
-__shared__ __align__(16) DqStage g_dq0;
-__shared__ __align__(16) DqStage g_dq1;
-__shared__ __align__(16) DqStage g_dq2;
-__shared__ __align__(16) DqStage g_dq3;
+__shared__ __align__(256) DqStage g_dq0;
+__shared__ __align__(256) DqStage g_dq1;
+__shared__ __align__(256) DqStage g_dq2;
+__shared__ __align__(256) DqStage g_dq3;
 template <int S>
-__device__ __forceinline__ const DqStage &dq_stage() {
+__device__ __forceinline__ DqStage &dq_stage() {
   return S == 0 ? g_dq0 : (S == 1 ? g_dq1 : (S == 2 ? g_dq2 : g_dq3));
+}
+// The LDS address of stage S plus an opaque zero: it keeps the per-lane addresses of all
+// stages from being hoisted into registers for the whole loop
+template <int S>
+__device__ __forceinline__ uint32_t dq_stage_addr() {
+  int z = 0;
+  asm volatile("" : "+v"(z));
+  return lds_addr(&dq_stage<S>()) + (uint32_t)z;
 }
 
 struct DqState {
   f16x8 qreg[8], doreg[8];
   f32x16 acc[4];
+  f16x8 db[2][2];  // the current unit's dS (float16 B operands) [half][slice]
   float lse2, ndlt;
 };
 
-template <int S>
-__device__ __forceinline__ void dq_unit(DqState &w, int lane, float scale_log2e) {
-  // an opaque zero added to the stage address keeps the compiler from hoisting the per-lane
-  // swizzled addresses of all stages out of the loop (they do not fit in the registers left
-  // beside the operands)
-  int z = 0;
-  asm volatile("" : "+v"(z));
-  const DqStage &sg = *reinterpret_cast<const DqStage *>(
-      reinterpret_cast<const uint8_t *>(&dq_stage<S>()) + z);
+// Keys 32a .. 32a + 31 of the unit at LDS address st: S^T = K Q^T and dP^T = V dO^T (dP
+// started at -delta; lane = query l32, register v = key 32a + (v/4)*8 + 4hh + v%4), their
+// MFMAs alternating, the next k-step's K and V operands read while one runs; then
+// dS = P (dP - delta) rounded to float16
+__device__ __forceinline__ void dq_half(const DqState &w, uint32_t st, int a, int lane,
+                                        float scale_log2e, f16x8 (&db)[2]) {
   const int l32 = lane & 31, hh = lane >> 5;
+  // chunk 2kk + hh of K row 32a + l32 at r ^ (kk << 5); the V row 16 KB further
+  const uint32_t r = row_base(st, 32 * a + l32) ^ (uint32_t)(hh << 4);
+  f32x16 s = f32x16{}, dp;
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {  // keys 32a .. 32a + 31
-    const int r = 32 * a + l32;
-    // S^T = K Q^T and dP^T = V dO^T (dP started at -delta) in groups of four operand
-    // reads ahead of their MFMAs
-    f32x16 s = f32x16{}, dp;
+  for (int v = 0; v < 16; ++v) dp[v] = w.ndlt;
+  f16x8 x[2][2];  // [buffer][K, V]: one k-step of 16 dims per group
+  auto load = [&](int buf, int kk) {
+    const uint32_t ad = r ^ (uint32_t)(kk << 5);
+    x[buf][0] = lds_row16(ad);
+    x[buf][1] = lds_row16(ad + 16384u);
+  };
+  load(0, 0);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) dp[v] = w.ndlt;
+  for (int kk = 0; kk < 8; ++kk) {
+    if (kk < 7) load((kk + 1) & 1, kk + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    s = mfma_f16(x[kk & 1][0], w.qreg[kk], s);
+    dp = mfma_f16(x[kk & 1][1], w.doreg[kk], dp);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
-    for (int grp = 0; grp < 2 * kQGroups; ++grp) {
-      constexpr int GS = 8 / kQGroups;
-      const uint8_t *tile = sg.tile[grp / kQGroups];
-      f16x8 ka[GS];
-#pragma unroll
-      for (int e = 0; e < GS; ++e)
-        ka[e] = __builtin_bit_cast(
-            f16x8, *reinterpret_cast<const u32x4 *>(
-                       tile + rm_swz(r, 2 * (GS * (grp % kQGroups) + e) + hh)));
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int e = 0; e < GS; ++e) {
-        const int kk = GS * (grp % kQGroups) + e;
-        if (grp < kQGroups)
-          s = mfma_f16(ka[e], w.qreg[kk], s);
-        else
-          dp = mfma_f16(ka[e], w.doreg[kk], dp);
-      }
-    }
-    // lane = query, register v = key 32a + (v/4)*8 + 4hh + v%4:  dS = P (dP - delta)
-    f16x8 db[2];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[v], scale_log2e, -w.lse2));
-      db[v >> 3][v & 7] = (_Float16)(p * dp[v]);
-    }
-    // dQ^T[d][q] += K^T[d][keys of this half] dS^T[keys][q], K^T read transposed
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-        w.acc[dt] = mfma_f16(tr_operand(sg.tile[0], 32 * a + 16 * g, 32 * dt, lane), db[g],
-                             w.acc[dt]);
+  for (int v = 0; v < 16; ++v) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(s[v], scale_log2e, -w.lse2));
+    db[v >> 3][v & 7] = (_Float16)(p * dp[v]);
   }
 }
-
-// s_waitcnt vmcnt(2 kQCpw) and a workgroup barrier: every wave issues exactly kQCpw copies
-// per step, so the unit two steps behind the newest has landed everywhere
-__device__ __forceinline__ void dq_wait_two_behind() {
-  wait_and_barrier<vmcnt_imm(2 * kQCpw)>();
+// dS of the unit at st (both halves, built fresh: the previous unit's is dead here)
+__device__ __forceinline__ void dq_scores(DqState &w, uint32_t st, int lane, float scale_log2e) {
+  f16x8 db[2][2];
+  dq_half(w, st, 0, lane, scale_log2e, db[0]);
+  dq_half(w, st, 1, lane, scale_log2e, db[1]);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) w.db[a][g] = db[a][g];
+}
+// dQ^T[d][q] += K^T[d][keys] dS^T[keys][q], K^T read transposed from the K tile at st
+__device__ __forceinline__ void dq_update(DqState &w, uint32_t st, int lane) {
+  tr_update(w.acc, tr_base(st, lane), w.db);
 }
 
-__global__ void __launch_bounds__(QW * 64)
-    attn_dq_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
-                        const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
-                        const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
-                        const uint16_t *__restrict__ dop, const float *__restrict__ lse2,
-                        const float *__restrict__ ndelta, const int *__restrict__ unit_blk,
-                        const int *__restrict__ blk_start, const int *__restrict__ blk_size,
-                        const int *__restrict__ sel_count, const int *__restrict__ csr_col,
-                        const int *__restrict__ perm, float scale, float scale_log2e,
-                        uint16_t *__restrict__ dq) {
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+// s_waitcnt vmcnt(kQCpw) and a workgroup barrier: every wave issues exactly kQCpw copies
+// per step, so the unit one step behind the newest has landed everywhere
+__device__ __forceinline__ void dq_wait_one_behind() {
+  wait_and_barrier<vmcnt_imm(kQCpw)>();
+}
+
+template <bool LATE>
+__device__ __forceinline__ void dq_waves(
+    int wave, int lane, int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
+    int ntiles, const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
+    const uint16_t *__restrict__ vp, const uint16_t *__restrict__ dop,
+    const float *__restrict__ lse2, const float *__restrict__ ndelta,
+    const int *__restrict__ unit_blk, const int *__restrict__ blk_start,
+    const int *__restrict__ blk_size, const int *__restrict__ sel_count,
+    const int *__restrict__ csr_col, const int *__restrict__ perm, float scale,
+    float scale_log2e, uint16_t *__restrict__ dq) {
   const int l32 = lane & 31, hh = lane >> 5;
-  const int ntiles = *tile_count;
-  // copies of this wave: K rows 16w.. (w < 4) or V rows 16(w-4).. (w >= 4)
-  const bool kcopy = wave < QW / 2;
+  // copies of this wave: K rows 16w.. (early waves) or V rows 16(w-4).. (late waves)
   const int wq = wave & (QW / 2 - 1);
-  const uint8_t *csrc = reinterpret_cast<const uint8_t *>(kcopy ? kp : vp);
-  const int cdst = (kcopy ? 0 : 16384) + wq * 4096;
+  const uint8_t *csrc = reinterpret_cast<const uint8_t *>(LATE ? vp : kp);
+  const int cdst = (LATE ? 16384 : 0) + wq * 4096;
   auto cofs = [&](int i) {  // byte offset inside the unit of this lane's 16 bytes, copy i
     const int r = 16 * wq + 4 * i + (lane >> 4);
     return r * 256 + (((lane & 15) ^ swz(r)) << 4);
@@ -223,6 +226,11 @@ __global__ void __launch_bounds__(QW * 64)
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) w.acc[dt] = f32x16{};
+    // the late wave's dQ product of the first step multiplies by zero (no previous unit)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) w.db[a][g] = f16x8{};
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // rows and cursor window in before any copy
 
     const uint8_t *hbase = csrc + (size_t)h * N * kDB * 2;
@@ -230,39 +238,48 @@ __global__ void __launch_bounds__(QW * 64)
     bool pending = true;
     // kQCpw copies per step; past the end of the list they repeat the last unit into a
     // stage no step reads any more (drained before the next tile)
-    auto issue = [&](const DqStage &st) {
+    auto issue = [&](DqStage &st) {
       const uint8_t *src = hbase + (size_t)pre.unit() * kUnit * kDB * 2;
 #pragma unroll
       for (int i = 0; i < kQCpw; ++i)
-        dma16(src + cofs(i), const_cast<uint8_t *>(reinterpret_cast<const uint8_t *>(&st)) +
-                                 cdst + 1024 * i);
+        dma16(src + cofs(i), reinterpret_cast<uint8_t *>(&st) + cdst + 1024 * i);
       if (pending) {
         ++issued;
         pending = pre.next();
       }
     };
+    // step u (stage S = u mod 4): wait for unit u (u + 1 stays in flight), refill the stage
+    // of unit u - 2 with unit u + 2, compute.  One step past the last unit finishes the
+    // late wave's dQ product.  Returns whether unit u existed.
+    auto step = [&](auto stage_tag, int u) {
+      constexpr int S = decltype(stage_tag)::value;
+      dq_wait_one_behind();
+      issue(dq_stage<(S + 2) % kQStages>());
+      const bool unit_u = u < issued;
+      if (active) {
+        const uint32_t st = dq_stage_addr<S>();
+        if constexpr (LATE) {
+          const uint32_t prev = dq_stage_addr<(S + kQStages - 1) % kQStages>();
+          dq_update(w, u == 0 ? st : prev, lane);
+          if (!unit_u) return false;
+          dq_scores(w, st, lane, scale_log2e);
+        } else {
+          if (!unit_u) return false;
+          dq_scores(w, st, lane, scale_log2e);
+          dq_update(w, st, lane);
+        }
+      }
+      return unit_u;
+    };
 
     workgroup_barrier();  // every wave is done with the previous tile's stages
     issue(g_dq0);
     issue(g_dq1);
-    issue(g_dq2);
     for (int i = 0;; i += kQStages) {
-      if (i >= issued) break;
-      dq_wait_two_behind();
-      issue(g_dq3);
-      if (active) dq_unit<0>(w, lane, scale_log2e);
-      if (i + 1 >= issued) break;
-      dq_wait_two_behind();
-      issue(g_dq0);
-      if (active) dq_unit<1>(w, lane, scale_log2e);
-      if (i + 2 >= issued) break;
-      dq_wait_two_behind();
-      issue(g_dq1);
-      if (active) dq_unit<2>(w, lane, scale_log2e);
-      if (i + 3 >= issued) break;
-      dq_wait_two_behind();
-      issue(g_dq2);
-      if (active) dq_unit<3>(w, lane, scale_log2e);
+      if (!step(std::integral_constant<int, 0>{}, i)) break;
+      if (!step(std::integral_constant<int, 1>{}, i + 1)) break;
+      if (!step(std::integral_constant<int, 2>{}, i + 2)) break;
+      if (!step(std::integral_constant<int, 3>{}, i + 3)) break;
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the trailing repeat copies
     if (!active) continue;
@@ -280,6 +297,30 @@ __global__ void __launch_bounds__(QW * 64)
         *reinterpret_cast<u32x2 *>(qrow + d0) = u32x2{lo, hi};
       }
   }
+}
+
+__global__ void __launch_bounds__(QW * 64)
+    attn_dq_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
+                        const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
+                        const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
+                        const uint16_t *__restrict__ dop, const float *__restrict__ lse2,
+                        const float *__restrict__ ndelta, const int *__restrict__ unit_blk,
+                        const int *__restrict__ blk_start, const int *__restrict__ blk_size,
+                        const int *__restrict__ sel_count, const int *__restrict__ csr_col,
+                        const int *__restrict__ perm, float scale, float scale_log2e,
+                        uint16_t *__restrict__ dq) {
+  // the wave index is uniform in the wave; the two roles run the same sequence of barriers
+  // and copies
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int ntiles = *tile_count;
+  if (wave < QW / 2)
+    dq_waves<false>(wave, lane, N, U, nb_max, heads, tiles, ntiles, qp, kp, vp, dop, lse2,
+                    ndelta, unit_blk, blk_start, blk_size, sel_count, csr_col, perm, scale,
+                    scale_log2e, dq);
+  else
+    dq_waves<true>(wave, lane, N, U, nb_max, heads, tiles, ntiles, qp, kp, vp, dop, lse2,
+                   ndelta, unit_blk, blk_start, blk_size, sel_count, csr_col, perm, scale,
+                   scale_log2e, dq);
 }
 
 // ============================================================================ float32

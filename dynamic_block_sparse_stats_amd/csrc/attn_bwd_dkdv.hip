@@ -99,29 +99,6 @@ __device__ __forceinline__ void both_halves_product(f32x16 (&acc)[2], uint32_t t
   }
 }
 
-// acc[dt] (C layout: lane = key, register -> d) += T^T[d][q] X[q][key] over the unit's 64
-// queries, T^T read transposed from the row-major tile whose transposed-read base is tb,
-// X the float16 B operands of the four 16-query slices ([half][slice]); per slice the
-// four d-tiles' accumulators are independent, and the next slice's operands are read
-// while one runs
-__device__ __forceinline__ void unit_update(f32x16 (&acc)[4], const TrBase &tb,
-                                            const f16x8 (&x)[2][2]) {
-  f16x8 ta[2][4];  // [buffer][dt]
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) ta[0][dt] = tr_read(tb, 0, 32 * dt);
-#pragma unroll
-  for (int sl = 0; sl < 4; ++sl) {
-    if (sl < 3)
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) ta[(sl + 1) & 1][dt] = tr_read(tb, 16 * (sl + 1), 32 * dt);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-      acc[dt] = mfma_f16(ta[sl & 1][dt], x[sl >> 1][sl & 1], acc[dt]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
 // The state of one wave of a pair: its B operand rows (K for the P wave, V for the dS
 // wave), its accumulators (dV^T or dK^T) and the values it carries: the P wave P * 2^10
 // as float16 (the operand of the dV product) [half][slice]; the dS wave dP - delta in
@@ -168,7 +145,7 @@ __device__ __forceinline__ void p_first(PState &w, uint32_t st, int pair, int la
 }
 // P wave, after the barrier: dV^T += dO^T (P * 2^10)
 __device__ __forceinline__ void p_second(PState &w, uint32_t st, int lane) {
-  unit_update(w.acc, tr_base(st + kDOTile, lane), w.x);
+  tr_update(w.acc, tr_base(st + kDOTile, lane), w.x);
 }
 // dS wave, before the barrier: dP, started at -delta
 __device__ __forceinline__ void d_dp(DState &w, uint32_t st, int lane) {
@@ -185,7 +162,7 @@ __device__ __forceinline__ void d_dp(DState &w, uint32_t st, int lane) {
 }
 // dS wave: dK^T += Q^T dS with the carried dS, Q^T read from the Q tile of stage st
 __device__ __forceinline__ void d_dk(DState &w, uint32_t st, int lane) {
-  unit_update(w.acc, tr_base(st, lane), w.db);
+  tr_update(w.acc, tr_base(st, lane), w.db);
 }
 // dS wave, after the barrier: dS = P (dP - delta) in float32, rounded once to float16
 __device__ __forceinline__ void d_ds(DState &w, int pair, int lane) {

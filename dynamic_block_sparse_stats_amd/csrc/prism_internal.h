@@ -204,6 +204,29 @@ __device__ __forceinline__ f32x16 mfma_f16(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// acc[dt] (C layout: lane = column j, register -> d) += T^T[d][k] X[k][j] over the 64 rows
+// k of a row-major [64][128] float16 tile whose transposed-read base is tb; X holds the
+// float16 B operands of the four 16-row slices ([half][slice], in the row order of a C
+// tile's registers).  Per slice the four d-tiles' accumulators are independent, and the
+// next slice's operands are read while one runs.
+__device__ __forceinline__ void tr_update(f32x16 (&acc)[4], const TrBase &tb,
+                                          const f16x8 (&x)[2][2]) {
+  f16x8 ta[2][4];  // [buffer][dt]
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) ta[0][dt] = tr_read(tb, 0, 32 * dt);
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) {
+    if (sl < 3)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) ta[(sl + 1) & 1][dt] = tr_read(tb, 16 * (sl + 1), 32 * dt);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      acc[dt] = mfma_f16(ta[sl & 1][dt], x[sl >> 1][sl & 1], acc[dt]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Direct global -> LDS copies (global_load_lds): lane l of one instruction writes its
 // 16 (or 4) bytes at dst + 16 * l (4 * l); dst must be uniform across the wave and is
 // passed in M0.  They are written as inline assembly on purpose: the compiler classes the
