@@ -140,6 +140,59 @@ def test_bf16_small_backward(T, H, W, bg, seed, need256):
                   f"(bound use {ratio:.2f})", flush=True)
 
 
+def _unit_list_lengths(views, h):
+    """Per query block, the units of its selected key blocks; per key block selected by at
+    least one query block, the units of those query blocks; and the key blocks nobody
+    selected."""
+    nb = int(views["zone_block"][h, -1])  # the head's block count
+    bsz = views["block_size"][h, :nb].cpu().numpy() // 64
+    cnt = views["sel_count"][h, :nb].cpu().numpy()
+    col = views["csr_col"][h, :nb].cpu().numpy()
+    ccnt = views["csc_count"][h, :nb].cpu().numpy()
+    crow = views["csc_row"][h, :nb].cpu().numpy()
+    q_units = [int(bsz[col[i, :cnt[i]]].sum()) for i in range(nb)]
+    k_units = [int(bsz[crow[j, :ccnt[j]]].sum()) for j in range(nb) if ccnt[j] > 0]
+    return q_units, k_units, int((ccnt == 0).sum())
+
+
+def test_bf16_short_lists():
+    """Pure Top-k with k = 1, 2, 3 (Top-p off): selection lists of a few units, so the
+    unrolled unit loops of the three attention kernels end at every stage position, and
+    key blocks that no query block selected get zero dK and dV."""
+    fwd_res, kv_res, unselected = set(), set(), 0
+    for k in (1, 2, 3):
+        wl = synth.custom(8, 16, 24, 2, 128, "bf16", top_k=k, top_p=0.0, bg_amp=1.0, seed=5)
+        inp_cpu, inp = _inputs(wl, with_dout=True)
+        cfg = P.config_for(wl)
+        att = run_plan(cfg, inp)
+        o, lse = att.forward()
+        dq, dk, dv = att.backward(inp["dout"])
+        torch.cuda.synchronize()
+        views = att.views()
+        for h in range(wl.heads):
+            q_units, k_units, unsel = _unit_list_lengths(views, h)
+            fwd_res |= {u % 4 for u in q_units}
+            kv_res |= {u % 3 for u in k_units}
+            unselected += unsel
+            print(f"k={k} head {h}: query lists {sorted(set(q_units))} units, key lists "
+                  f"{sorted(set(k_units))} units, unselected key blocks {unsel}", flush=True)
+            op, exact = _check_head(wl, cfg, att, inp_cpu, h, o, lse)
+            if not exact.all():
+                print(f"k={k} head {h}: a near-threshold block differs; gradients not compared")
+                continue
+            g = oracle.attn_bwd(op, inp_cpu["q"][:, h], inp_cpu["k"][:, h],
+                                inp_cpu["v"][:, h], inp_cpu["dout"][:, h])
+            for name, gpu, ref in (("dq", dq, g[0]), ("dk", dk, g[1]), ("dv", dv, g[2])):
+                err, ratio = check_close(gpu[:, h].float().cpu().numpy(), ref, "bf16",
+                                         f"k={k} head {h} {name}")
+                print(f"k={k} head {h} {name}: max abs err {err:.3e} (bound use {ratio:.2f})",
+                      flush=True)
+    # the forward and dQ loops are unrolled by four stages, dK/dV by three
+    assert fwd_res == {0, 1, 2, 3}, fwd_res
+    assert kv_res == {0, 1, 2}, kv_res
+    assert unselected > 0
+
+
 def test_deterministic_rerun():
     """Two runs of plan, forward and backward give bit-identical results."""
     wl = synth.custom(8, 16, 24, 2, 128, "bf16", seed=9)
