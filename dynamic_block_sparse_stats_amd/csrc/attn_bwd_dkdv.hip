@@ -190,11 +190,12 @@ __device__ __forceinline__ void publish_sync() { wait_and_barrier<kLgkm0>(); }
 template <bool PW>
 __device__ __forceinline__ void dkdv_waves(
     int wave, int lane, int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
-    int ntiles, const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
-    const uint16_t *__restrict__ vp, const uint16_t *__restrict__ dop,
-    const float *__restrict__ lse2, const float *__restrict__ ndelta,
-    const int *__restrict__ unit_blk, const int *__restrict__ blk_start,
-    const int *__restrict__ blk_size, const int *__restrict__ csc_count,
+    const int *__restrict__ tile_count, int ntiles, const uint16_t *__restrict__ qp,
+    const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
+    const uint16_t *__restrict__ dop, const float *__restrict__ lse2,
+    const float *__restrict__ ndelta, const int *__restrict__ unit_blk,
+    const int *__restrict__ blk_start, const int *__restrict__ blk_size,
+    const int *__restrict__ csc_count,
     const int *__restrict__ csc_row, const int *__restrict__ perm, float scale,
     float scale_log2e, uint16_t *__restrict__ dk, uint16_t *__restrict__ dv) {
   const int l32 = lane & 31, hh = lane >> 5;
@@ -210,7 +211,13 @@ __device__ __forceinline__ void dkdv_waves(
   const bool vcopy = wave < 2;
   const float *vsrc = wave == 1 ? ndelta : lse2;
 
-  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+  // the two halves of a 256-token key block (tiles 2p and 2p + 1 of the first npaired) go
+  // to slots j and j + 8 of a group of 16, i.e. to workgroups b and b + 8, which sit on the
+  // same XCD (workgroups are dealt to the eight XCDs in turn)
+  const int npaired = __builtin_amdgcn_readfirstlane(tile_count[2]) & ~15;
+  for (int slot = blockIdx.x; slot < ntiles; slot += gridDim.x) {
+    const int j = slot & 15;
+    const int t = slot < npaired ? (slot & ~15) + 2 * (j & 7) + (j >> 3) : slot;
     const int2 tl = tiles[t];
     const int h = __builtin_amdgcn_readfirstlane(tl.x);
     const int ty = __builtin_amdgcn_readfirstlane(tl.y);
@@ -344,13 +351,13 @@ __global__ void __launch_bounds__(NW * 64)
   const int ntiles = *tile_count;
   // the two roles run the same sequence of barriers and copies
   if (wave < 4)
-    dkdv_waves<true>(wave, lane, N, U, nb_max, heads, tiles, ntiles, qp, kp, vp, dop, lse2,
-                     ndelta, unit_blk, blk_start, blk_size, csc_count, csc_row, perm, scale,
-                     scale_log2e, dk, dv);
+    dkdv_waves<true>(wave, lane, N, U, nb_max, heads, tiles, tile_count, ntiles, qp, kp, vp,
+                     dop, lse2, ndelta, unit_blk, blk_start, blk_size, csc_count, csc_row,
+                     perm, scale, scale_log2e, dk, dv);
   else
-    dkdv_waves<false>(wave, lane, N, U, nb_max, heads, tiles, ntiles, qp, kp, vp, dop, lse2,
-                      ndelta, unit_blk, blk_start, blk_size, csc_count, csc_row, perm, scale,
-                      scale_log2e, dk, dv);
+    dkdv_waves<false>(wave, lane, N, U, nb_max, heads, tiles, tile_count, ntiles, qp, kp, vp,
+                      dop, lse2, ndelta, unit_blk, blk_start, blk_size, csc_count, csc_row,
+                      perm, scale, scale_log2e, dk, dv);
 }
 
 hipError_t launch_dkdv_bf16(int work_items, hipStream_t s, int N, int U, int nb_max, int heads,

@@ -491,67 +491,82 @@ hipError_t launch_gather(const Dims &d, const void *q, const void *k, const void
 }
 
 // ============================================================================ tile lists
-// Attention work items: 128-row tiles inside blocks of 128 or 256 tokens and 64-row tiles
-// for 64-token blocks (the 64-token atomic unit of the digest's training section; 128- and
-// 256-token blocks are 2 and 4 units).  The same tiles serve as query tiles (forward, dQ)
-// and key tiles (dK/dV) because Q, K and V share one partition.  Entry (head, first unit |
-// kTile64 flag).  The order of the list changes no result, only which tiles run together.
-// Tiles in (head, zone, position) order: the persistent attention kernels take tiles
-// t, t + grid, ... so the workgroups resident at any moment work on neighbouring tiles of
-// one head and stream that head's keys in the same ascending order, sharing them in L2.
+// Attention work items.  Key tiles (dK/dV, `tiles`): 128 keys inside blocks of 128 or 256
+// tokens, 64 keys for 64-token blocks (the 64-token atomic unit of the digest's training
+// section; 128- and 256-token blocks are 2 and 4 units); entry (head, first unit | kTile64
+// flag).  Block tiles (forward, dQ, `btiles`): one query block each; entry (head, first unit
+// | units << 16).  The same partition serves queries and keys because Q, K and V share it.
+// The order of a list changes no result, only which tiles run together.
+//
+// Block tiles are in (head, zone, position) order: the persistent kernels take tiles t,
+// t + grid, ..., so the workgroups resident at any moment work on tiles of one head.  Key
+// tiles put the 256-token blocks first (four tiles per zone, so the two halves of a block
+// sit at positions 2p and 2p + 1), then the zones of smaller blocks, whose shorter tiles
+// then even out the end of the walk; counters[2] holds the number of tiles of the first
+// part.  The dK/dV kernel gives the two halves of a block (same query units, same cost) to
+// two workgroups of one XCD.
 constexpr int kTileThreads = 1024;
 
 __global__ void __launch_bounds__(kTileThreads)
     tiles_kernel(int heads, int Z, const int *__restrict__ zshape, int2 *tiles, int2 *btiles,
                  int *counters) {
-  __shared__ int scan[kTileThreads], bscan[kTileThreads];
+  __shared__ int pscan[kTileThreads], rscan[kTileThreads], bscan[kTileThreads];
   const int tid = threadIdx.x, n = heads * Z;
   const int chunk = (n + kTileThreads - 1) / kTileThreads;
   const int i0 = min(n, tid * chunk), i1 = min(n, i0 + chunk);
-  auto ntile = [&](int idx) {
-    const int code = zshape[idx];
-    return ((code >> 4) & 3) + ((code >> 2) & 3) + (code & 3) >= 7 ? 4 : 8;
-  };
   // units per block: log2 of the block volume is the sum of the log2 edges (6, 7 or 8)
   auto bunits = [&](int idx) {
     const int code = zshape[idx];
     return 1 << (((code >> 4) & 3) + ((code >> 2) & 3) + (code & 3) - 6);
   };
-  int local = 0, blocal = 0;
+  // key tiles of a zone: four of 128 keys (128- and 256-token blocks) or eight of 64
+  auto ntile = [&](int idx) { return bunits(idx) >= 2 ? 4 : 8; };
+  int plocal = 0, rlocal = 0, blocal = 0;
   for (int i = i0; i < i1; ++i) {
-    local += ntile(i);
+    if (bunits(i) == 4)
+      plocal += 4;
+    else
+      rlocal += ntile(i);
     blocal += 8 / bunits(i);
   }
-  scan[tid] = local;
+  pscan[tid] = plocal;
+  rscan[tid] = rlocal;
   bscan[tid] = blocal;
   __syncthreads();
   for (int off = 1; off < kTileThreads; off <<= 1) {
-    const int add = tid >= off ? scan[tid - off] : 0;
+    const int padd = tid >= off ? pscan[tid - off] : 0;
+    const int radd = tid >= off ? rscan[tid - off] : 0;
     const int badd = tid >= off ? bscan[tid - off] : 0;
     __syncthreads();
-    scan[tid] += add;
+    pscan[tid] += padd;
+    rscan[tid] += radd;
     bscan[tid] += badd;
     __syncthreads();
   }
-  int at = scan[tid] - local, bat = bscan[tid] - blocal;
+  const int npaired = pscan[kTileThreads - 1];
+  int pat = pscan[tid] - plocal, rat = npaired + rscan[tid] - rlocal, bat = bscan[tid] - blocal;
   for (int i = i0; i < i1; ++i) {
     const int h = i / Z, m = i % Z, nu = bunits(i);
     for (int b = 0; b < 8 / nu; ++b) btiles[bat + b] = make_int2(h, (8 * m + b * nu) | (nu << 16));
     bat += 8 / nu;
   }
   for (int i = i0; i < i1; ++i) {
-    const int h = i / Z, m = i % Z;
-    if (ntile(i) == 4) {
-      for (int s = 0; s < 4; ++s) tiles[at + s] = make_int2(h, 8 * m + 2 * s);
-      at += 4;
+    const int h = i / Z, m = i % Z, nu = bunits(i);
+    if (nu == 4) {
+      for (int s = 0; s < 4; ++s) tiles[pat + s] = make_int2(h, 8 * m + 2 * s);
+      pat += 4;
+    } else if (nu == 2) {
+      for (int s = 0; s < 4; ++s) tiles[rat + s] = make_int2(h, 8 * m + 2 * s);
+      rat += 4;
     } else {
-      for (int s = 0; s < 8; ++s) tiles[at + s] = make_int2(h, (8 * m + s) | kTile64);
-      at += 8;
+      for (int s = 0; s < 8; ++s) tiles[rat + s] = make_int2(h, (8 * m + s) | kTile64);
+      rat += 8;
     }
   }
   if (tid == kTileThreads - 1) {
-    counters[0] = scan[tid];
+    counters[0] = npaired + rscan[tid];
     counters[1] = bscan[tid];
+    counters[2] = npaired;
   }
 }
 
