@@ -62,9 +62,9 @@ class PrismError(RuntimeError):
 
 
 _lib = None
-EXPORTS = ["prism_workspace_bytes", "prism_plan_layout", "prism_plan", "prism_attn_fwd",
-           "prism_attn_bwd", "prism_a2v_norm", "prism_status_string", "prism_last_error",
-           "prism_trace_enable", "prism_trace_read", "prism_stage_name"]
+EXPORTS = ["prism_workspace_bytes", "prism_plan_layout", "prism_plan_view", "prism_plan",
+           "prism_attn_fwd", "prism_attn_bwd", "prism_a2v_norm", "prism_status_string",
+           "prism_last_error", "prism_trace_enable", "prism_trace_read", "prism_stage_name"]
 STAGES = ["audio_stats", "zone_stats", "quantize", "gather", "tiles", "scores", "select",
           "attn_fwd", "bwd_prep", "bwd_dkdv", "bwd_dq"]
 
@@ -82,7 +82,10 @@ def lib():
         L.prism_workspace_bytes.restype = ctypes.c_size_t
         L.prism_plan_layout.argtypes = [cfgp, ctypes.POINTER(PrismLayout)]
         L.prism_plan_layout.restype = ctypes.c_int
-        L.prism_plan.argtypes = [cfgp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.prism_plan_view.argtypes = [cfgp, vp, ctypes.POINTER(PrismLayout)]
+        L.prism_plan_view.restype = ctypes.c_int
+        L.prism_plan.argtypes = [cfgp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64, vp, vp,
+                                 ctypes.c_size_t, vp]
         L.prism_plan.restype = ctypes.c_int
         L.prism_attn_fwd.argtypes = [cfgp, vp, ctypes.c_size_t, vp, vp, vp]
         L.prism_attn_fwd.restype = ctypes.c_int
@@ -166,12 +169,14 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _tok(cfg, t, name, dtype=None):
+def _tok(cfg, t, name, dtype=None, strided=False):
     dtype = dtype or cfg.torch_dtype
     shape = (cfg.N, cfg.num_heads, cfg.head_dim)
-    if t.dtype != dtype or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
-        raise ValueError(f"{name}: expected contiguous {dtype} {shape} on the GPU, got "
-                         f"{t.dtype} {tuple(t.shape)} on {t.device}")
+    layout_ok = t.stride(2) == 1 and min(t.stride()) >= 0 if strided else t.is_contiguous()
+    if t.dtype != dtype or tuple(t.shape) != shape or not layout_ok or not t.is_cuda:
+        what = "unit channel stride" if strided else "contiguous"
+        raise ValueError(f"{name}: expected {what} {dtype} {shape} on the GPU, got "
+                         f"{t.dtype} {tuple(t.shape)} strides {t.stride()} on {t.device}")
 
 
 def workspace_bytes(cfg: PrismConfig) -> int:
@@ -188,13 +193,18 @@ def plan_layout(cfg: PrismConfig) -> PrismLayout:
 
 
 def plan(cfg, q, k, v, a2v, ws, stream=None):
+    """q, k, v: [N, heads, D] GPU tensors, dense or strided views with unit channel stride
+    and the same strides (e.g. slices of a fused [N, 3, heads, D] QKV projection)."""
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _tok(cfg, t, name)
+        _tok(cfg, t, name, strided=True)
+    if not (q.stride() == k.stride() == v.stride()):
+        raise ValueError("q, k, v must share their strides")
     if a2v is not None and (a2v.dtype != torch.float32 or a2v.numel() != cfg.N
                             or not a2v.is_contiguous() or not a2v.is_cuda):
         raise ValueError("a2v: expected a contiguous float32 [N] GPU tensor")
-    _check(lib().prism_plan(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(a2v), _ptr(ws),
-                            ws.numel() * ws.element_size(), _stream(stream)), "prism_plan")
+    _check(lib().prism_plan(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), q.stride(0),
+                            q.stride(1), _ptr(a2v), _ptr(ws), ws.numel() * ws.element_size(),
+                            _stream(stream)), "prism_plan")
 
 
 def attn_fwd(cfg, ws, o, lse, stream=None):

@@ -72,17 +72,16 @@ hipError_t launch_audio_stats(const Dims &d, const float *a2v, double *astat, hi
 // sums and the sum of squares, all shifted by the zone's first token to keep the variance
 // formulas well conditioned.
 template <typename T, int D>
-__global__ void __launch_bounds__(64) zone_stats_kernel(int H, int W, int heads, int nzh,
-                                                        int nzw, const T *__restrict__ v,
-                                                        int dmode, double *__restrict__ out,
-                                                        int Z) {
+__global__ void __launch_bounds__(64) zone_stats_kernel(int H, int W, int nzh, int nzw,
+                                                        const T *__restrict__ v, size_t tstride,
+                                                        size_t hstride, int dmode,
+                                                        double *__restrict__ out, int Z) {
   constexpr int CPL = D / 64;  // channels per lane
   const int m = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const int zw = m % nzw, zh = (m / nzw) % nzh, zt = m / (nzw * nzh);
   const int c0 = lane * CPL;
-  const size_t tstride = (size_t)heads * D;
   const T *base = v + ((((size_t)zt * kZone) * H + zh * kZone) * W + zw * kZone) * tstride +
-                  (size_t)h * D + c0;
+                  (size_t)h * hstride + c0;
   auto load = [&](int i, int j, int l, double *x) {
     const T *p = base + ((size_t)(i * H + j) * W + l) * tstride;
     if constexpr (sizeof(T) == 2 && CPL == 2) {
@@ -177,13 +176,14 @@ hipError_t launch_zone_stats(const Dims &d, const void *v, int dmode, double *zs
   dim3 grid(d.Z, d.heads);
   if (d.dtype == PRISM_BF16) {
     hipLaunchKernelGGL((zone_stats_kernel<uint16_t, 128>), grid, dim3(64), 0, s, d.H, d.W,
-                       d.heads, d.nzh, d.nzw, (const uint16_t *)v, dmode, zstat, d.Z);
+                       d.nzh, d.nzw, (const uint16_t *)v, d.tok_stride, d.head_stride, dmode,
+                       zstat, d.Z);
   } else if (d.D == 64) {
-    hipLaunchKernelGGL((zone_stats_kernel<float, 64>), grid, dim3(64), 0, s, d.H, d.W, d.heads,
-                       d.nzh, d.nzw, (const float *)v, dmode, zstat, d.Z);
+    hipLaunchKernelGGL((zone_stats_kernel<float, 64>), grid, dim3(64), 0, s, d.H, d.W, d.nzh,
+                       d.nzw, (const float *)v, d.tok_stride, d.head_stride, dmode, zstat, d.Z);
   } else {
-    hipLaunchKernelGGL((zone_stats_kernel<float, 128>), grid, dim3(64), 0, s, d.H, d.W, d.heads,
-                       d.nzh, d.nzw, (const float *)v, dmode, zstat, d.Z);
+    hipLaunchKernelGGL((zone_stats_kernel<float, 128>), grid, dim3(64), 0, s, d.H, d.W, d.nzh,
+                       d.nzw, (const float *)v, d.tok_stride, d.head_stride, dmode, zstat, d.Z);
   }
   return hipGetLastError();
 }
@@ -364,8 +364,8 @@ hipError_t launch_quantize(const Dims &d, const prism_config *cfg, const double 
 // selection sections).
 template <typename T, int D, bool F16>
 __global__ void __launch_bounds__(256)
-    gather_kernel(int H, int W, int heads, int nzh, int nzw, int N, int nb_max, const T *q,
-                  const T *k, const T *v, const int *__restrict__ zshape,
+    gather_kernel(int H, int W, int nzh, int nzw, int N, int nb_max, const T *q, const T *k,
+                  const T *v, size_t tstride, size_t hstride, const int *__restrict__ zshape,
                   const int *__restrict__ zblock, int *__restrict__ perm,
                   int *__restrict__ inv, T *qp, T *kp, T *vp, float *__restrict__ qbar,
                   float *__restrict__ kbar, int Z) {
@@ -401,7 +401,6 @@ __global__ void __launch_bounds__(256)
   const T *src[3] = {q, k, v};
   T *dst[3] = {qp, kp, vp};
   float *bar[2] = {qbar, kbar};
-  const size_t tstride = (size_t)heads * D;
   for (int x = 0; x < 3; ++x) {
     float acc[VPC];
 #pragma unroll
@@ -412,7 +411,7 @@ __global__ void __launch_bounds__(256)
       for (int rr = 0; rr < RPT; ++rr) {
         int p = s * kUnit + rg + RG * rr;
         buf[rr] = *reinterpret_cast<const u32x4 *>(src[x] + (size_t)tok[p] * tstride +
-                                                   (size_t)h * D + c * VPC);
+                                                   (size_t)h * hstride + c * VPC);
       }
 #pragma unroll
       for (int rr = 0; rr < RPT; ++rr) {
@@ -470,22 +469,22 @@ hipError_t launch_gather(const Dims &d, const void *q, const void *k, const void
   float *qbar = (float *)(ws + L.pub.qbar), *kbar = (float *)(ws + L.pub.kbar);
   if (d.dtype == PRISM_BF16) {
     typedef uint16_t T;
-    hipLaunchKernelGGL((gather_kernel<T, 128, true>), grid, dim3(256), 0, s, d.H, d.W, d.heads,
-                       d.nzh, d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k, (const T *)v,
-                       zshape, zblock, perm, inv, (T *)(ws + L.qp), (T *)(ws + L.kp),
-                       (T *)(ws + L.vp), qbar, kbar, d.Z);
+    hipLaunchKernelGGL((gather_kernel<T, 128, true>), grid, dim3(256), 0, s, d.H, d.W, d.nzh,
+                       d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k, (const T *)v,
+                       d.tok_stride, d.head_stride, zshape, zblock, perm, inv,
+                       (T *)(ws + L.qp), (T *)(ws + L.kp), (T *)(ws + L.vp), qbar, kbar, d.Z);
   } else if (d.D == 64) {
     typedef float T;
-    hipLaunchKernelGGL((gather_kernel<T, 64, false>), grid, dim3(256), 0, s, d.H, d.W, d.heads,
-                       d.nzh, d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k, (const T *)v,
-                       zshape, zblock, perm, inv, (T *)(ws + L.qp), (T *)(ws + L.kp),
-                       (T *)(ws + L.vp), qbar, kbar, d.Z);
+    hipLaunchKernelGGL((gather_kernel<T, 64, false>), grid, dim3(256), 0, s, d.H, d.W, d.nzh,
+                       d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k, (const T *)v,
+                       d.tok_stride, d.head_stride, zshape, zblock, perm, inv,
+                       (T *)(ws + L.qp), (T *)(ws + L.kp), (T *)(ws + L.vp), qbar, kbar, d.Z);
   } else {
     typedef float T;
-    hipLaunchKernelGGL((gather_kernel<T, 128, false>), grid, dim3(256), 0, s, d.H, d.W,
-                       d.heads, d.nzh, d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k,
-                       (const T *)v, zshape, zblock, perm, inv, (T *)(ws + L.qp),
-                       (T *)(ws + L.kp), (T *)(ws + L.vp), qbar, kbar, d.Z);
+    hipLaunchKernelGGL((gather_kernel<T, 128, false>), grid, dim3(256), 0, s, d.H, d.W, d.nzh,
+                       d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k, (const T *)v,
+                       d.tok_stride, d.head_stride, zshape, zblock, perm, inv,
+                       (T *)(ws + L.qp), (T *)(ws + L.kp), (T *)(ws + L.vp), qbar, kbar, d.Z);
   }
   return hipGetLastError();
 }

@@ -137,6 +137,8 @@ prism_status check_config(const prism_config *cfg, Dims *d, const char **why) {
   d->nzw = cfg->W / kZone;
   d->words = (d->nb_max + 31) / 32;
   d->elt = cfg->dtype == PRISM_BF16 ? 2 : 4;
+  d->tok_stride = (size_t)cfg->num_heads * cfg->head_dim;
+  d->head_stride = (size_t)cfg->head_dim;
   return PRISM_OK;
 }
 
@@ -239,14 +241,29 @@ prism_status prism_plan_layout(const prism_config *cfg, prism_layout *out) {
   return PRISM_OK;
 }
 
+prism_status prism_plan_view(const prism_config *cfg, const void *workspace,
+                             prism_layout *out) {
+  if (!workspace) return fail(PRISM_ERR_ARG, "null workspace");
+  return prism_plan_layout(cfg, out);
+}
+
 prism_status prism_plan(const prism_config *cfg, const void *q, const void *k, const void *v,
-                        const float *a2v_norm, void *workspace, size_t workspace_bytes,
-                        void *stream) {
+                        int64_t tok_stride, int64_t head_stride, const float *a2v_norm,
+                        void *workspace, size_t workspace_bytes, void *stream) {
   Dims d;
   const char *why;
   prism_status st = check_config(cfg, &d, &why);
   if (st != PRISM_OK) return fail(st, why);
   if (!q || !k || !v || !workspace) return fail(PRISM_ERR_ARG, "null tensor or workspace");
+  if (tok_stride < 0 || head_stride < 0)
+    return fail(PRISM_ERR_ARG, "strides must be non-negative (0 selects the dense layout)");
+  if (tok_stride) d.tok_stride = (size_t)tok_stride;
+  if (head_stride) d.head_stride = (size_t)head_stride;
+  // the gather reads 16-byte pieces of every row
+  if ((d.tok_stride * d.elt) % 16 || (d.head_stride * d.elt) % 16 ||
+      ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) % 16)
+    return fail(PRISM_ERR_ARG, "q, k, v must be 16-byte aligned and their strides multiples "
+                               "of 16 bytes");
   Layout L = make_layout(d);
   if (workspace_bytes < L.total) return fail(PRISM_ERR_WORKSPACE, "workspace too small");
   hipStream_t s = (hipStream_t)stream;

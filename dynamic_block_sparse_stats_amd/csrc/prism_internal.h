@@ -42,6 +42,9 @@ struct Dims {
   int nzt, nzh, nzw;     // zones per axis
   int words;             // 32-bit words per selection bitmask row
   size_t elt;            // bytes per token-tensor element
+  // element strides of the q, k, v inputs of prism_plan: (token n, head h, channel c) at
+  // n * tok_stride + h * head_stride + c (dense [N][heads][D] by default)
+  size_t tok_stride, head_stride;
 };
 
 // Internal workspace layout: the public arrays of prism_layout plus scratch.

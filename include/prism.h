@@ -117,14 +117,24 @@ size_t prism_workspace_bytes(const prism_config *cfg);
  * rejected configuration. */
 prism_status prism_plan_layout(const prism_config *cfg, prism_layout *out);
 
+/* The same, for a planned workspace: *out holds byte offsets into workspace of the plan's
+ * arrays (zone shapes, permutation, block table, CSR and CSC lists, ...), for viewing
+ * them.  PRISM_ERR_ARG on a null workspace or output. */
+prism_status prism_plan_view(const prism_config *cfg, const void *workspace,
+                             prism_layout *out);
+
 /* Plans every head: zone statistics of V and of the A2V norm field, shapes, permutation,
  * permuted copies of Q, K, V, block means, block scores and the Top-k union Top-p
- * selection (steps 1-4 above).  q, k, v: [N][heads][D]; a2v_norm: [N] float32, or NULL
- * for a layer with no cached A2V norm (the first layer: video guidance only).  The plan
- * is written into workspace, which must stay untouched until the last fwd/bwd using it. */
+ * selection (steps 1-4 above).  q, k, v: element (token n, head h, channel c) at
+ * n * tok_stride + h * head_stride + c, in elements, the same strides for the three (0
+ * selects the dense [N][heads][D] value: heads * D, respectively D), so q, k, v may be
+ * views into a fused QKV projection; they must be 16-byte aligned and the strides
+ * multiples of 16 bytes (PRISM_ERR_ARG otherwise).  a2v_norm: [N] float32, or NULL for a
+ * layer with no cached A2V norm (the first layer: video guidance only).  The plan is
+ * written into workspace, which must stay untouched until the last fwd/bwd using it. */
 prism_status prism_plan(const prism_config *cfg, const void *q, const void *k, const void *v,
-                        const float *a2v_norm, void *workspace, size_t workspace_bytes,
-                        void *stream);
+                        int64_t tok_stride, int64_t head_stride, const float *a2v_norm,
+                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* Sparse attention forward over the plan in workspace (step 5): o [N][heads][D] in token
  * order, lse [heads][N] float32 (natural-log sum of exp of the scaled logits).  Also keeps

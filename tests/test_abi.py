@@ -64,7 +64,7 @@ def test_rejected_configs(lib, over, code):
     assert lib.prism_plan_layout(ctypes.byref(cfg), ctypes.byref(out)) == code
     # the same check runs first in every entry point: nothing is launched
     dummy = ctypes.c_void_p(16)
-    assert lib.prism_plan(ctypes.byref(cfg), dummy, dummy, dummy, None, dummy, 1 << 40,
+    assert lib.prism_plan(ctypes.byref(cfg), dummy, dummy, dummy, 0, 0, None, dummy, 1 << 40,
                           None) == code
     assert lib.prism_attn_fwd(ctypes.byref(cfg), dummy, 1 << 40, dummy, dummy, None) == code
     assert lib.prism_last_error().decode() != ""
@@ -73,13 +73,34 @@ def test_rejected_configs(lib, over, code):
 def test_null_and_small_workspace(lib):
     cfg = P.make_config(8, 16, 16, 2, 128, "bf16")
     d = ctypes.c_void_p(256)
-    assert lib.prism_plan(ctypes.byref(cfg), None, d, d, None, d, 1 << 40, None) == -1
+    assert lib.prism_plan(ctypes.byref(cfg), None, d, d, 0, 0, None, d, 1 << 40, None) == -1
     need = lib.prism_workspace_bytes(ctypes.byref(cfg))
-    assert lib.prism_plan(ctypes.byref(cfg), d, d, d, None, d, need - 1, None) == -3
+    assert lib.prism_plan(ctypes.byref(cfg), d, d, d, 0, 0, None, d, need - 1, None) == -3
     assert lib.prism_attn_fwd(ctypes.byref(cfg), d, need - 1, d, d, None) == -3
     assert lib.prism_attn_bwd(ctypes.byref(cfg), d, need, d, d, None, d, None) == -1
     assert lib.prism_attn_bwd(ctypes.byref(cfg), d, need - 1, d, d, d, d, None) == -3
     assert lib.prism_status_string(-3) == b"workspace too small"
+
+
+def test_plan_rejects_bad_strides(lib):
+    cfg = P.make_config(8, 16, 16, 2, 128, "bf16")
+    d = ctypes.c_void_p(256)
+    need = lib.prism_workspace_bytes(ctypes.byref(cfg))
+    for tok, head in ((-256, 0), (0, -1), (2 * 128 + 4, 128), (3 * 2 * 128, 132)):
+        # negative, or a row not starting on a 16-byte boundary (bf16: 8 elements)
+        assert lib.prism_plan(ctypes.byref(cfg), d, d, d, tok, head, None, d, need,
+                              None) == -1, (tok, head)
+    assert lib.prism_plan(ctypes.byref(cfg), ctypes.c_void_p(264), d, d, 0, 0, None, d, need,
+                          None) == -1  # q not 16-byte aligned
+
+
+def test_plan_view_matches_layout(lib):
+    cfg = P.make_config(8, 16, 16, 2, 128, "bf16")
+    a, b = P.PrismLayout(), P.PrismLayout()
+    assert lib.prism_plan_layout(ctypes.byref(cfg), ctypes.byref(a)) == 0
+    assert lib.prism_plan_view(ctypes.byref(cfg), ctypes.c_void_p(256), ctypes.byref(b)) == 0
+    assert bytes(a) == bytes(b)
+    assert lib.prism_plan_view(ctypes.byref(cfg), None, ctypes.byref(b)) == -1
 
 
 def test_accepted_ablation_configs(lib):
