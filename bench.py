@@ -157,9 +157,67 @@ def time_dense_own(P, wl, inp, heads, backward, steps=2):
     return min(ts)
 
 
-def cpu_baseline(wl, cfg, inp, budget_s):
+def plan_agreement(views, op, h, top_p):
+    """Head h of the timed step against the oracle's plan of the same head: zone shapes
+    (zones whose tier or shape decision margin is below 1e-9 are near-ties, where either
+    answer is correct), then the selection lists row by row.  A differing key block is
+    near-threshold when its logit lies within 1e-5 of the row's cut logit or the Top-p mass
+    before it within 1e-5 of p.  Returns the counts and the mask of rows that matched."""
+    gshape = views["zone_shape"][h].cpu().numpy()
+    near = (op.zone_diag[:, 9] < 1e-9) | (op.zone_diag[:, 10] < 1e-9)
+    diff = gshape != op.shape
+    rep = {"head": h, "zones": int(len(gshape)), "near_tie_zones": int(near.sum()),
+           "zones_differing": int(diff.sum()),
+           "zones_differing_not_near_tie": int((diff & ~near).sum())}
+    if diff.any():
+        return rep, None
+    nb = op.nb
+    rep["perm_equal"] = bool(np.array_equal(views["perm"][h].cpu().numpy(), op.perm))
+    cnt = views["sel_count"][h, :nb].cpu().numpy()
+    cols = views["csr_col"][h, :nb, :nb].cpu().numpy()
+    exact = np.zeros(nb, dtype=bool)
+    near_blk = far_blk = 0
+    for i in range(nb):
+        g = cols[i, :cnt[i]]
+        o_ = op.cols[i, :op.count[i]]
+        if cnt[i] == op.count[i] and np.array_equal(g, o_):
+            exact[i] = True
+            continue
+        order = np.lexsort((np.arange(nb), -op.P[i]))
+        pos = np.empty(nb, dtype=np.int64)
+        pos[order] = np.arange(nb)
+        cum = np.concatenate([[0.0], np.cumsum(op.P[i][order])])
+        s_cut = op.s[i, order[op.count[i] - 1]]
+        for j in np.setxor1d(g, o_):
+            if abs(op.s[i, j] - s_cut) <= 1e-5 or abs(cum[pos[j]] - top_p) <= 1e-5:
+                near_blk += 1
+            else:
+                far_blk += 1
+    rep.update({"blocks": nb, "rows_exact": int(exact.sum()),
+                "excluded_near_threshold_blocks": near_blk, "differing_other_blocks": far_blk})
+    return rep, exact
+
+
+def sample_error(got, ref, mag):
+    """Max-abs error of bfloat16 results against the float64 oracle, and the largest share
+    used of the bound 2e-2 + one bfloat16 ulp of the reference value + 2^-11 (the float16
+    unit roundoff) times the oracle's first-order size of the result's change under a
+    relative perturbation of the attention weights and dS, which the kernels feed to the
+    MFMA as float16; also the share of the bound without that last term."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    base = 2e-2 + 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+    return (float(err.max()), float((err / (base + 2.0 ** -11 * mag)).max()),
+            float((err / base).max()))
+
+
+def cpu_baseline(wl, cfg, inp, budget_s, views=None, outputs=None):
     """The CPU oracle as it stands on a bounded sample of the workload: the full plan of
-    head 0, then the forward and backward of a seeded sample of head-0 query rows."""
+    head 0, then the forward and backward of a seeded sample of head-0 query rows.  With
+    the timed step's plan views and outputs, also reports how the two agree on that head
+    (plan counts, and the sampled output and dQ rows of query blocks whose selection
+    matched)."""
     import oracle
     h = 0
     # exact float64 copies of the bits the GPU read
@@ -192,6 +250,16 @@ def cpu_baseline(wl, cfg, inp, budget_s):
     oracle.attn_fwd(op, q, k, v, rows=rows)
     t_fwd = time.perf_counter() - t0
     flops = 4.0 * wl.head_dim * keys_tok[rows].sum()
+    agree, exact_blk = (plan_agreement(views, op, h, cfg.top_p) if views is not None
+                        else (None, None))
+    ok = exact_blk[tok_blk[rows]] if exact_blk is not None else None
+    bf16 = wl.dtype == "bf16"
+    if ok is not None and outputs is not None and ok.any() and bf16:
+        o_ref, _, mo = oracle.attn_fwd(op, q, k, v, rows=rows[ok], with_mag=True)
+        r_ = rows[ok]
+        e, r, r0 = sample_error(outputs["o"][r_, h].float().cpu().numpy(), o_ref[r_], mo[r_])
+        agree.update({"o_rows": int(ok.sum()), "o_max_err": e, "o_bound_use": round(r, 3),
+                      "o_use_without_operand_term": round(r0, 3)})
     t_bwd, nb_rows = 0.0, 0
     if do is not None:
         dsp = np.zeros((wl.N, wl.head_dim))
@@ -207,6 +275,16 @@ def cpu_baseline(wl, cfg, inp, budget_s):
         oracle.attn_bwd(op, q, k, v, dsp, rows=brow)
         t_bwd = time.perf_counter() - t0
         flops += 10.0 * wl.head_dim * keys_tok[brow].sum()
+        okb = exact_blk[tok_blk[brow]] if exact_blk is not None else None
+        if okb is not None and outputs is not None and "dq" in outputs and okb.any() and bf16:
+            # dq of row x depends on the upstream gradient of row x only
+            b_ = brow[okb]
+            dq_ref, _, _, mq, _, _ = oracle.attn_bwd(op, q, k, v, dsp, rows=b_, with_mag=True)
+            e, r, r0 = sample_error(outputs["dq"][b_, h].float().cpu().numpy(), dq_ref[b_],
+                                    mq[b_])
+            agree.update({"dq_rows": int(okb.sum()), "dq_max_err": e,
+                          "dq_bound_use": round(r, 3),
+                          "dq_use_without_operand_term": round(r0, 3)})
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {
         "value": flops / (t_fwd + t_bwd) / 1e12, "unit": "TFLOP/s", "cores": cores,
@@ -215,6 +293,7 @@ def cpu_baseline(wl, cfg, inp, budget_s):
                    f"seeded query rows in {t_fwd:.1f} s ({cores} OpenMP threads); backward of "
                    f"{nb_rows} of those rows in {t_bwd:.1f} s (single thread); float64"),
         "plan_s_per_head": t_plan,
+        "agreement": agree,
     }
 
 
@@ -258,11 +337,13 @@ def main():
     cfg = P.config_for(wl, **over)
     att = P.PrismAttention(cfg)
 
+    last = {}
+
     def step():
         att.plan(inp["q"], inp["k"], inp["v"], inp["a2v"])
-        att.forward()
+        last["o"], _ = att.forward()
         if backward:
-            att.backward(inp["dout"])
+            last["dq"], _, _ = att.backward(inp["dout"])
 
     for i in range(args.warmup):
         step()
@@ -294,6 +375,26 @@ def main():
     flop_bwd = 10.0 * D * tot_pairs if backward else 0.0
     eff = flop_fwd + flop_bwd
     density = [p / float(N) ** 2 for p in pairs]
+    cnts = torch.cat([views["sel_count"][h, :nb].long() for h, nb in
+                      enumerate(int(views["zone_block"][h, -1]) for h in range(Hh))])
+    selection = {"nnz": int(cnts.sum()), "blocks": int(cnts.numel()),
+                 "selected_per_row_min_median_max": [int(cnts.min()),
+                                                     int(cnts.median()), int(cnts.max())],
+                 "density_per_head": [round(x, 4) for x in density]}
+    # the HBM-bound planning and preparation kernels: algorithmic bytes per launch over
+    # the launch time (tokens x heads x bytes per token-head)
+    th = float(N) * Hh
+    eb = 2.0 if wl.dtype == "bf16" else 4.0
+    hbm_bytes = {"zone_stats": th * D * eb,                       # read V
+                 "gather": th * (6 * D * eb + 8),                 # Q, K, V in and out,
+                                                                  #   perm and inverse out
+                 "bwd_prep": th * (2 * D * eb + 4 * D + 16)}      # dO in + out, O (f32),
+    plan_hbm = {}                                                 #   lse in, delta, lse2 out
+    for s_, b in hbm_bytes.items():
+        if stage_ms.get(s_, 0) > 0 and (s_ != "bwd_prep" or backward):
+            gbs = b / (stage_ms[s_] * 1e-3) / 1e9
+            plan_hbm[s_] = {"GB": round(b / 1e9, 2), "GB/s": round(gbs, 1),
+                            "frac": round(gbs / PEAK_HBM_GBS, 3)}
     zs = views["zone_shape"][:, :].cpu().numpy()
     vol = 2 ** (((zs >> 4) & 3) + ((zs >> 2) & 3) + (zs & 3))
     nbs = [int(views["zone_block"][h, -1]) for h in range(Hh)]
@@ -363,7 +464,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         try:
-            cpu = cpu_baseline(wl, cfg, inp, args.cpu_seconds)
+            cpu = cpu_baseline(wl, cfg, inp, args.cpu_seconds, views, last)
         except Exception as e:  # noqa: BLE001
             cpu = {"error": repr(e)[:300]}
 
@@ -390,6 +491,8 @@ def main():
         "density_mean": round(float(np.mean(density)), 4),
         "density_min_max": [round(min(density), 4), round(max(density), 4)],
         "blocks_per_head_mean": round(float(np.mean(nbs)), 1),
+        "selection": selection,
+        "hbm_kernels": plan_hbm,
         "zones_B64_B128_B256": [int((vol == 64).sum()), int((vol == 128).sum()),
                                 int((vol == 256).sum())],
         "dense": dense,

@@ -19,6 +19,9 @@ Parity status of each function (what pins it; see tests/test_oracle_pins.py):
   attn_fwd                 -- Top-k = all equals textbook dense attention; any plan equals
                               dense attention under the plan's block mask
   attn_bwd                 -- central finite differences of attn_fwd
+  with_mag outputs         -- bound the change of o, dq, dk, dv under relative
+                              perturbations of the weights and dS (dense masked
+                              formulation, random and worst-case signs; tight for o, dv)
   row_norms                -- closed forms (unit vectors, constant rows, Pythagorean rows)
 """
 from __future__ import annotations
@@ -243,8 +246,10 @@ def plan_head(T, H, W, q, k, v, a=None, top_k=8, top_p=0.9, tau128=0.5, tau256=0
                     cols, sd)
 
 
-def attn_fwd(plan: HeadPlan, q, k, v, scale=None, rows=None):
-    """o [N, D], lse [N] (only listed rows are written when rows is given)."""
+def attn_fwd(plan: HeadPlan, q, k, v, scale=None, rows=None, with_mag=False):
+    """o [N, D], lse [N] (only listed rows are written when rows is given); with_mag also
+    returns mo [N, D], the first-order size of the change in o under a relative
+    perturbation of at most 1 of every attention weight (see orc_attn_fwd)."""
     lib = _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     N, D = q.shape
@@ -252,21 +257,26 @@ def attn_fwd(plan: HeadPlan, q, k, v, scale=None, rows=None):
         scale = 1.0 / np.sqrt(D)
     o = np.zeros((N, D))
     lse = np.full(N, np.nan)
+    mo = np.zeros((N, D)) if with_mag else None
     lib.orc_attn_fwd.argtypes = [ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 8 + [
         ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p,
-        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     rws = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
     lib.orc_attn_fwd(N, D, q.ctypes.data, k.ctypes.data, v.ctypes.data, plan.perm.ctypes.data,
                      plan.inv.ctypes.data, plan.bstart.ctypes.data, plan.bsize.ctypes.data,
                      plan.bof.ctypes.data, plan.nb, plan.count.ctypes.data,
                      plan.cols.ctypes.data, float(scale),
                      None if rws is None else rws.ctypes.data,
-                     0 if rws is None else len(rws), o.ctypes.data, lse.ctypes.data)
-    return o, lse
+                     0 if rws is None else len(rws), o.ctypes.data, lse.ctypes.data,
+                     None if mo is None else mo.ctypes.data)
+    return (o, lse, mo) if with_mag else (o, lse)
 
 
-def attn_bwd(plan: HeadPlan, q, k, v, dout, scale=None, rows=None):
-    """dq, dk, dv [N, D]; with rows given, only those query tokens' terms are summed."""
+def attn_bwd(plan: HeadPlan, q, k, v, dout, scale=None, rows=None, with_mag=False):
+    """dq, dk, dv [N, D]; with rows given, only those query tokens' terms are summed.
+    with_mag also returns mq, mk, mv [N, D]: the first-order size of the change in each
+    gradient under a relative perturbation of at most 1 of every attention weight and
+    every dS (see orc_attn_bwd)."""
     lib = _load()
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     N, D = q.shape
@@ -275,9 +285,10 @@ def attn_bwd(plan: HeadPlan, q, k, v, dout, scale=None, rows=None):
     dq = np.zeros((N, D))
     dk = np.zeros((N, D))
     dv = np.zeros((N, D))
+    mags = [np.zeros((N, D)) for _ in range(3)] if with_mag else [None] * 3
     lib.orc_attn_bwd.argtypes = [ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 9 + [
         ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p,
-        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        ctypes.c_int] + [ctypes.c_void_p] * 6
     rws = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
     lib.orc_attn_bwd(N, D, q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
                      plan.perm.ctypes.data, plan.inv.ctypes.data, plan.bstart.ctypes.data,
@@ -285,8 +296,8 @@ def attn_bwd(plan: HeadPlan, q, k, v, dout, scale=None, rows=None):
                      plan.count.ctypes.data, plan.cols.ctypes.data, float(scale),
                      None if rws is None else rws.ctypes.data,
                      0 if rws is None else len(rws), dq.ctypes.data, dk.ctypes.data,
-                     dv.ctypes.data)
-    return dq, dk, dv
+                     dv.ctypes.data, *[None if m is None else m.ctypes.data for m in mags])
+    return (dq, dk, dv, *mags) if with_mag else (dq, dk, dv)
 
 
 def row_norms(x, rows=None):

@@ -441,11 +441,15 @@ static int key_tokens(int x, const int *perm, const int *inv, const int *blk_sta
  * implied by indexing by token).  No causal mask.
  *   q, k, v [N][D]; rows [nrows] (token indices) or NULL for all N;
  *   o [N][D], lse [N]: written for the listed rows only.
+ *   mo [N][D] or NULL: sum_y P_xy |v_y - o_x| per channel, the size of the change in o_x
+ *   when every weight P_xy is perturbed by a relative amount of at most 1 and the
+ *   weights are renormalised (first order); a tolerance for an implementation that rounds
+ *   the weights scales it by that rounding's unit roundoff.
  * ---------------------------------------------------------------------------------- */
 int orc_attn_fwd(int N, int D, const double *q, const double *k, const double *v,
                  const int *perm, const int *inv, const int *blk_start, const int *blk_size,
                  const int *blk_of, int nb, const int *count, const int *cols, double scale,
-                 const int *rows, int nrows, double *o, double *lse)
+                 const int *rows, int nrows, double *o, double *lse, double *mo)
 {
     int total = rows ? nrows : N;
 #pragma omp parallel
@@ -472,6 +476,15 @@ int orc_attn_fwd(int N, int D, const double *q, const double *k, const double *v
                 double p = exp(s[y] - l);
                 for (int c = 0; c < D; ++c) o[(size_t)x * D + c] += p * v[(size_t)keys[y] * D + c];
             }
+            if (mo) {
+                double *m = mo + (size_t)x * D;
+                const double *ox = o + (size_t)x * D;
+                for (int c = 0; c < D; ++c) m[c] = 0;
+                for (int y = 0; y < nk; ++y) {
+                    double p = exp(s[y] - l);
+                    for (int c = 0; c < D; ++c) m[c] += p * fabs(v[(size_t)keys[y] * D + c] - ox[c]);
+                }
+            }
         }
         free(keys);
         free(s);
@@ -489,20 +502,35 @@ int orc_attn_fwd(int N, int D, const double *q, const double *k, const double *v
  * o and lse are recomputed here in float64.  rows: the query tokens whose terms are
  * summed (NULL = all); with an upstream gradient that is zero on every other token this
  * is the full gradient.  dq, dk, dv [N][D] are overwritten (dq only on the listed rows).
+ *
+ * mq, mk, mv [N][D] (all three or none): how far each gradient moves, to first order,
+ * when every weight P_xy and every dS_xy is perturbed by a relative amount of at most 1
+ * (a tolerance for an implementation that rounds them scales this by that rounding's
+ * unit roundoff).  With S_x = sum_y |dS_xy|, the bound on the change of delta_x that the
+ * weights' perturbation causes through o_x:
+ *   mv_y = sum_x P_xy |do_x|,
+ *   mq_x = scale sum_y (|dS_xy| + P_xy S_x) |k_y|,
+ *   mk_y = scale sum_x (|dS_xy| + P_xy S_x) |q_x|   (per channel).
  * ---------------------------------------------------------------------------------- */
 int orc_attn_bwd(int N, int D, const double *q, const double *k, const double *v,
                  const double *dout, const int *perm, const int *inv, const int *blk_start,
                  const int *blk_size, const int *blk_of, int nb, const int *count,
                  const int *cols, double scale, const int *rows, int nrows, double *dq,
-                 double *dk, double *dv)
+                 double *dk, double *dv, double *mq, double *mk, double *mv)
 {
     int total = rows ? nrows : N;
     int *keys = malloc(sizeof(int) * (size_t)N);
     double *s = malloc(sizeof(double) * (size_t)N);
+    double *dsv = malloc(sizeof(double) * (size_t)N);
     double *o = malloc(sizeof(double) * (size_t)D);
     memset(dq, 0, sizeof(double) * (size_t)N * D);
     memset(dk, 0, sizeof(double) * (size_t)N * D);
     memset(dv, 0, sizeof(double) * (size_t)N * D);
+    if (mq) {
+        memset(mq, 0, sizeof(double) * (size_t)N * D);
+        memset(mk, 0, sizeof(double) * (size_t)N * D);
+        memset(mv, 0, sizeof(double) * (size_t)N * D);
+    }
     for (int r = 0; r < total; ++r) {
         int x = rows ? rows[r] : r;
         const double *qx = q + (size_t)x * D, *dox = dout + (size_t)x * D;
@@ -524,21 +552,37 @@ int orc_attn_bwd(int N, int D, const double *q, const double *k, const double *v
         }
         double delta = 0;
         for (int c = 0; c < D; ++c) delta += dox[c] * o[c];
+        double sabs = 0;
         for (int y = 0; y < nk; ++y) {
-            const double *ky = k + (size_t)keys[y] * D, *vy = v + (size_t)keys[y] * D;
+            const double *vy = v + (size_t)keys[y] * D;
             double p = exp(s[y] - l);
             double dp = 0;
             for (int c = 0; c < D; ++c) dp += dox[c] * vy[c];
-            double ds = p * (dp - delta);
+            dsv[y] = p * (dp - delta);
+            sabs += fabs(dsv[y]);
+        }
+        for (int y = 0; y < nk; ++y) {
+            const double *ky = k + (size_t)keys[y] * D;
+            double p = exp(s[y] - l);
+            double ds = dsv[y];
             for (int c = 0; c < D; ++c) {
                 dv[(size_t)keys[y] * D + c] += p * dox[c];
                 dq[(size_t)x * D + c] += scale * ds * ky[c];
                 dk[(size_t)keys[y] * D + c] += scale * ds * qx[c];
             }
+            if (mq) {
+                double w = scale * (fabs(ds) + p * sabs);
+                for (int c = 0; c < D; ++c) {
+                    mv[(size_t)keys[y] * D + c] += p * fabs(dox[c]);
+                    mq[(size_t)x * D + c] += w * fabs(ky[c]);
+                    mk[(size_t)keys[y] * D + c] += w * fabs(qx[c]);
+                }
+            }
         }
     }
     free(keys);
     free(s);
+    free(dsv);
     free(o);
     return 0;
 }

@@ -3,8 +3,10 @@ inputs.  Plans: zone shapes, permutations, block tables bit-exact (zones whose t
 decision margin is below 1e-9 are counted and excluded); selections bit-exact as sets except
 key blocks whose logit lies within 1e-5 of the row's cut logit or whose inclusion by Top-p
 depends on a cumulative mass within 1e-5 of p (counted).  Attention outputs and gradients
-within max-abs 1e-4 (float32) or 2e-2 plus one bfloat16 ulp of the reference value
-(bfloat16) on rows whose selection matched."""
+within max-abs 1e-4 (float32) or, for bfloat16, 2e-2 plus one bfloat16 ulp of the
+reference value plus the float16 unit roundoff times the oracle's first-order size of the
+result's change under a relative perturbation of its attention weights and dS (the float16
+MFMA operands), on rows whose selection matched."""
 from __future__ import annotations
 
 import numpy as np
@@ -22,14 +24,23 @@ def ulp_bf16(x):
     return 2.0 ** (np.floor(np.log2(ax)) - 7)
 
 
-def check_close(got, ref, dtype, what=""):
+U16 = 2.0 ** -11   # unit roundoff of float16 (round to nearest even)
+
+
+def check_close(got, ref, dtype, what="", mag=None):
     """float32: max-abs <= 1e-4.  bfloat16: |got - ref| <= 2e-2 + one bf16 ulp of ref (the
     stored result cannot be closer to the exact value than its own rounding step, which
-    exceeds 2e-2 once |ref| >= 8).  Returns (max abs error, max error / bound)."""
+    exceeds 2e-2 once |ref| >= 8) + U16 * mag, where mag is the oracle's first-order size of
+    the result's change when each attention weight and each dS moves by a relative amount
+    of at most 1 (the HIP path feeds both to the MFMA as float16; at unit-variance inputs
+    this term is far below 2e-2, in rows dominated by a few large logits it is not).
+    Returns (max abs error, max error / bound)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     err = np.abs(got - ref)
     bound = TOL[dtype] + (ulp_bf16(ref) if dtype == "bf16" else 0.0)
+    if dtype == "bf16" and mag is not None:
+        bound = bound + U16 * np.asarray(mag, dtype=np.float64)
     ratio = float((err / bound).max()) if err.size else 0.0
     worst = np.unravel_index(int(np.argmax(err / bound)), err.shape) if err.size else ()
     assert ratio <= 1.0, (f"{what}: error {err[worst]:.3e} at {worst} exceeds bound "

@@ -45,8 +45,9 @@ def test_fullsize(cid):
         exact, excl, nnz = compare_selection(views, h, op, wl.top_p)
         ok_rows = np.nonzero(rows_of_exact_blocks(op, exact))[0]
         rows = np.sort(rng.choice(ok_rows, size=64, replace=False))
-        oo, ol = oracle.attn_fwd(op, hi["q"], hi["k"], hi["v"], rows=rows)
-        e_o, r_o = check_close(o[rows, h].float().cpu().numpy(), oo[rows], "bf16", f"h{h} O")
+        oo, ol, mo = oracle.attn_fwd(op, hi["q"], hi["k"], hi["v"], rows=rows, with_mag=True)
+        e_o, r_o = check_close(o[rows, h].float().cpu().numpy(), oo[rows], "bf16", f"h{h} O",
+                               mo[rows])
         e_l, r_l = check_close(lse[h, rows].cpu().numpy(), ol[rows], "bf16", f"h{h} lse")
         print(f"   head {h}: nb {op.nb} nnz {nnz} excluded {excl} near-tie zones "
               f"{rep['near_tie_zones']} | O err {e_o:.2e} (bound use {r_o:.2f}) "
@@ -71,10 +72,12 @@ def test_fullsize(cid):
         op, hi, _ = samples[h]
         br = brows[h]
         d_np = dout[:, h].double().cpu().numpy()
-        rq, rk, rv = oracle.attn_bwd(op, hi["q"], hi["k"], hi["v"], d_np, rows=br)
-        e_q, _ = check_close(dq[:, h].float().cpu().numpy(), rq, "bf16", f"h{h} dq")
-        e_k, _ = check_close(dk[:, h].float().cpu().numpy(), rk, "bf16", f"h{h} dk")
-        e_v, _ = check_close(dv[:, h].float().cpu().numpy(), rv, "bf16", f"h{h} dv")
+        rq, rk, rv, mq, mk, mv = oracle.attn_bwd(op, hi["q"], hi["k"], hi["v"], d_np, rows=br,
+                                                 with_mag=True)
+        e_q, u_q = check_close(dq[:, h].float().cpu().numpy(), rq, "bf16", f"h{h} dq", mq)
+        e_k, u_k = check_close(dk[:, h].float().cpu().numpy(), rk, "bf16", f"h{h} dk", mk)
+        e_v, u_v = check_close(dv[:, h].float().cpu().numpy(), rv, "bf16", f"h{h} dv", mv)
         nz = int((np.abs(rv).sum(1) > 0).sum())
-        print(f"   head {h}: dq err {e_q:.2e} dk err {e_k:.2e} dv err {e_v:.2e} "
+        print(f"   head {h}: dq err {e_q:.2e} ({u_q:.2f} of bound) dk err {e_k:.2e} "
+              f"({u_k:.2f}) dv err {e_v:.2e} ({u_v:.2f}) "
               f"({nz} key rows with nonzero gradient)", flush=True)

@@ -27,11 +27,12 @@ def _check_head(wl, cfg, att, inp_cpu, h, o, lse, a2v=True, **over):
     assert not rep.get("downstream_skipped"), rep
     exact, excl, nnz = compare_selection(views, h, op, cfg.top_p, to_np(views["scores"])
                                          if h == cfg.num_heads - 1 else None)
-    oo, ol = oracle.attn_fwd(op, inp_cpu["q"][:, h], inp_cpu["k"][:, h], inp_cpu["v"][:, h])
+    oo, ol, mo = oracle.attn_fwd(op, inp_cpu["q"][:, h], inp_cpu["k"][:, h],
+                                 inp_cpu["v"][:, h], with_mag=True)
     rows = rows_of_exact_blocks(op, exact)
     go = o[:, h].float().cpu().numpy()
     gl = lse[h].cpu().numpy()
-    err_o, r_o = check_close(go[rows], oo[rows], wl.dtype, f"head {h} O")
+    err_o, r_o = check_close(go[rows], oo[rows], wl.dtype, f"head {h} O", mo[rows])
     err_l, r_l = check_close(gl[rows], ol[rows], "f32" if wl.dtype == "f32" else "bf16",
                              f"head {h} lse")
     print(f"head {h}: nb {op.nb} nnz {nnz} excluded {excl} near-tie zones "
@@ -132,10 +133,11 @@ def test_bf16_small_backward(T, H, W, bg, seed, need256):
         if not exact.all():
             pytest.skip("selection differs at a near-threshold block; gradient rows excluded")
         g = oracle.attn_bwd(op, inp_cpu["q"][:, h], inp_cpu["k"][:, h], inp_cpu["v"][:, h],
-                            inp_cpu["dout"][:, h])
-        for name, gpu, ref in (("dq", dq, g[0]), ("dk", dk, g[1]), ("dv", dv, g[2])):
+                            inp_cpu["dout"][:, h], with_mag=True)
+        for name, gpu, ref, mag in (("dq", dq, g[0], g[3]), ("dk", dk, g[1], g[4]),
+                                    ("dv", dv, g[2], g[5])):
             err, ratio = check_close(gpu[:, h].float().cpu().numpy(), ref, "bf16",
-                                     f"head {h} {name}")
+                                     f"head {h} {name}", mag)
             print(f"head {h} {name}: max|ref| {np.abs(ref).max():.2f} max abs err {err:.3e} "
                   f"(bound use {ratio:.2f})", flush=True)
 
@@ -181,10 +183,11 @@ def test_bf16_short_lists():
                 print(f"k={k} head {h}: a near-threshold block differs; gradients not compared")
                 continue
             g = oracle.attn_bwd(op, inp_cpu["q"][:, h], inp_cpu["k"][:, h],
-                                inp_cpu["v"][:, h], inp_cpu["dout"][:, h])
-            for name, gpu, ref in (("dq", dq, g[0]), ("dk", dk, g[1]), ("dv", dv, g[2])):
+                                inp_cpu["v"][:, h], inp_cpu["dout"][:, h], with_mag=True)
+            for name, gpu, ref, mag in (("dq", dq, g[0], g[3]), ("dk", dk, g[1], g[4]),
+                                        ("dv", dv, g[2], g[5])):
                 err, ratio = check_close(gpu[:, h].float().cpu().numpy(), ref, "bf16",
-                                         f"k={k} head {h} {name}")
+                                         f"k={k} head {h} {name}", mag)
                 print(f"k={k} head {h} {name}: max abs err {err:.3e} (bound use {ratio:.2f})",
                       flush=True)
     # the forward and dQ loops are unrolled by four stages, dK/dV by three
@@ -276,10 +279,11 @@ def test_bf16_fixed_shape_backward(shape):
             print(f"head {h}: a near-threshold block differs; gradients not compared")
             continue
         g = oracle.attn_bwd(op, inp_cpu["q"][:, h], inp_cpu["k"][:, h], inp_cpu["v"][:, h],
-                            inp_cpu["dout"][:, h])
-        for name, gpu, ref in (("dq", dq, g[0]), ("dk", dk, g[1]), ("dv", dv, g[2])):
+                            inp_cpu["dout"][:, h], with_mag=True)
+        for name, gpu, ref, mag in (("dq", dq, g[0], g[3]), ("dk", dk, g[1], g[4]),
+                                    ("dv", dv, g[2], g[5])):
             err, ratio = check_close(gpu[:, h].float().cpu().numpy(), ref, "bf16",
-                                     f"{shape} head {h} {name}")
+                                     f"{shape} head {h} {name}", mag)
             print(f"{shape} head {h} {name}: max abs err {err:.3e} (bound use {ratio:.2f})",
                   flush=True)
         compared += 1

@@ -401,6 +401,61 @@ def test_attn_bwd_rows_subset():
     np.testing.assert_allclose(full[1].sum(0), 0, atol=1e-10)
 
 
+def _dense_grads(q, k, v, do, scale, mask, wf=None, wb=None, wd=None):
+    """Dense masked attention gradients with optional relative perturbations: wf of the
+    forward's weights (renormalised; it moves o and so delta), wb of the weights in the
+    dV product, wd of dS.  Returns o, dq, dk, dv."""
+    s = np.where(mask, scale * q @ k.T, -np.inf)
+    P = np.exp(s - s.max(1, keepdims=True))
+    P /= P.sum(1, keepdims=True)
+    Pf = P if wf is None else P * (1 + wf)
+    o = (Pf / Pf.sum(1, keepdims=True)) @ v
+    delta = np.sum(do * o, 1, keepdims=True)
+    dS = P * (do @ v.T - delta)
+    if wd is not None:
+        dS = dS * (1 + wd)
+    Pb = P if wb is None else P * (1 + wb)
+    return o, scale * dS @ k, scale * dS.T @ q, Pb.T @ do
+
+
+def test_rounding_magnitudes_bound_perturbed_weights():
+    """The oracle's magnitude outputs bound, to first order, how far o, dq, dk and dv move
+    when every attention weight and every dS is perturbed by a relative amount of at most
+    u (checked on the dense masked formulation with random and with worst-case signs), are
+    reached by the worst case (o, dv), and are never below the results' own sizes."""
+    q, k, v, plan = _small_problem(6, D=16, scale_inputs=1.5)
+    N, D = q.shape
+    scale = 1 / math.sqrt(D)
+    r = np.random.default_rng(8)
+    do = r.normal(size=(N, D))
+    mask = _block_mask(plan, N)
+    o0, mo = oracle.attn_fwd(plan, q, k, v, with_mag=True)[0::2]
+    dq0, dk0, dv0, mq, mk, mv = oracle.attn_bwd(plan, q, k, v, do, with_mag=True)
+    od, dqd, dkd, dvd = _dense_grads(q, k, v, do, scale, mask)
+    np.testing.assert_allclose(od, o0, atol=1e-12)
+    for g, m in ((dq0, mq), (dk0, mk), (dv0, mv)):
+        assert np.all(np.abs(g) <= m * (1 + 1e-12) + 1e-15)
+    u = 2.0 ** -11
+    slack = 1 + 8 * u   # second-order terms
+    for seed in range(3):
+        rr = np.random.default_rng(100 + seed)
+        wf, wb, wd = (u * rr.uniform(-1, 1, size=(N, N)) for _ in range(3))
+        o1, dq1, dk1, dv1 = _dense_grads(q, k, v, do, scale, mask, wf, wb, wd)
+        for a, b, m in ((o1, od, mo), (dq1, dqd, mq), (dk1, dkd, mk), (dv1, dvd, mv)):
+            assert np.all(np.abs(a - b) <= u * m * slack + 1e-14)
+    # worst case for channel c: weights moved toward the sign of (v - o) and of do
+    for c in (0, 7):
+        wf = u * np.sign(v[None, :, c] - od[:, None, c])
+        o1 = _dense_grads(q, k, v, do, scale, mask, wf=wf)[0]
+        ratio = np.abs(o1[:, c] - od[:, c]) / (u * mo[:, c])
+        assert ratio.max() <= slack and ratio.max() >= 0.99
+        wb = u * np.sign(do[:, None, c]) * np.ones((1, N))
+        dv1 = _dense_grads(q, k, v, do, scale, mask, wb=wb)[3]
+        hit = mv[:, c] > 0
+        ratio = np.abs(dv1[hit, c] - dvd[hit, c]) / (u * mv[hit, c])
+        assert ratio.max() <= slack and ratio.min() >= 1 - 1e-9
+
+
 # ----------------------------------------------------------------------------- ablation settings
 
 def test_density_terms_separable():
