@@ -105,6 +105,10 @@ prism_status check_config(const prism_config *cfg, Dims *d, const char **why) {
     *why = "top_k_frac must be in [0, 1], map_exponent finite, density_mode 0..3";
     return PRISM_ERR_ARG;
   }
+  if (cfg->fixed_shape < 0) {
+    *why = "fixed_shape must be 0 (shapes from the guidance) or a packed shape";
+    return PRISM_ERR_ARG;
+  }
   if (cfg->fixed_shape > 0) {
     const int f = cfg->fixed_shape, a = (f >> 4) & 3, b = (f >> 2) & 3, c = f & 3;
     if (f > 63 || a < cfg->min_edge_log2 || b < cfg->min_edge_log2 ||
@@ -117,8 +121,10 @@ prism_status check_config(const prism_config *cfg, Dims *d, const char **why) {
     *why = "too many heads in one call";
     return PRISM_ERR_UNSUPPORTED;
   }
-  long long N = (long long)cfg->T * cfg->H * cfg->W;
-  if (N / kUnit > kMaxUnits) {
+  // T * H first: each factor is below 2^31, so neither product overflows
+  const long long TH = (long long)cfg->T * cfg->H;
+  const long long N = TH > (long long)kMaxUnits * kUnit ? 0 : TH * cfg->W;
+  if (N == 0 || N / kUnit > kMaxUnits) {
     *why = "more than 65535 64-token units per head";
     return PRISM_ERR_UNSUPPORTED;
   }
@@ -255,6 +261,7 @@ prism_status prism_plan(const prism_config *cfg, const void *q, const void *k, c
   prism_status st = check_config(cfg, &d, &why);
   if (st != PRISM_OK) return fail(st, why);
   if (!q || !k || !v || !workspace) return fail(PRISM_ERR_ARG, "null tensor or workspace");
+  if ((uintptr_t)workspace % 256) return fail(PRISM_ERR_ARG, "workspace not 256-byte aligned");
   if (tok_stride < 0 || head_stride < 0)
     return fail(PRISM_ERR_ARG, "strides must be non-negative (0 selects the dense layout)");
   if (tok_stride) d.tok_stride = (size_t)tok_stride;
@@ -292,6 +299,8 @@ prism_status prism_attn_fwd(const prism_config *cfg, void *workspace, size_t wor
   prism_status st = check_config(cfg, &d, &why);
   if (st != PRISM_OK) return fail(st, why);
   if (!o || !lse || !workspace) return fail(PRISM_ERR_ARG, "null output or workspace");
+  if ((uintptr_t)workspace % 256 || (uintptr_t)o % 16 || (uintptr_t)lse % 4)
+    return fail(PRISM_ERR_ARG, "workspace must be 256-byte, o 16-byte, lse 4-byte aligned");
   Layout L = make_layout(d);
   if (workspace_bytes < L.total) return fail(PRISM_ERR_WORKSPACE, "workspace too small");
   Scales sc = scales_of(cfg, d);
@@ -308,6 +317,10 @@ prism_status prism_attn_bwd(const prism_config *cfg, void *workspace, size_t wor
   if (st != PRISM_OK) return fail(st, why);
   if (!dout || !dq || !dk || !dv || !workspace)
     return fail(PRISM_ERR_ARG, "null tensor or workspace");
+  if ((uintptr_t)workspace % 256 || ((uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk |
+                                     (uintptr_t)dv) % 16)
+    return fail(PRISM_ERR_ARG, "workspace must be 256-byte aligned, dout, dq, dk, dv "
+                               "16-byte aligned");
   Layout L = make_layout(d);
   if (workspace_bytes < L.total) return fail(PRISM_ERR_WORKSPACE, "workspace too small");
   Scales sc = scales_of(cfg, d);

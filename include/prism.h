@@ -131,14 +131,16 @@ prism_status prism_plan_view(const prism_config *cfg, const void *workspace,
  * views into a fused QKV projection; they must be 16-byte aligned and the strides
  * multiples of 16 bytes (PRISM_ERR_ARG otherwise).  a2v_norm: [N] float32, or NULL for a
  * layer with no cached A2V norm (the first layer: video guidance only).  The plan is
- * written into workspace, which must stay untouched until the last fwd/bwd using it. */
+ * written into workspace (256-byte aligned, PRISM_ERR_ARG otherwise), which must stay
+ * untouched until the last fwd/bwd using it. */
 prism_status prism_plan(const prism_config *cfg, const void *q, const void *k, const void *v,
                         int64_t tok_stride, int64_t head_stride, const float *a2v_norm,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* Sparse attention forward over the plan in workspace (step 5): o [N][heads][D] in token
  * order, lse [heads][N] float32 (natural-log sum of exp of the scaled logits).  Also keeps
- * a float32 copy of o and the lse in workspace for prism_attn_bwd. */
+ * a float32 copy of o and the lse in workspace for prism_attn_bwd.  o must be 16-byte
+ * aligned, lse 4-byte, workspace 256-byte (PRISM_ERR_ARG otherwise). */
 prism_status prism_attn_fwd(const prism_config *cfg, void *workspace, size_t workspace_bytes,
                             void *o, float *lse, void *stream);
 
@@ -156,7 +158,8 @@ prism_status prism_a2v_norm(const void *x, int64_t n_tokens, int channels, int64
 /* Sparse attention backward with the plan held constant (digest, training section): given
  * dout [N][heads][D], writes dq, dk, dv [N][heads][D] (overwritten, token order).  Reads
  * the float32 copy of the output and the lse that prism_attn_fwd left in workspace, so
- * prism_attn_fwd must have run on this workspace since the last prism_plan. */
+ * prism_attn_fwd must have run on this workspace since the last prism_plan.  dout, dq, dk,
+ * dv must be 16-byte aligned, workspace 256-byte (PRISM_ERR_ARG otherwise). */
 prism_status prism_attn_bwd(const prism_config *cfg, void *workspace, size_t workspace_bytes,
                             const void *dout, void *dq, void *dk, void *dv, void *stream);
 

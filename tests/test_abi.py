@@ -51,6 +51,8 @@ def test_layout_and_workspace(lib):
     (dict(fixed_shape=(1 << 4) | (1 << 2) | 1), -1),     # 2x2x2: 8 tokens
     (dict(fixed_shape=(3 << 4) | (3 << 2) | 3), -1),     # 8x8x8: 512 tokens
     (dict(fixed_shape=(0 << 4) | (3 << 2) | 3), -1),     # edge 1 with min_edge_log2 = 1
+    (dict(fixed_shape=-1), -1),
+    (dict(T=1 << 30, H=1 << 30, W=1 << 30), -2),          # T * H * W beyond 64 bits
 ])
 def test_rejected_configs(lib, over, code):
     base = dict(T=8, H=16, W=16, num_heads=2, head_dim=128, dtype=P.BF16, min_edge_log2=1,
@@ -92,6 +94,23 @@ def test_plan_rejects_bad_strides(lib):
                               None) == -1, (tok, head)
     assert lib.prism_plan(ctypes.byref(cfg), ctypes.c_void_p(264), d, d, 0, 0, None, d, need,
                           None) == -1  # q not 16-byte aligned
+
+
+def test_entry_points_reject_misaligned_buffers(lib):
+    cfg = P.make_config(8, 16, 16, 2, 128, "bf16")
+    need = lib.prism_workspace_bytes(ctypes.byref(cfg))
+    d, ws, bad_ws = ctypes.c_void_p(4096), ctypes.c_void_p(8192), ctypes.c_void_p(8192 + 16)
+    assert lib.prism_plan(ctypes.byref(cfg), d, d, d, 0, 0, None, bad_ws, need, None) == -1
+    assert lib.prism_attn_fwd(ctypes.byref(cfg), bad_ws, need, d, d, None) == -1
+    assert lib.prism_attn_fwd(ctypes.byref(cfg), ws, need, ctypes.c_void_p(4104), d,
+                              None) == -1                                  # o
+    assert lib.prism_attn_fwd(ctypes.byref(cfg), ws, need, d, ctypes.c_void_p(4098),
+                              None) == -1                                  # lse
+    assert lib.prism_attn_bwd(ctypes.byref(cfg), bad_ws, need, d, d, d, d, None) == -1
+    for i in range(4):
+        args = [d] * 4
+        args[i] = ctypes.c_void_p(4104)
+        assert lib.prism_attn_bwd(ctypes.byref(cfg), ws, need, *args, None) == -1, i
 
 
 def test_plan_view_matches_layout(lib):
