@@ -7,8 +7,8 @@ streams.  There is no fallback: if the library is missing or was built for anoth
 calls raise.
 
 Entry points (same names as the C ABI):
-  workspace_bytes(cfg), plan_layout(cfg), plan(cfg, q, k, v, a2v, ws),
-  attn_fwd(cfg, ws, o, lse), attn_bwd(cfg, ws, dout, dq, dk, dv)
+  workspace_bytes(cfg), plan_layout(cfg), plan_view(cfg, ws), plan(cfg, q, k, v, a2v, ws),
+  attn_fwd(cfg, ws, o, lse), attn_bwd(cfg, ws, dout, dq, dk, dv), a2v_norm(x)
 and ``PrismAttention``, which owns a workspace and chains them.
 """
 from __future__ import annotations
@@ -179,6 +179,12 @@ def _tok(cfg, t, name, dtype=None, strided=False):
                          f"{t.dtype} {tuple(t.shape)} strides {t.stride()} on {t.device}")
 
 
+def _ws(ws):
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace: expected a contiguous GPU tensor")
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
 def workspace_bytes(cfg: PrismConfig) -> int:
     n = lib().prism_workspace_bytes(ctypes.byref(cfg))
     if n == 0:
@@ -203,25 +209,24 @@ def plan(cfg, q, k, v, a2v, ws, stream=None):
                             or not a2v.is_contiguous() or not a2v.is_cuda):
         raise ValueError("a2v: expected a contiguous float32 [N] GPU tensor")
     _check(lib().prism_plan(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), q.stride(0),
-                            q.stride(1), _ptr(a2v), _ptr(ws), ws.numel() * ws.element_size(),
-                            _stream(stream)), "prism_plan")
+                            q.stride(1), _ptr(a2v), *_ws(ws), _stream(stream)), "prism_plan")
 
 
 def attn_fwd(cfg, ws, o, lse, stream=None):
     _tok(cfg, o, "o")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (cfg.num_heads, cfg.N):
-        raise ValueError("lse: expected float32 [heads, N]")
-    _check(lib().prism_attn_fwd(ctypes.byref(cfg), _ptr(ws), ws.numel() * ws.element_size(),
-                                _ptr(o), _ptr(lse), _stream(stream)), "prism_attn_fwd")
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (cfg.num_heads, cfg.N)
+            or not lse.is_contiguous() or not lse.is_cuda):
+        raise ValueError("lse: expected a contiguous float32 [heads, N] GPU tensor")
+    _check(lib().prism_attn_fwd(ctypes.byref(cfg), *_ws(ws), _ptr(o), _ptr(lse),
+                                _stream(stream)), "prism_attn_fwd")
 
 
 def attn_bwd(cfg, ws, dout, dq, dk, dv, stream=None):
     """Needs prism_attn_fwd to have run on ws since the last plan (it keeps O and lse)."""
     for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         _tok(cfg, t, name)
-    _check(lib().prism_attn_bwd(ctypes.byref(cfg), _ptr(ws), ws.numel() * ws.element_size(),
-                                _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)),
-           "prism_attn_bwd")
+    _check(lib().prism_attn_bwd(ctypes.byref(cfg), *_ws(ws), _ptr(dout), _ptr(dq), _ptr(dk),
+                                _ptr(dv), _stream(stream)), "prism_attn_bwd")
 
 
 def a2v_norm(x, out=None, stream=None):
@@ -234,8 +239,9 @@ def a2v_norm(x, out=None, stream=None):
     n = x.shape[0]
     if out is None:
         out = torch.empty(n, dtype=torch.float32, device=x.device)
-    if out.shape != (n,) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out: expected float32 [N]")
+    if (out.shape != (n,) or out.dtype != torch.float32 or not out.is_contiguous()
+            or not out.is_cuda):
+        raise ValueError("out: expected a contiguous float32 [N] GPU tensor")
     dt = BF16 if x.dtype == torch.bfloat16 else F32
     _check(lib().prism_a2v_norm(_ptr(x), n, x.shape[1], x.stride(0), dt, _ptr(out),
                                 _stream(stream)), "prism_a2v_norm")
@@ -257,9 +263,17 @@ def trace_read() -> dict:
     return {lib().prism_stage_name(i).decode(): (ms[i], calls[i]) for i in range(n)}
 
 
+def plan_view(cfg: PrismConfig, ws) -> PrismLayout:
+    """Byte offsets of the plan's arrays inside the workspace ws (prism_plan_view)."""
+    out = PrismLayout()
+    _check(lib().prism_plan_view(ctypes.byref(cfg), _ws(ws)[0], ctypes.byref(out)),
+           "prism_plan_view")
+    return out
+
+
 def plan_views(cfg, ws) -> dict:
     """Typed views of the plan's arrays inside the workspace (see prism_layout)."""
-    L = plan_layout(cfg)
+    L = plan_view(cfg, ws)
     Hh, Z, nb, N, D = cfg.num_heads, L.Z, L.nb_max, L.N, cfg.head_dim
 
     def view(off, dtype, shape):
