@@ -242,7 +242,7 @@ __device__ __forceinline__ void dq_waves(
       const uint8_t *src = hbase + (size_t)pre.unit() * kUnit * kDB * 2;
 #pragma unroll
       for (int i = 0; i < kQCpw; ++i)
-        dma16(src + cofs(i), reinterpret_cast<uint8_t *>(&st) + cdst + 1024 * i);
+        dma16(src, (uint32_t)cofs(i), reinterpret_cast<uint8_t *>(&st) + cdst + 1024 * i);
       if (pending) {
         ++issued;
         pending = pre.next();

@@ -120,6 +120,14 @@ struct DState {
 __device__ __forceinline__ void p_first(PState &w, uint32_t st, int pair, int lane,
                                         float scale_log2e) {
   const int l32 = lane & 31, hh = lane >> 5;
+  // the lse values of the lane's 32 queries are read before the product, so that the
+  // exponentials below never wait on LDS
+  f32x4 lv[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4)
+      lv[a][v4] = lds_f32x4(st + kVecs + 4u * (32 * a + 8 * v4 + 4 * hh));
   f32x16 sacc[2] = {f32x16{}, f32x16{}};
   both_halves_product(sacc, st, w.breg, l32, hh);
   f16x8 x[2][2];  // built fresh: the previous unit's weights are dead here
@@ -127,7 +135,7 @@ __device__ __forceinline__ void p_first(PState &w, uint32_t st, int pair, int la
   for (int a = 0; a < 2; ++a) {
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4) {
-      const f32x4 l4 = lds_f32x4(st + kVecs + 4u * (32 * a + 8 * v4 + 4 * hh));
+      const f32x4 l4 = lv[a][v4];
       f32x4 p4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -166,12 +174,19 @@ __device__ __forceinline__ void d_dk(DState &w, uint32_t st, int lane) {
 }
 // dS wave, after the barrier: dS = P (dP - delta) in float32, rounded once to float16
 __device__ __forceinline__ void d_ds(DState &w, int pair, int lane) {
+  // all eight reads of P are in flight together, then the products
+  f32x4 pv[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) pv[a][v4] = g_pex[pair][a][v4][lane];
+  __builtin_amdgcn_sched_barrier(0);
   f16x8 db[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4) {
-      const f32x4 p4 = g_pex[pair][a][v4][lane];
+      const f32x4 p4 = pv[a][v4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int v = 4 * v4 + e;
@@ -260,8 +275,8 @@ __device__ __forceinline__ void dkdv_waves(
       const uint8_t *src = tsrc + (hb + (size_t)u * kUnit) * kDB * 2;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        dma16(src + cofs(i), reinterpret_cast<uint8_t *>(&st) + cdst + 1024 * i);
-      if (vcopy) dma4(vsrc + hb + (size_t)u * kUnit + lane, st.vec[wave]);
+        dma16(src, (uint32_t)cofs(i), reinterpret_cast<uint8_t *>(&st) + cdst + 1024 * i);
+      if (vcopy) dma4(vsrc + hb + (size_t)u * kUnit, 4u * (uint32_t)lane, st.vec[wave]);
       if (pending) {
         ++issued;
         pending = pre.next();

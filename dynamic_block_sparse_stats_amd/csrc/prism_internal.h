@@ -230,12 +230,13 @@ __device__ __forceinline__ void tr_update(f32x16 (&acc)[4], const TrBase &tb,
   }
 }
 
-// Direct global -> LDS copies (global_load_lds): lane l of one instruction writes its
-// 16 (or 4) bytes at dst + 16 * l (4 * l); dst must be uniform across the wave and is
-// passed in M0.  They are written as inline assembly on purpose: the compiler classes the
-// instruction as a flat access that may touch LDS, and while one is outstanding on vmcnt
-// (in these kernels: always) it makes every wait for an LDS read wait for all of them
-// (lgkmcnt(0)), which stops any LDS read from overlapping the MFMAs before it.  The
+// Direct global -> LDS copies (global_load_lds): lane l of one instruction reads 16 (or 4)
+// bytes at base + off and writes them at dst + 16 * l (4 * l); base and dst must be
+// uniform across the wave (dst is passed in M0).  They are written as inline assembly on
+// purpose: the compiler classes the instruction as a flat access that may touch LDS, and
+// while one is outstanding on vmcnt (in these kernels: always) it makes every wait for an
+// LDS read wait for all of them (lgkmcnt(0)), which stops any LDS read from overlapping
+// the MFMAs before it.  The
 // hardware counts these copies on vmcnt only.  Hidden from the compiler, they are ordered
 // by the kernels themselves: explicit s_waitcnt vmcnt before the barrier that publishes a
 // stage, and the "memory" clobber, which keeps the compiler from moving LDS accesses across
@@ -245,16 +246,19 @@ __device__ __forceinline__ uint32_t lds_dst(void *dst) {
   return __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)dst);
 }
-__device__ __forceinline__ void dma16(const void *src, void *dst) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+// The copies take the instruction's saddr form: a wave-uniform 64-bit base in SGPRs plus a
+// 32-bit per-lane byte offset, so a copy costs no per-lane 64-bit address arithmetic (the
+// offsets stay in registers across the whole list walk).
+__device__ __forceinline__ void dma16(const void *base, uint32_t off, void *dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(src), "s"(lds_dst(dst))
+               : "v"(off), "s"(base), "s"(lds_dst(dst))
                : "memory");
 }
-__device__ __forceinline__ void dma4(const void *src, void *dst) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+__device__ __forceinline__ void dma4(const void *base, uint32_t off, void *dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                :
-               : "v"(src), "s"(lds_dst(dst))
+               : "v"(off), "s"(base), "s"(lds_dst(dst))
                : "memory");
 }
 
