@@ -20,12 +20,15 @@ def _head_inputs(inp, h):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cid", [1, 2, 4])
-def test_fullsize(cid):
+@pytest.mark.parametrize("cid,policy", [(1, None), (2, None), (4, None), (4, "pages")],
+                         ids=["720p", "1080p", "2k", "2k-pages-operating-point"])
+def test_fullsize(cid, policy):
     wl = synth.workload(cid)
-    print(f"\n== {wl.name}: generating inputs", flush=True)
+    print(f"\n== {wl.name} {policy or ''}: generating inputs", flush=True)
     inp = synth.make_inputs(wl, device="cuda", with_dout=False)
-    cfg = P.config_for(wl)
+    over = dict(P.POLICIES[policy]) if policy else {}
+    cfg = P.config_for(wl, **over)
+    sel = dict(top_k=cfg.top_k, top_p=cfg.top_p, top_k_frac=cfg.top_k_frac)
     att = P.PrismAttention(cfg)
     att.plan(inp["q"], inp["k"], inp["v"], inp["a2v"])
     o, lse = att.forward()
@@ -38,11 +41,11 @@ def test_fullsize(cid):
     views = att.views()
     for h in heads:
         hi = _head_inputs(inp, h)
-        op = oracle.plan_head(wl.T, wl.H, wl.W, hi["q"], hi["k"], hi["v"], a2v, top_k=wl.top_k,
-                              top_p=wl.top_p, min_edge_log2=wl.min_edge_log2)
+        op = oracle.plan_head(wl.T, wl.H, wl.W, hi["q"], hi["k"], hi["v"], a2v,
+                              min_edge_log2=wl.min_edge_log2, **sel)
         rep = compare_plan(views, h, op)
         assert not rep.get("downstream_skipped"), rep
-        exact, excl, nnz = compare_selection(views, h, op, wl.top_p)
+        exact, excl, nnz = compare_selection(views, h, op, cfg.top_p)
         ok_rows = np.nonzero(rows_of_exact_blocks(op, exact))[0]
         rows = np.sort(rng.choice(ok_rows, size=64, replace=False))
         oo, ol, mo = oracle.attn_fwd(op, hi["q"], hi["k"], hi["v"], rows=rows, with_mag=True)
