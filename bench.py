@@ -414,6 +414,19 @@ def main():
     if roofline["traffic"] is not None:
         roofline["traffic_note"] = ("HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                     "scaled by a 1 GiB copy)")
+    # the same figures for each attention kernel of the step (algorithmic FLOPs: forward
+    # 4*D, dK/dV 8*D, dQ 2*D per pair; dQ also executes 4*D of recomputed S and dP)
+    attention_kernels = {}
+    for k, fl in kernel_flops.items():
+        if k in trace and trace[k][1] > 0:
+            ms_k = trace[k][0] / trace[k][1]
+            a_k = fl / (ms_k * 1e-3) / 1e12
+            attention_kernels[k] = {"launch_ms": round(ms_k, 3), "achieved": round(a_k, 2),
+                                    "frac": round(a_k / PEAK_BF16_TFLOPS, 4),
+                                    "traffic": measured_traffic(k, wl.name)}
+    if "bwd_dq" in attention_kernels:
+        ex = 6.0 * D * tot_pairs / (attention_kernels["bwd_dq"]["launch_ms"] * 1e-3) / 1e12
+        attention_kernels["bwd_dq"]["executed_incl_recompute"] = round(ex, 2)
 
     # the A2V norm producer (the field the next layer's plan reads) on a synthetic
     # cross-attention output of hidden width heads x D: an HBM-bound row reduction
@@ -498,6 +511,7 @@ def main():
         "dense": dense,
         "a2v_norm": a2v_norm,
         "roofline": roofline,
+        "attention_kernels": attention_kernels,
         "cpu_baseline": cpu,
     }
     s = json.dumps(line)

@@ -142,6 +142,9 @@ __device__ __forceinline__ void dq_half(const DqState &w, uint32_t st, int a, in
     x[buf][0] = lds_row16(ad);
     x[buf][1] = lds_row16(ad + 16384u);
   };
+  // raised issue priority while forming S and dP (the exponentials below wait for them),
+  // default priority for the exponentials: the SIMD's other wave runs its MFMAs under them
+  __builtin_amdgcn_s_setprio(1);
   load(0, 0);
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
@@ -151,6 +154,7 @@ __device__ __forceinline__ void dq_half(const DqState &w, uint32_t st, int a, in
     dp = mfma_f16(x[kk & 1][1], w.doreg[kk], dp);
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(0);
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const float p = __builtin_amdgcn_exp2f(fmaf(s[v], scale_log2e, -w.lse2));

@@ -81,6 +81,10 @@ __device__ __forceinline__ void fwd_scores(FwdState &w, uint32_t kt, int lane,
       for (int e = 0; e < 2; ++e)
         ka[buf][a][e] = lds_row16((kr ^ (uint32_t)((2 * grp + e) << 5)) + 8192u * a);
   };
+  // the wave issues at a raised priority while it forms the scores its softmax waits for,
+  // and at the default one for the exponentials, so that the SIMD's other wave runs its
+  // MFMAs under them
+  __builtin_amdgcn_s_setprio(1);
   load(0, 0);
 #pragma unroll
   for (int grp = 0; grp < 4; ++grp) {
@@ -92,6 +96,7 @@ __device__ __forceinline__ void fwd_scores(FwdState &w, uint32_t kt, int lane,
       for (int a = 0; a < 2; ++a) s[a] = mfma_f16(ka[grp & 1][a][e], w.qreg[2 * grp + e], s[a]);
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(0);
   // online softmax (log2 domain) with lazy rescaling: the running max only moves when a
   // query's new maximum exceeds it by more than 2^kLazy, so the float16 weights
   // 2^(t - m + 10) stay below 2^15
