@@ -36,9 +36,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SOURCES = {"attn_fwd": "attn_fwd.hip", "bwd_dkdv": "attn_bwd_dkdv.hip",
                   "bwd_dq": "attn_bwd.hip"}
 MEASURED_TRAFFIC = {
-    ("attn_fwd", "2k-train-64x104x128"): ("22da6d389af4e7d1", 30.776e12),
-    ("bwd_dkdv", "2k-train-64x104x128"): ("9a3bff2c2fcebf40", 41.108e12),
-    ("bwd_dq", "2k-train-64x104x128"): ("5fc7568e5bcca23a", 30.766e12),
+    ("attn_fwd", "2k-train-64x104x128"): ("9e206c674f073b53", 30.770e12),
+    ("bwd_dkdv", "2k-train-64x104x128"): ("9a3bff2c2fcebf40", 41.588e12),
+    ("bwd_dq", "2k-train-64x104x128"): ("6c79804ef4788f78", 30.761e12),
 }
 
 
