@@ -168,9 +168,33 @@ __device__ __forceinline__ void d_dp(DState &w, uint32_t st, int lane) {
     }
   both_halves_product(w.dp, st + kDOTile, w.breg, l32, hh);
 }
-// dS wave: dK^T += Q^T dS with the carried dS, Q^T read from the Q tile of stage st
-__device__ __forceinline__ void d_dk(DState &w, uint32_t st, int lane) {
-  tr_update(w.acc, tr_base(st, lane), w.db);
+// dS wave: the transposed-read base of the Q tile at st and the A operands of the first
+// 16-row slice of the dK product, read before the dP product so that the dK product does
+// not start on an LDS round trip
+__device__ __forceinline__ TrBase d_dk_first(uint32_t st, int lane, f16x8 (&first)[4]) {
+  const TrBase tb = tr_base(st, lane);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) first[dt] = tr_read(tb, 0, 32 * dt);
+  return tb;
+}
+// dS wave: dK^T += Q^T dS with the carried dS (Q^T through tb, its first slice in first);
+// per slice the four d-tiles' accumulators are independent, and the next slice's operands
+// are read while one runs
+__device__ __forceinline__ void d_dk(DState &w, const TrBase &tb, const f16x8 (&first)[4]) {
+  f16x8 ta[2][4];  // [buffer][dt]
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) ta[0][dt] = first[dt];
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) {
+    if (sl < 3)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) ta[(sl + 1) & 1][dt] = tr_read(tb, 16 * (sl + 1), 32 * dt);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      w.acc[dt] = mfma_f16(ta[sl & 1][dt], w.db[sl >> 1][sl & 1], w.acc[dt]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 // dS wave, after the barrier: dS = P (dP - delta) in float32, rounded once to float16
 __device__ __forceinline__ void d_ds(DState &w, int pair, int lane) {
@@ -306,9 +330,11 @@ __device__ __forceinline__ void dkdv_waves(
         if (active) p_second(w, st, lane);
       } else {
         if (active) {
-          d_dp(w, st, lane);
           const uint32_t prev = stage_addr<(S + kStages - 1) % kStages>();
-          d_dk(w, u == 0 ? st : prev, lane);
+          f16x8 first[4];
+          const TrBase tb = d_dk_first(u == 0 ? st : prev, lane, first);
+          d_dp(w, st, lane);
+          d_dk(w, tb, first);
         }
         if (!unit_u) return false;
         publish_sync();
