@@ -258,22 +258,26 @@ __device__ __forceinline__ void dq_waves(
     auto step = [&](auto stage_tag, int u) {
       constexpr int S = decltype(stage_tag)::value;
       dq_wait_one_behind();
-      issue(dq_stage<(S + 2) % kQStages>());
+      // issued counts the units up to u + 1 at least, or all of them
       const bool unit_u = u < issued;
-      if (active) {
-        const uint32_t st = dq_stage_addr<S>();
-        if constexpr (LATE) {
-          const uint32_t prev = dq_stage_addr<(S + kQStages - 1) % kQStages>();
-          dq_update(w, u == 0 ? st : prev, lane);
-          if (!unit_u) return false;
-          dq_scores(w, st, lane, scale_log2e);
-        } else {
-          if (!unit_u) return false;
+      const uint32_t st = dq_stage_addr<S>();
+      if constexpr (LATE) {
+        // the late wave issues its copies after its dQ product, so that right after the
+        // barrier the early waves' copies and score products go first
+        const uint32_t prev = dq_stage_addr<(S + kQStages - 1) % kQStages>();
+        if (active) dq_update(w, u == 0 ? st : prev, lane);
+        issue(dq_stage<(S + 2) % kQStages>());
+        if (!unit_u) return false;
+        if (active) dq_scores(w, st, lane, scale_log2e);
+      } else {
+        issue(dq_stage<(S + 2) % kQStages>());
+        if (!unit_u) return false;
+        if (active) {
           dq_scores(w, st, lane, scale_log2e);
           dq_update(w, st, lane);
         }
       }
-      return unit_u;
+      return true;
     };
 
     workgroup_barrier();  // every wave is done with the previous tile's stages

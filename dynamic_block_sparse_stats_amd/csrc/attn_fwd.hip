@@ -258,22 +258,26 @@ __device__ __forceinline__ void fwd_waves(
     auto step = [&](auto stage_tag, int u) {
       constexpr int S = decltype(stage_tag)::value;
       wait_unit_one_behind();
-      issue(fwd_stage<(S + 2) % kStages>());
+      // issued counts the units up to u + 1 at least, or all of them
       const bool unit_u = u < issued;
-      if (active) {
-        const uint32_t st = fwd_stage_addr<S>();
-        if constexpr (LATE) {
-          const uint32_t prev = fwd_stage_addr<(S + kStages - 1) % kStages>();
-          fwd_values(w, (u == 0 ? st : prev) + 16384, lane);
-          if (!unit_u) return false;
-          fwd_scores(w, st, lane, scale_log2e);
-        } else {
-          if (!unit_u) return false;
+      const uint32_t st = fwd_stage_addr<S>();
+      if constexpr (LATE) {
+        // the late wave issues its copies after its PV product, so that right after the
+        // barrier the early waves' copies and score products go first
+        const uint32_t prev = fwd_stage_addr<(S + kStages - 1) % kStages>();
+        if (active) fwd_values(w, (u == 0 ? st : prev) + 16384, lane);
+        issue(fwd_stage<(S + 2) % kStages>());
+        if (!unit_u) return false;
+        if (active) fwd_scores(w, st, lane, scale_log2e);
+      } else {
+        issue(fwd_stage<(S + 2) % kStages>());
+        if (!unit_u) return false;
+        if (active) {
           fwd_scores(w, st, lane, scale_log2e);
           fwd_values(w, st + 16384, lane);
         }
       }
-      return unit_u;
+      return true;
     };
 #pragma unroll
     for (int g = 0; g < 4; ++g) w.pb[g] = f16x8{};
