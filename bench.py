@@ -36,9 +36,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SOURCES = {"attn_fwd": "attn_fwd.hip", "bwd_dkdv": "attn_bwd_dkdv.hip",
                   "bwd_dq": "attn_bwd.hip"}
 MEASURED_TRAFFIC = {
-    ("attn_fwd", "2k-train-64x104x128"): ("9e206c674f073b53", 30.770e12),
-    ("bwd_dkdv", "2k-train-64x104x128"): ("9a3bff2c2fcebf40", 41.588e12),
-    ("bwd_dq", "2k-train-64x104x128"): ("6c79804ef4788f78", 30.761e12),
+    ("attn_fwd", "2k-train-64x104x128"): ("e57bfb5901d07a92", 30.778e12),
+    ("bwd_dkdv", "2k-train-64x104x128"): ("1d86237831a8c3b0", 57.133e12),
+    ("bwd_dq", "2k-train-64x104x128"): ("bce6fb3b39bf4e99", 30.772e12),
 }
 
 
