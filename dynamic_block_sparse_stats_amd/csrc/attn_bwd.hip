@@ -91,9 +91,10 @@ __global__ void __launch_bounds__(256)
 // 16 V rows, four one-kilobyte copies per wave and unit.  Per unit a wave forms S^T and
 // dP^T (K and V rows read directly), dS = P (dP - delta) as float16, and dQ^T += K^T dS^T
 // (K^T through transposing reads).  As in the forward, the two waves of a SIMD run half a
-// unit apart: the late wave (w >= 4) runs the dQ product of the previous unit before the
-// scores of the current one, carrying dS across the barrier, so one wave's exponentials
-// overlap the other's MFMAs.
+// unit apart: the late wave (w >= 4) runs the dQ product of the previous unit (then issues
+// its copies) before the scores of the current one, carrying dS across the barrier, so one
+// wave's exponentials overlap the other's MFMAs; a wave raises its issue priority while it
+// forms S and dP.
 constexpr int QW = 8;
 constexpr int kQStages = 4;
 constexpr int kQCpw = 32 / QW;

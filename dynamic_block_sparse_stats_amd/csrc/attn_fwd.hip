@@ -16,8 +16,10 @@
 //     [64 keys][128] float16, XOR-swizzled by 16-byte chunk; K rows are read directly, V^T
 //     with transposing LDS reads (ds_read_b64_tr_b16);
 //   * the two waves of a SIMD run half a unit apart (the late one finishes the previous
-//     unit's PV product while the early one forms its scores), and each wave reads the
-//     operands of its next group of MFMAs while the current group runs;
+//     unit's PV product, then issues its copies, while the early one issues its copies and
+//     forms its scores), each wave raises its issue priority while it forms the scores its
+//     softmax waits for, and each reads the operands of its next group of MFMAs while the
+//     current group runs;
 //   * the softmax weights go to the PV product as float16 scaled by 2^10 (11-bit
 //     significands where bf16 has 8: at 2K, value rows reach |v| ~ 20 and the PV sums
 //     cancel, so bf16 weights cost ~3e-2 absolute); the row sum adds the same float16
