@@ -98,6 +98,7 @@ __global__ void __launch_bounds__(256)
 constexpr int QW = 8;
 constexpr int kQStages = 4;
 constexpr int kQCpw = 32 / QW;
+static_assert(kQCpw == 4, "copy_rows16 issues four copies per wave and unit");
 struct DqStage {
   uint8_t tile[2][16384];  // K, V
 };
@@ -198,10 +199,7 @@ __device__ __forceinline__ void dq_waves(
   const int wq = wave & (QW / 2 - 1);
   const uint8_t *csrc = reinterpret_cast<const uint8_t *>(LATE ? vp : kp);
   const int cdst = (LATE ? 16384 : 0) + wq * 4096;
-  auto cofs = [&](int i) {  // byte offset inside the unit of this lane's 16 bytes, copy i
-    const int r = 16 * wq + 4 * i + (lane >> 4);
-    return r * 256 + (((lane & 15) ^ swz(r)) << 4);
-  };
+  const uint32_t c0 = copy_offset(16 * wq, lane);  // this lane's source offset in the unit
 
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int2 tl = tiles[t];
@@ -245,9 +243,7 @@ __device__ __forceinline__ void dq_waves(
     // stage no step reads any more (drained before the next tile)
     auto issue = [&](DqStage &st) {
       const uint8_t *src = hbase + (size_t)pre.unit() * kUnit * kDB * 2;
-#pragma unroll
-      for (int i = 0; i < kQCpw; ++i)
-        dma16(src, (uint32_t)cofs(i), reinterpret_cast<uint8_t *>(&st) + cdst + 1024 * i);
+      copy_rows16(src, c0, reinterpret_cast<uint8_t *>(&st) + cdst);
       if (pending) {
         ++issued;
         pending = pre.next();

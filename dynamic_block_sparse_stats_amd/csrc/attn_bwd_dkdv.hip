@@ -243,10 +243,7 @@ __device__ __forceinline__ void dkdv_waves(
   // and 1 also copy the lse and delta vectors
   const uint8_t *tsrc = reinterpret_cast<const uint8_t *>(PW ? qp : dop);
   const int cdst = (PW ? 0 : 16384) + pair * 4096;
-  auto cofs = [&](int i) {  // byte offset inside the unit of this lane's 16 bytes, copy i
-    const int r = 16 * pair + 4 * i + (lane >> 4);
-    return r * 256 + (((lane & 15) ^ swz(r)) << 4);
-  };
+  const uint32_t c0 = copy_offset(16 * pair, lane);  // this lane's source offset in the unit
   const bool vcopy = wave < 2;
   const float *vsrc = wave == 1 ? ndelta : lse2;
 
@@ -297,9 +294,7 @@ __device__ __forceinline__ void dkdv_waves(
     auto issue = [&](Stage &st) {
       const int u = pre.unit();
       const uint8_t *src = tsrc + (hb + (size_t)u * kUnit) * kDB * 2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dma16(src, (uint32_t)cofs(i), reinterpret_cast<uint8_t *>(&st) + cdst + 1024 * i);
+      copy_rows16(src, c0, reinterpret_cast<uint8_t *>(&st) + cdst);
       if (vcopy) dma4(vsrc + hb + (size_t)u * kUnit, 4u * (uint32_t)lane, st.vec[wave]);
       if (pending) {
         ++issued;

@@ -41,6 +41,7 @@ constexpr int kD = 128;
 constexpr int NW = 8;      // waves per workgroup: 8 x 32 = 256 query rows, one block
 constexpr int kStages = 4;  // LDS ring depth (copies run 2 units ahead of the one computed)
 constexpr int kCpw = 32 / NW;  // 1 KB copies per wave per unit (16 for K, 16 for V)
+static_assert(kCpw == 4, "copy_rows16 issues four copies per wave and unit");
 
 // Four LDS stages of 32 KB (distinct objects, named statically by the unrolled unit loop)
 // filled by direct global->LDS copies: waves 0-3 copy 16 K rows each, waves 4-7 16 V rows
@@ -202,10 +203,7 @@ __device__ __forceinline__ void fwd_waves(
   const int wq = wave & (NW / 2 - 1);
   const uint8_t *csrc = reinterpret_cast<const uint8_t *>(LATE ? vp : kp);
   const int cdst = (LATE ? 16384 : 0) + wq * 4096;
-  auto cofs = [&](int i) {  // byte offset inside the unit of this lane's 16 bytes, copy i
-    const int r = 16 * wq + 4 * i + (lane >> 4);
-    return r * 256 + (((lane & 15) ^ swz(r)) << 4);
-  };
+  const uint32_t c0 = copy_offset(16 * wq, lane);  // this lane's source offset in the unit
 
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int2 tl = tiles[t];
@@ -244,9 +242,7 @@ __device__ __forceinline__ void fwd_waves(
     // into a stage no step reads any more (drained before the next tile)
     auto issue = [&](FwdStage &st) {
       const uint8_t *src = hbase + (size_t)pre.unit() * kUnit * kD * 2;
-#pragma unroll
-      for (int i = 0; i < kCpw; ++i)
-        dma16(src, (uint32_t)cofs(i), reinterpret_cast<uint8_t *>(&st) + cdst + 1024 * i);
+      copy_rows16(src, c0, reinterpret_cast<uint8_t *>(&st) + cdst);
       if (pending) {
         ++issued;
         pending = pre.next();

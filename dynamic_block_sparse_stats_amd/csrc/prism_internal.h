@@ -249,11 +249,32 @@ __device__ __forceinline__ uint32_t lds_dst(void *dst) {
 // The copies take the instruction's saddr form: a wave-uniform 64-bit base in SGPRs plus a
 // 32-bit per-lane byte offset, so a copy costs no per-lane 64-bit address arithmetic (the
 // offsets stay in registers across the whole list walk).
+// IMM, the instruction's offset field (0 .. 4095), is added to both addresses: the global
+// one (base + off + IMM) and the LDS one (dst + IMM)
+template <int IMM = 0>
 __device__ __forceinline__ void dma16(const void *base, uint32_t off, void *dst) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3"
                :
-               : "v"(off), "s"(base), "s"(lds_dst(dst))
+               : "v"(off), "s"(base), "s"(lds_dst(dst)), "i"(IMM)
                : "memory");
+}
+
+// A wave's share of a unit copy: rows r0 .. r0 + 15 (r0 a multiple of 16) of a row-major
+// [64][128] 16-bit tile, swizzled as in rm_swz, in four 1 KB copies of four rows each.  Lane
+// l fetches chunk (l % 16) ^ swz(r) of row r = r0 + 4i + l / 16 in copy i; with r0 a multiple
+// of 16, swz(r) = 4 (l / 16) + i, so the lane's source offset in copy i is
+// (c0 ^ 16 i) + 1024 i with c0 = copy_offset(r0, l) that of copy 0: one register and a XOR
+// per copy, the 1024 i going into the instruction's offset field (which moves the LDS
+// destination by the same 1024 i).
+__device__ __forceinline__ uint32_t copy_offset(int r0, int lane) {
+  const int r = r0 + (lane >> 4);
+  return (uint32_t)(r * 256 + (((lane & 15) ^ swz(r)) << 4));
+}
+__device__ __forceinline__ void copy_rows16(const void *src, uint32_t c0, uint8_t *dst) {
+  dma16<0>(src, c0, dst);
+  dma16<1024>(src, c0 ^ 16u, dst);
+  dma16<2048>(src, c0 ^ 32u, dst);
+  dma16<3072>(src, c0 ^ 48u, dst);
 }
 __device__ __forceinline__ void dma4(const void *base, uint32_t off, void *dst) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
