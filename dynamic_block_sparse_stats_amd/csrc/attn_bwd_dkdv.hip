@@ -23,10 +23,12 @@ constexpr int kDB = 128;
 //   * the dS wave (w >= 4) holds V as B operand, forms dP = dO V^T and accumulates
 //     dK^T += Q^T dS with dS = P (dP - delta).
 // The two waves of a pair share a SIMD.  Each unit has two barriers: after the first the
-// P wave forms S and P while the dS wave forms dP and then the dK product of the previous
-// unit (so the P wave's exponentials overlap MFMAs); after the second (P published) the P
-// wave runs its dV product while the dS wave forms dS, which it keeps for the next unit.
-// One step past the last unit finishes the last dK product.
+// P wave forms S and P (its lse values read before the S product, so the exponentials never
+// wait on LDS) while the dS wave forms dP and then the dK product of the previous unit (the
+// first operands of which it reads before dP), so the P wave's exponentials overlap MFMAs;
+// after the second (P published) the P wave runs its dV product while the dS wave forms dS,
+// which it keeps for the next unit.  One step past the last unit finishes the last dK
+// product.
 //
 // Query units stream through a three-stage LDS ring filled by direct global->LDS copies
 // (global_load_lds_dwordx4: lane l of one instruction lands at +16*l, so the XOR swizzle
