@@ -16,10 +16,10 @@
 //     [64 keys][128] float16, XOR-swizzled by 16-byte chunk; K rows are read directly, V^T
 //     with transposing LDS reads (ds_read_b64_tr_b16);
 //   * the two waves of a SIMD run half a unit apart (the late one finishes the previous
-//     unit's PV product, then issues its copies, while the early one issues its copies and
-//     forms its scores), each wave raises its issue priority while it forms the scores its
-//     softmax waits for, and each reads the operands of its next group of MFMAs while the
-//     current group runs;
+//     unit's PV product and forms its scores, then issues its copies, while the early one
+//     issues its copies and forms its scores), each wave raises its issue priority while it
+//     forms the scores its softmax waits for, and each reads the operands of its next group
+//     of MFMAs while the current group runs;
 //   * the softmax weights go to the PV product as float16 scaled by 2^10 (11-bit
 //     significands where bf16 has 8: at 2K, value rows reach |v| ~ 20 and the PV sums
 //     cancel, so bf16 weights cost ~3e-2 absolute); the row sum adds the same float16
@@ -260,13 +260,13 @@ __device__ __forceinline__ void fwd_waves(
       const bool unit_u = u < issued;
       const uint32_t st = fwd_stage_addr<S>();
       if constexpr (LATE) {
-        // the late wave issues its copies after its PV product, so that right after the
+        // the late wave issues its copies at the end of its step, so that right after the
         // barrier the early waves' copies and score products go first
         const uint32_t prev = fwd_stage_addr<(S + kStages - 1) % kStages>();
         if (active) fwd_values(w, (u == 0 ? st : prev) + 16384, lane);
+        if (unit_u && active) fwd_scores(w, st, lane, scale_log2e);
         issue(fwd_stage<(S + 2) % kStages>());
         if (!unit_u) return false;
-        if (active) fwd_scores(w, st, lane, scale_log2e);
       } else {
         issue(fwd_stage<(S + 2) % kStages>());
         if (!unit_u) return false;
