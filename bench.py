@@ -36,9 +36,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SOURCES = {"attn_fwd": "attn_fwd.hip", "bwd_dkdv": "attn_bwd_dkdv.hip",
                   "bwd_dq": "attn_bwd.hip"}
 MEASURED_TRAFFIC = {
-    ("attn_fwd", "2k-train-64x104x128"): ("6ddb368f863db32e", 30.773e12),
-    ("bwd_dkdv", "2k-train-64x104x128"): ("20352c6fcd989e62", 51.061e12),
-    ("bwd_dq", "2k-train-64x104x128"): ("5844853f8407c16f", 30.762e12),
+    ("attn_fwd", "2k-train-64x104x128"): ("192c0ff358424f69", 30.777e12),
+    ("bwd_dkdv", "2k-train-64x104x128"): ("20352c6fcd989e62", 49.600e12),
+    ("bwd_dq", "2k-train-64x104x128"): ("5844853f8407c16f", 30.766e12),
 }
 
 
