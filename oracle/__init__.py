@@ -290,6 +290,8 @@ def attn_bwd(plan: HeadPlan, q, k, v, dout, scale=None, rows=None, with_mag=Fals
         ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p,
         ctypes.c_int] + [ctypes.c_void_p] * 6
     rws = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    if rws is not None and len(np.unique(rws)) != len(rws):
+        raise ValueError("attn_bwd: rows must not repeat a token")
     lib.orc_attn_bwd(N, D, q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
                      plan.perm.ctypes.data, plan.inv.ctypes.data, plan.bstart.ctypes.data,
                      plan.bsize.ctypes.data, plan.bof.ctypes.data, plan.nb,

@@ -500,8 +500,11 @@ int orc_attn_fwd(int N, int D, const double *q, const double *k, const double *v
  *   dv_y += P_xy do_x, dS_xy = P_xy (do_x . v_y - delta_x),
  *   dq_x += scale dS_xy k_y, dk_y += scale dS_xy q_x.
  * o and lse are recomputed here in float64.  rows: the query tokens whose terms are
- * summed (NULL = all); with an upstream gradient that is zero on every other token this
- * is the full gradient.  dq, dk, dv [N][D] are overwritten (dq only on the listed rows).
+ * summed (NULL = all; no token listed twice); with an upstream gradient that is zero on
+ * every other token this is the full gradient.  dq, dk, dv [N][D] are overwritten (dq
+ * only on the listed rows).  dq is summed one query row at a time, dk and dv one key
+ * token at a time (each sum over its own terms only), so rows and key tokens are
+ * independent and are spread over OpenMP threads.
  *
  * mq, mk, mv [N][D] (all three or none): how far each gradient moves, to first order,
  * when every weight P_xy and every dS_xy is perturbed by a relative amount of at most 1
@@ -519,10 +522,9 @@ int orc_attn_bwd(int N, int D, const double *q, const double *k, const double *v
                  double *dk, double *dv, double *mq, double *mk, double *mv)
 {
     int total = rows ? nrows : N;
-    int *keys = malloc(sizeof(int) * (size_t)N);
-    double *s = malloc(sizeof(double) * (size_t)N);
-    double *dsv = malloc(sizeof(double) * (size_t)N);
-    double *o = malloc(sizeof(double) * (size_t)D);
+    double *lse = malloc(sizeof(double) * (size_t)N);
+    double *delta = malloc(sizeof(double) * (size_t)N);
+    double *sabs = malloc(sizeof(double) * (size_t)N);
     memset(dq, 0, sizeof(double) * (size_t)N * D);
     memset(dk, 0, sizeof(double) * (size_t)N * D);
     memset(dv, 0, sizeof(double) * (size_t)N * D);
@@ -531,59 +533,131 @@ int orc_attn_bwd(int N, int D, const double *q, const double *k, const double *v
         memset(mk, 0, sizeof(double) * (size_t)N * D);
         memset(mv, 0, sizeof(double) * (size_t)N * D);
     }
+    /* Query side, one listed row x at a time: lse_x, o_x, delta_x, dS_xy over the row's
+     * key tokens, dq_x = scale sum_y dS_xy k_y, and S_x. */
+#pragma omp parallel
+    {
+        int *keys = malloc(sizeof(int) * (size_t)N);
+        double *s = malloc(sizeof(double) * (size_t)N);
+        double *dsv = malloc(sizeof(double) * (size_t)N);
+        double *o = malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(dynamic, 16)
+        for (int r = 0; r < total; ++r) {
+            int x = rows ? rows[r] : r;
+            const double *qx = q + (size_t)x * D, *dox = dout + (size_t)x * D;
+            int nk = key_tokens(x, perm, inv, blk_start, blk_size, blk_of, count, cols, nb, keys);
+            double mx = -INFINITY;
+            for (int y = 0; y < nk; ++y) {
+                double acc = 0;
+                for (int c = 0; c < D; ++c) acc += qx[c] * k[(size_t)keys[y] * D + c];
+                s[y] = scale * acc;
+                if (s[y] > mx) mx = s[y];
+            }
+            double z = 0;
+            for (int y = 0; y < nk; ++y) z += exp(s[y] - mx);
+            double l = mx + log(z);
+            for (int c = 0; c < D; ++c) o[c] = 0;
+            for (int y = 0; y < nk; ++y) {
+                double p = exp(s[y] - l);
+                for (int c = 0; c < D; ++c) o[c] += p * v[(size_t)keys[y] * D + c];
+            }
+            double dl = 0;
+            for (int c = 0; c < D; ++c) dl += dox[c] * o[c];
+            double sa = 0;
+            for (int y = 0; y < nk; ++y) {
+                const double *vy = v + (size_t)keys[y] * D;
+                double p = exp(s[y] - l);
+                double dp = 0;
+                for (int c = 0; c < D; ++c) dp += dox[c] * vy[c];
+                dsv[y] = p * (dp - dl);
+                sa += fabs(dsv[y]);
+            }
+            for (int y = 0; y < nk; ++y) {
+                const double *ky = k + (size_t)keys[y] * D;
+                for (int c = 0; c < D; ++c) dq[(size_t)x * D + c] += scale * dsv[y] * ky[c];
+                if (mq) {
+                    double w = scale * (fabs(dsv[y]) + exp(s[y] - l) * sa);
+                    for (int c = 0; c < D; ++c) mq[(size_t)x * D + c] += w * fabs(ky[c]);
+                }
+            }
+            lse[x] = l;
+            delta[x] = dl;
+            sabs[x] = sa;
+        }
+        free(keys);
+        free(s);
+        free(dsv);
+        free(o);
+    }
+
+    /* Key side: dv_y = sum_x P_xy do_x and dk_y = scale sum_x dS_xy q_x, summed over the
+     * listed rows x whose query block selected y's block.  The listed rows are grouped by
+     * their query block, and each key block gets the ascending list of query blocks that
+     * selected it and hold listed rows; P_xy and dS_xy are formed again from lse_x and
+     * delta_x exactly as on the query side. */
+    int *rptr = calloc((size_t)nb + 1, sizeof(int));
+    int *rlist = malloc(sizeof(int) * (size_t)(total > 0 ? total : 1));
+    for (int r = 0; r < total; ++r) rptr[blk_of[inv[rows ? rows[r] : r]] + 1]++;
+    for (int i = 0; i < nb; ++i) rptr[i + 1] += rptr[i];
+    int *fill = malloc(sizeof(int) * (size_t)(nb > 0 ? nb : 1));
+    for (int i = 0; i < nb; ++i) fill[i] = rptr[i];
     for (int r = 0; r < total; ++r) {
         int x = rows ? rows[r] : r;
-        const double *qx = q + (size_t)x * D, *dox = dout + (size_t)x * D;
-        int nk = key_tokens(x, perm, inv, blk_start, blk_size, blk_of, count, cols, nb, keys);
-        double mx = -INFINITY;
-        for (int y = 0; y < nk; ++y) {
-            double acc = 0;
-            for (int c = 0; c < D; ++c) acc += qx[c] * k[(size_t)keys[y] * D + c];
-            s[y] = scale * acc;
-            if (s[y] > mx) mx = s[y];
-        }
-        double z = 0;
-        for (int y = 0; y < nk; ++y) z += exp(s[y] - mx);
-        double l = mx + log(z);
-        for (int c = 0; c < D; ++c) o[c] = 0;
-        for (int y = 0; y < nk; ++y) {
-            double p = exp(s[y] - l);
-            for (int c = 0; c < D; ++c) o[c] += p * v[(size_t)keys[y] * D + c];
-        }
-        double delta = 0;
-        for (int c = 0; c < D; ++c) delta += dox[c] * o[c];
-        double sabs = 0;
-        for (int y = 0; y < nk; ++y) {
-            const double *vy = v + (size_t)keys[y] * D;
-            double p = exp(s[y] - l);
-            double dp = 0;
-            for (int c = 0; c < D; ++c) dp += dox[c] * vy[c];
-            dsv[y] = p * (dp - delta);
-            sabs += fabs(dsv[y]);
-        }
-        for (int y = 0; y < nk; ++y) {
-            const double *ky = k + (size_t)keys[y] * D;
-            double p = exp(s[y] - l);
-            double ds = dsv[y];
-            for (int c = 0; c < D; ++c) {
-                dv[(size_t)keys[y] * D + c] += p * dox[c];
-                dq[(size_t)x * D + c] += scale * ds * ky[c];
-                dk[(size_t)keys[y] * D + c] += scale * ds * qx[c];
+        rlist[fill[blk_of[inv[x]]]++] = x;
+    }
+    int *cptr = calloc((size_t)nb + 1, sizeof(int));
+    for (int i = 0; i < nb; ++i)
+        if (rptr[i + 1] > rptr[i])
+            for (int e = 0; e < count[i]; ++e) cptr[cols[(size_t)i * nb + e] + 1]++;
+    for (int j = 0; j < nb; ++j) cptr[j + 1] += cptr[j];
+    int *clist = malloc(sizeof(int) * (size_t)(cptr[nb] > 0 ? cptr[nb] : 1));
+    for (int j = 0; j < nb; ++j) fill[j] = cptr[j];
+    for (int i = 0; i < nb; ++i)
+        if (rptr[i + 1] > rptr[i])
+            for (int e = 0; e < count[i]; ++e) {
+                int j = cols[(size_t)i * nb + e];
+                clist[fill[j]++] = i;
             }
-            if (mq) {
-                double w = scale * (fabs(ds) + p * sabs);
-                for (int c = 0; c < D; ++c) {
-                    mv[(size_t)keys[y] * D + c] += p * fabs(dox[c]);
-                    mq[(size_t)x * D + c] += w * fabs(ky[c]);
-                    mk[(size_t)keys[y] * D + c] += w * fabs(qx[c]);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int j = 0; j < nb; ++j) {
+        for (int u = 0; u < blk_size[j]; ++u) {
+            int y = perm[blk_start[j] + u];
+            const double *ky = k + (size_t)y * D, *vy = v + (size_t)y * D;
+            double *dky = dk + (size_t)y * D, *dvy = dv + (size_t)y * D;
+            for (int e = cptr[j]; e < cptr[j + 1]; ++e) {
+                int i = clist[e];
+                for (int r = rptr[i]; r < rptr[i + 1]; ++r) {
+                    int x = rlist[r];
+                    const double *qx = q + (size_t)x * D, *dox = dout + (size_t)x * D;
+                    double acc = 0;
+                    for (int c = 0; c < D; ++c) acc += qx[c] * ky[c];
+                    double p = exp(scale * acc - lse[x]);
+                    double dp = 0;
+                    for (int c = 0; c < D; ++c) dp += dox[c] * vy[c];
+                    double ds = p * (dp - delta[x]);
+                    for (int c = 0; c < D; ++c) {
+                        dvy[c] += p * dox[c];
+                        dky[c] += scale * ds * qx[c];
+                    }
+                    if (mq) {
+                        double w = scale * (fabs(ds) + p * sabs[x]);
+                        for (int c = 0; c < D; ++c) {
+                            mv[(size_t)y * D + c] += p * fabs(dox[c]);
+                            mk[(size_t)y * D + c] += w * fabs(qx[c]);
+                        }
+                    }
                 }
             }
         }
     }
-    free(keys);
-    free(s);
-    free(dsv);
-    free(o);
+    free(rptr);
+    free(rlist);
+    free(fill);
+    free(cptr);
+    free(clist);
+    free(lse);
+    free(delta);
+    free(sabs);
     return 0;
 }
 
