@@ -296,7 +296,7 @@ def cpu_baseline(wl, cfg, inp, budget_s, views=None, outputs=None):
         "kind": "oracle",
         "sample": (f"head 0 of {wl.name}: full plan in {t_plan:.1f} s; forward of {nrows} "
                    f"seeded query rows in {t_fwd:.1f} s ({cores} OpenMP threads); backward of "
-                   f"{nb_rows} of those rows in {t_bwd:.1f} s (single thread); float64"),
+                   f"{nb_rows} of those rows in {t_bwd:.1f} s ({cores} OpenMP threads); float64"),
         "plan_s_per_head": t_plan,
         "agreement": agree,
     }
