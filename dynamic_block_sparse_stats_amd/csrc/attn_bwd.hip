@@ -39,7 +39,9 @@ __global__ void __launch_bounds__(256)
   constexpr int CH = D / VPC;
   constexpr int RG = 256 / CH;
   constexpr int RPT = kUnit / RG;
-  const int u = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  // heads vary fastest across the grid: the workgroups resident together gather every
+  // head's slice of the same zones' token rows
+  const int u = blockIdx.x / heads, h = blockIdx.x % heads, tid = threadIdx.x;
   const int c = tid % CH, rg = tid / CH;
   const size_t tstride = (size_t)heads * D;
 #pragma unroll
@@ -474,11 +476,12 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
   float *delta = (float *)(ws + L.delta), *lse2 = (float *)(ws + L.lse2);
   const float *lsep = (const float *)(ws + L.lsep), *o32p = (const float *)(ws + L.o32p);
   dim3 ugrid(d.U, d.heads);
+  dim3 pgrid(d.U * d.heads);  // bwd_prep: one-dimensional, heads fastest
   if (d.dtype == PRISM_BF16) {
     typedef uint16_t T;
     {
       TraceScope tr(PRISM_STAGE_BWD_PREP, s);
-      hipLaunchKernelGGL((bwd_prep_kernel<T, 128, true>), ugrid, dim3(256), 0, s, d.N, d.heads,
+      hipLaunchKernelGGL((bwd_prep_kernel<T, 128, true>), pgrid, dim3(256), 0, s, d.N, d.heads,
                          perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop), delta, lse2);
     }
     const int *counters = (const int *)(ws + L.counters);
@@ -506,7 +509,7 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
     const T *qp = (const T *)(ws + L.qp), *kp = (const T *)(ws + L.kp),
             *vp = (const T *)(ws + L.vp), *dop = (const T *)(ws + L.dop);
     if (d.D == 64) {
-      hipLaunchKernelGGL((bwd_prep_kernel<T, 64, false>), ugrid, dim3(256), 0, s, d.N, d.heads,
+      hipLaunchKernelGGL((bwd_prep_kernel<T, 64, false>), pgrid, dim3(256), 0, s, d.N, d.heads,
                          perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop), delta, nullptr);
       hipLaunchKernelGGL((attn_dq_f32_kernel<64>), ugrid, dim3(256), 0, s, d.N, d.U, d.nb_max,
                          d.heads, qp, kp, vp, dop, lsep, delta, unit_blk, bstart, bsize, cnt,
@@ -515,7 +518,7 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
                          d.nb_max, d.heads, qp, kp, vp, dop, lsep, delta, unit_blk, bstart,
                          bsize, tcnt, trows, perm, scale, (T *)dk, (T *)dv);
     } else {
-      hipLaunchKernelGGL((bwd_prep_kernel<T, 128, false>), ugrid, dim3(256), 0, s, d.N,
+      hipLaunchKernelGGL((bwd_prep_kernel<T, 128, false>), pgrid, dim3(256), 0, s, d.N,
                          d.heads, perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop), delta,
                          nullptr);
       hipLaunchKernelGGL((attn_dq_f32_kernel<128>), ugrid, dim3(256), 0, s, d.N, d.U, d.nb_max,

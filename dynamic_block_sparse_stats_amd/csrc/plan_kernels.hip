@@ -75,9 +75,12 @@ template <typename T, int D>
 __global__ void __launch_bounds__(64) zone_stats_kernel(int H, int W, int nzh, int nzw,
                                                         const T *__restrict__ v, size_t tstride,
                                                         size_t hstride, int dmode,
-                                                        double *__restrict__ out, int Z) {
+                                                        double *__restrict__ out, int Z,
+                                                        int heads) {
   constexpr int CPL = D / 64;  // channels per lane
-  const int m = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  // heads vary fastest across the grid, so the workgroups resident together read every
+  // head's slice of the same token rows
+  const int m = blockIdx.x / heads, h = blockIdx.x % heads, lane = threadIdx.x;
   const int zw = m % nzw, zh = (m / nzw) % nzh, zt = m / (nzw * nzh);
   const int c0 = lane * CPL;
   const T *base = v + ((((size_t)zt * kZone) * H + zh * kZone) * W + zw * kZone) * tstride +
@@ -173,17 +176,19 @@ __global__ void __launch_bounds__(64) zone_stats_kernel(int H, int W, int nzh, i
 hipError_t launch_zone_stats(const Dims &d, const void *v, int dmode, double *zstat,
                              hipStream_t s) {
   TraceScope tr(PRISM_STAGE_ZONE_STATS, s);
-  dim3 grid(d.Z, d.heads);
+  dim3 grid(d.Z * d.heads);
   if (d.dtype == PRISM_BF16) {
     hipLaunchKernelGGL((zone_stats_kernel<uint16_t, 128>), grid, dim3(64), 0, s, d.H, d.W,
                        d.nzh, d.nzw, (const uint16_t *)v, d.tok_stride, d.head_stride, dmode,
-                       zstat, d.Z);
+                       zstat, d.Z, d.heads);
   } else if (d.D == 64) {
     hipLaunchKernelGGL((zone_stats_kernel<float, 64>), grid, dim3(64), 0, s, d.H, d.W, d.nzh,
-                       d.nzw, (const float *)v, d.tok_stride, d.head_stride, dmode, zstat, d.Z);
+                       d.nzw, (const float *)v, d.tok_stride, d.head_stride, dmode, zstat, d.Z,
+                       d.heads);
   } else {
     hipLaunchKernelGGL((zone_stats_kernel<float, 128>), grid, dim3(64), 0, s, d.H, d.W, d.nzh,
-                       d.nzw, (const float *)v, d.tok_stride, d.head_stride, dmode, zstat, d.Z);
+                       d.nzw, (const float *)v, d.tok_stride, d.head_stride, dmode, zstat, d.Z,
+                       d.heads);
   }
   return hipGetLastError();
 }
@@ -368,12 +373,14 @@ __global__ void __launch_bounds__(256)
                   const T *v, size_t tstride, size_t hstride, const int *__restrict__ zshape,
                   const int *__restrict__ zblock, int *__restrict__ perm,
                   int *__restrict__ inv, T *qp, T *kp, T *vp, float *__restrict__ qbar,
-                  float *__restrict__ kbar, int Z) {
+                  float *__restrict__ kbar, int Z, int heads) {
   constexpr int VPC = 16 / (int)sizeof(T);  // values per 16-byte chunk
   constexpr int CH = D / VPC;               // chunks per row
   constexpr int RG = 256 / CH;              // rows per pass
   constexpr int RPT = kUnit / RG;           // rows per thread per unit
-  const int m = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  // heads vary fastest across the grid (as in the zone statistics): the workgroups
+  // resident together read every head's slice of the same token rows
+  const int m = blockIdx.x / heads, h = blockIdx.x % heads, tid = threadIdx.x;
   const int zw = m % nzw, zh = (m / nzw) % nzh, zt = m / (nzw * nzh);
   const int code = zshape[(size_t)h * Z + m];
   const int lt = (code >> 4) & 3, lh = (code >> 2) & 3, lw = code & 3;
@@ -382,7 +389,7 @@ __global__ void __launch_bounds__(256)
   const int blk0 = zblock[(size_t)h * (Z + 1) + m];
 
   __shared__ int tok[kZoneTok];
-  __shared__ float psum[RG][D];
+  __shared__ float psum[2][RG][D];
 
   for (int p = tid; p < kZoneTok; p += 256) {
     int beta = p / B, r = p % B;
@@ -397,64 +404,75 @@ __global__ void __launch_bounds__(256)
   }
   __syncthreads();
 
+  // per unit of 64 rows, each thread has its rows of Q, K and V in flight at once; the
+  // block sums of Q and K are reduced together at each block boundary
   const int c = tid % CH, rg = tid / CH;
   const T *src[3] = {q, k, v};
   T *dst[3] = {qp, kp, vp};
   float *bar[2] = {qbar, kbar};
-  for (int x = 0; x < 3; ++x) {
-    float acc[VPC];
+  float acc[2][VPC];
 #pragma unroll
-    for (int e = 0; e < VPC; ++e) acc[e] = 0.f;
-    for (int s = 0; s < kZoneTok / kUnit; ++s) {
-      u32x4 buf[RPT];
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int e = 0; e < VPC; ++e) acc[x][e] = 0.f;
+  for (int s = 0; s < kZoneTok / kUnit; ++s) {
+    u32x4 buf[3][RPT];
+#pragma unroll
+    for (int x = 0; x < 3; ++x)
 #pragma unroll
       for (int rr = 0; rr < RPT; ++rr) {
         int p = s * kUnit + rg + RG * rr;
-        buf[rr] = *reinterpret_cast<const u32x4 *>(src[x] + (size_t)tok[p] * tstride +
-                                                   (size_t)h * hstride + c * VPC);
+        buf[x][rr] = *reinterpret_cast<const u32x4 *>(src[x] + (size_t)tok[p] * tstride +
+                                                      (size_t)h * hstride + c * VPC);
       }
 #pragma unroll
+    for (int x = 0; x < 3; ++x)
+#pragma unroll
       for (int rr = 0; rr < RPT; ++rr) {
         int p = s * kUnit + rg + RG * rr;
-        u32x4 out = buf[rr];
+        u32x4 out = buf[x][rr];
         if constexpr (F16) {  // the attention kernels read float16 copies
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            out[e] = (uint32_t)bf16_to_f16_bits((uint16_t)(buf[rr][e] & 0xffffu)) |
-                     ((uint32_t)bf16_to_f16_bits((uint16_t)(buf[rr][e] >> 16)) << 16);
+            out[e] = (uint32_t)bf16_to_f16_bits((uint16_t)(buf[x][rr][e] & 0xffffu)) |
+                     ((uint32_t)bf16_to_f16_bits((uint16_t)(buf[x][rr][e] >> 16)) << 16);
         }
         *reinterpret_cast<u32x4 *>(dst[x] + ((size_t)h * N + kZoneTok * m + p) * D + c * VPC) =
             out;
         if (x < 2) {
           if constexpr (sizeof(T) == 2) {
-            const uint32_t *w32 = reinterpret_cast<const uint32_t *>(&buf[rr]);
+            const uint32_t *w32 = reinterpret_cast<const uint32_t *>(&buf[x][rr]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              acc[2 * e] += __uint_as_float(w32[e] << 16);
-              acc[2 * e + 1] += __uint_as_float(w32[e] & 0xffff0000u);
+              acc[x][2 * e] += __uint_as_float(w32[e] << 16);
+              acc[x][2 * e + 1] += __uint_as_float(w32[e] & 0xffff0000u);
             }
           } else {
-            const float *f = reinterpret_cast<const float *>(&buf[rr]);
+            const float *f = reinterpret_cast<const float *>(&buf[x][rr]);
 #pragma unroll
-            for (int e = 0; e < VPC; ++e) acc[e] += f[e];
+            for (int e = 0; e < VPC; ++e) acc[x][e] += f[e];
           }
         }
       }
-      // block boundary: reduce the pooled sums over the row groups
-      if (x < 2 && ((s + 1) * kUnit) % B == 0) {
+    // block boundary: reduce the pooled sums of Q and K over the row groups
+    if (((s + 1) * kUnit) % B == 0) {
 #pragma unroll
-        for (int e = 0; e < VPC; ++e) psum[rg][c * VPC + e] = acc[e];
-        __syncthreads();
-        if (tid < D) {
-          float sum = 0.f;
-          for (int g = 0; g < RG; ++g) sum += psum[g][tid];
-          int blk = blk0 + (s * kUnit) / B;
-          bar[x][((size_t)h * nb_max + blk) * D + tid] = sum / (float)B;
-        }
-        __syncthreads();
+      for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int e = 0; e < VPC; ++e) acc[e] = 0.f;
+        for (int e = 0; e < VPC; ++e) psum[x][rg][c * VPC + e] = acc[x][e];
+      __syncthreads();
+      if (tid < 2 * D) {
+        const int x = tid / D, ch = tid % D;
+        float sum = 0.f;
+        for (int g = 0; g < RG; ++g) sum += psum[x][g][ch];
+        int blk = blk0 + (s * kUnit) / B;
+        bar[x][((size_t)h * nb_max + blk) * D + ch] = sum / (float)B;
       }
+      __syncthreads();
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int e = 0; e < VPC; ++e) acc[x][e] = 0.f;
     }
   }
 }
@@ -462,7 +480,7 @@ __global__ void __launch_bounds__(256)
 hipError_t launch_gather(const Dims &d, const void *q, const void *k, const void *v,
                          uint8_t *ws, const Layout &L, hipStream_t s) {
   TraceScope tr(PRISM_STAGE_GATHER, s);
-  dim3 grid(d.Z, d.heads);
+  dim3 grid(d.Z * d.heads);
   const int *zshape = (const int *)(ws + L.pub.zone_shape);
   const int *zblock = (const int *)(ws + L.pub.zone_block);
   int *perm = (int *)(ws + L.pub.perm), *inv = (int *)(ws + L.pub.inv_perm);
@@ -472,19 +490,22 @@ hipError_t launch_gather(const Dims &d, const void *q, const void *k, const void
     hipLaunchKernelGGL((gather_kernel<T, 128, true>), grid, dim3(256), 0, s, d.H, d.W, d.nzh,
                        d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k, (const T *)v,
                        d.tok_stride, d.head_stride, zshape, zblock, perm, inv,
-                       (T *)(ws + L.qp), (T *)(ws + L.kp), (T *)(ws + L.vp), qbar, kbar, d.Z);
+                       (T *)(ws + L.qp), (T *)(ws + L.kp), (T *)(ws + L.vp), qbar, kbar, d.Z,
+                       d.heads);
   } else if (d.D == 64) {
     typedef float T;
     hipLaunchKernelGGL((gather_kernel<T, 64, false>), grid, dim3(256), 0, s, d.H, d.W, d.nzh,
                        d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k, (const T *)v,
                        d.tok_stride, d.head_stride, zshape, zblock, perm, inv,
-                       (T *)(ws + L.qp), (T *)(ws + L.kp), (T *)(ws + L.vp), qbar, kbar, d.Z);
+                       (T *)(ws + L.qp), (T *)(ws + L.kp), (T *)(ws + L.vp), qbar, kbar, d.Z,
+                       d.heads);
   } else {
     typedef float T;
     hipLaunchKernelGGL((gather_kernel<T, 128, false>), grid, dim3(256), 0, s, d.H, d.W, d.nzh,
                        d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k, (const T *)v,
                        d.tok_stride, d.head_stride, zshape, zblock, perm, inv,
-                       (T *)(ws + L.qp), (T *)(ws + L.kp), (T *)(ws + L.vp), qbar, kbar, d.Z);
+                       (T *)(ws + L.qp), (T *)(ws + L.kp), (T *)(ws + L.vp), qbar, kbar, d.Z,
+                       d.heads);
   }
   return hipGetLastError();
 }
