@@ -399,6 +399,9 @@ def test_attn_bwd_rows_subset():
     # sum over keys of dV equals the sum of dO; dK sums to zero
     np.testing.assert_allclose(full[2].sum(0), do.sum(0), atol=1e-10)
     np.testing.assert_allclose(full[1].sum(0), 0, atol=1e-10)
+    # a row listed twice would count its terms twice: refused
+    with pytest.raises(ValueError):
+        oracle.attn_bwd(plan, q, k, v, do, rows=np.concatenate([rows, rows[:1]]))
 
 
 def _dense_grads(q, k, v, do, scale, mask, wf=None, wb=None, wd=None):
