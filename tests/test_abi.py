@@ -72,6 +72,20 @@ def test_rejected_configs(lib, over, code):
     assert lib.prism_last_error().decode() != ""
 
 
+@pytest.mark.parametrize("W,code", [(8 * 8191, 0), (8 * 8192, -2)])
+def test_largest_grid(lib, W, code):
+    """A head holds at most 65535 64-token units.  With 8x8x8 zones the largest grid has
+    8191 zones (65528 units) and is accepted; one zone more is refused before any launch."""
+    cfg = P.make_config(8, 8, W, 1, 128, "bf16", top_k=8, top_p=0.9)
+    out = P.PrismLayout()
+    assert lib.prism_plan_layout(ctypes.byref(cfg), ctypes.byref(out)) == code
+    if code == 0:
+        assert out.N == 8 * 8 * W and out.Z == 8191 and out.nb_max == 8 * 8191
+        assert lib.prism_workspace_bytes(ctypes.byref(cfg)) == out.total > 0
+    else:
+        assert lib.prism_workspace_bytes(ctypes.byref(cfg)) == 0
+
+
 def test_null_and_small_workspace(lib):
     cfg = P.make_config(8, 16, 16, 2, 128, "bf16")
     d = ctypes.c_void_p(256)
