@@ -38,7 +38,7 @@ KERNEL_SOURCES = {"attn_fwd": "attn_fwd.hip", "bwd_dkdv": "attn_bwd_dkdv.hip",
 MEASURED_TRAFFIC = {
     ("attn_fwd", "2k-train-64x104x128"): ("192c0ff358424f69", 30.777e12),
     ("bwd_dkdv", "2k-train-64x104x128"): ("20352c6fcd989e62", 49.600e12),
-    ("bwd_dq", "2k-train-64x104x128"): ("72ff7c563fe5849a", 30.768e12),
+    ("bwd_dq", "2k-train-64x104x128"): ("4b95a96e12497379", 30.768e12),
 }
 
 

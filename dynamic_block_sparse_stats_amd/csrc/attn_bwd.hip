@@ -65,7 +65,8 @@ __global__ void __launch_bounds__(256)
         hv[e] = (uint32_t)bf16_to_f16_bits((uint16_t)(a[e] & 0xffffu)) |
                 ((uint32_t)bf16_to_f16_bits((uint16_t)(a[e] >> 16)) << 16);
       }
-      *reinterpret_cast<u32x4 *>(dop + ((size_t)h * N + p) * D + c * VPC) = hv;
+      __builtin_nontemporal_store(hv,
+                                  reinterpret_cast<u32x4 *>(dop + ((size_t)h * N + p) * D + c * VPC));
     } else {
       const f32x4 o0 = *reinterpret_cast<const f32x4 *>(orow);
 #pragma unroll

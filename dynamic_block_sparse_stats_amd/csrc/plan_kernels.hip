@@ -437,8 +437,9 @@ __global__ void __launch_bounds__(256)
             out[e] = (uint32_t)bf16_to_f16_bits((uint16_t)(buf[x][rr][e] & 0xffffu)) |
                      ((uint32_t)bf16_to_f16_bits((uint16_t)(buf[x][rr][e] >> 16)) << 16);
         }
-        *reinterpret_cast<u32x4 *>(dst[x] + ((size_t)h * N + kZoneTok * m + p) * D + c * VPC) =
-            out;
+        __builtin_nontemporal_store(
+            out, reinterpret_cast<u32x4 *>(dst[x] + ((size_t)h * N + kZoneTok * m + p) * D +
+                                           c * VPC));
         if (x < 2) {
           if constexpr (sizeof(T) == 2) {
             const uint32_t *w32 = reinterpret_cast<const uint32_t *>(&buf[x][rr]);
