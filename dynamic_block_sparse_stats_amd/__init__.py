@@ -36,7 +36,7 @@ class PrismConfig(ctypes.Structure):
                 ("eps", ctypes.c_double), ("score_scale", ctypes.c_float),
                 ("softmax_scale", ctypes.c_float), ("top_k_frac", ctypes.c_float),
                 ("fixed_shape", ctypes.c_int), ("map_exponent", ctypes.c_float),
-                ("density_mode", ctypes.c_int)]
+                ("density_mode", ctypes.c_int), ("max_pairs", ctypes.c_longlong)]
 
     @property
     def N(self) -> int:
@@ -49,12 +49,18 @@ class PrismConfig(ctypes.Structure):
 
 _LAYOUT_FIELDS = ["zone_stats", "audio_stats", "zone_diag", "zone_shape", "zone_block",
                   "block_start", "block_size", "unit_block", "perm", "inv_perm", "qbar",
-                  "kbar", "sel_count", "csr_col", "csc_count", "csc_row", "scores", "total"]
+                  "kbar", "sel_count", "csr_ptr", "csr_col", "csc_count", "csc_ptr", "csc_row",
+                  "scores", "flags", "total"]
 
 
 class PrismLayout(ctypes.Structure):
     _fields_ = [(f, ctypes.c_size_t) for f in _LAYOUT_FIELDS] + [
-        ("N", ctypes.c_int), ("Z", ctypes.c_int), ("nb_max", ctypes.c_int)]
+        ("N", ctypes.c_int), ("Z", ctypes.c_int), ("nb_max", ctypes.c_int),
+        ("pair_cap", ctypes.c_longlong)]
+
+
+# status flags of a head (include/prism.h, PRISM_FLAG_*)
+FLAG_QKV_RANGE, FLAG_SELECTION_OVERFLOW, FLAG_DOUT_RANGE, FLAG_DS_RANGE = 1, 2, 4, 8
 
 
 class PrismError(RuntimeError):
@@ -63,8 +69,9 @@ class PrismError(RuntimeError):
 
 _lib = None
 EXPORTS = ["prism_workspace_bytes", "prism_plan_layout", "prism_plan_view", "prism_plan",
-           "prism_attn_fwd", "prism_attn_bwd", "prism_a2v_norm", "prism_status_string",
-           "prism_last_error", "prism_trace_enable", "prism_trace_read", "prism_stage_name"]
+           "prism_attn_fwd", "prism_attn_bwd", "prism_a2v_norm", "prism_check_flags",
+           "prism_status_string", "prism_last_error", "prism_trace_enable", "prism_trace_read",
+           "prism_stage_name"]
 STAGES = ["audio_stats", "zone_stats", "quantize", "gather", "tiles", "scores", "select",
           "attn_fwd", "bwd_prep", "bwd_dkdv", "bwd_dq"]
 
@@ -94,6 +101,8 @@ def lib():
         L.prism_a2v_norm.argtypes = [vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
                                      ctypes.c_int, vp, vp]
         L.prism_a2v_norm.restype = ctypes.c_int
+        L.prism_check_flags.argtypes = [cfgp, vp, vp, vp]
+        L.prism_check_flags.restype = ctypes.c_int
         L.prism_status_string.argtypes = [ctypes.c_int]
         L.prism_status_string.restype = ctypes.c_char_p
         L.prism_last_error.argtypes = []
@@ -111,13 +120,14 @@ def lib():
 def make_config(T, H, W, num_heads, head_dim, dtype="bf16", min_edge_log2=1, top_k=8,
                 top_p=0.9, tau128=0.5, tau256=0.25, eps=1e-6, score_scale=0.0,
                 softmax_scale=0.0, top_k_frac=0.0, fixed_shape=0, map_exponent=0.0,
-                density_mode=0) -> PrismConfig:
+                density_mode=0, max_pairs=0) -> PrismConfig:
     dt = {"f32": F32, "bf16": BF16, F32: F32, BF16: BF16, torch.float32: F32,
           torch.bfloat16: BF16}[dtype]
     return PrismConfig(T, H, W, num_heads, head_dim, dt, min_edge_log2, int(top_k),
                        float(top_p), float(tau128), float(tau256), float(eps),
                        float(score_scale), float(softmax_scale), float(top_k_frac),
-                       int(fixed_shape), float(map_exponent), int(density_mode))
+                       int(fixed_shape), float(map_exponent), int(density_mode),
+                       int(max_pairs))
 
 
 def shape_code(bT: int, bH: int, bW: int) -> int:
@@ -144,10 +154,19 @@ POLICIES = {
 }
 
 
+def default_max_pairs(n_tokens: int) -> int:
+    """Selection-list capacity per head for the named workload grids: (N/128)^2 block
+    pairs, i.e. every pair of a head whose blocks average 128 tokens or more, or a
+    selection density up to 1/4 of the finest (all-64) partition."""
+    return (n_tokens // 128) ** 2
+
+
 def config_for(wl, **over) -> PrismConfig:
-    """Configuration of a synth.Workload."""
+    """Configuration of a synth.Workload.  The named 720p-2K workloads bound their
+    selection lists at default_max_pairs(N); other grids keep the worst case."""
     kw = dict(dtype=wl.dtype, min_edge_log2=wl.min_edge_log2, top_k=wl.top_k,
-              top_p=wl.top_p)
+              top_p=wl.top_p, max_pairs=default_max_pairs(wl.N) if wl.cid in (1, 2, 3, 4)
+              else 0)
     kw.update(over)
     return make_config(wl.T, wl.H, wl.W, wl.heads, wl.head_dim, **kw)
 
@@ -248,6 +267,17 @@ def a2v_norm(x, out=None, stream=None):
     return out
 
 
+def check_flags(cfg, ws, stream=None):
+    """Waits for the stream, then returns the per-head status flags (a list of ints; see
+    FLAG_*) of the workspace; prism_check_flags."""
+    flags = (ctypes.c_uint32 * cfg.num_heads)()
+    st = lib().prism_check_flags(ctypes.byref(cfg), _ws(ws)[0], ctypes.addressof(flags),
+                                 _stream(stream))
+    if st not in (0, -6):
+        _check(st, "prism_check_flags")
+    return list(flags)
+
+
 def trace_enable(on: bool = True):
     """Per-stage HIP-event tracing inside the library (see prism_trace_enable)."""
     _check(lib().prism_trace_enable(1 if on else 0), "prism_trace_enable")
@@ -274,7 +304,7 @@ def plan_view(cfg: PrismConfig, ws) -> PrismLayout:
 def plan_views(cfg, ws) -> dict:
     """Typed views of the plan's arrays inside the workspace (see prism_layout)."""
     L = plan_view(cfg, ws)
-    Hh, Z, nb, N, D = cfg.num_heads, L.Z, L.nb_max, L.N, cfg.head_dim
+    Hh, Z, nb, N, D, cap = cfg.num_heads, L.Z, L.nb_max, L.N, cfg.head_dim, L.pair_cap
 
     def view(off, dtype, shape):
         n = int(math.prod(shape))
@@ -295,11 +325,24 @@ def plan_views(cfg, ws) -> dict:
         "qbar": view(L.qbar, torch.float32, (Hh, nb, D)),
         "kbar": view(L.kbar, torch.float32, (Hh, nb, D)),
         "sel_count": view(L.sel_count, torch.int32, (Hh, nb)),
-        "csr_col": view(L.csr_col, torch.int32, (Hh, nb, nb)),
+        "csr_ptr": view(L.csr_ptr, torch.int32, (Hh, nb + 1)),
+        "csr_col": view(L.csr_col, torch.int32, (Hh, cap)),
         "csc_count": view(L.csc_count, torch.int32, (Hh, nb)),
-        "csc_row": view(L.csc_row, torch.int32, (Hh, nb, nb)),
+        "csc_ptr": view(L.csc_ptr, torch.int32, (Hh, nb + 1)),
+        "csc_row": view(L.csc_row, torch.int32, (Hh, cap)),
         "scores": view(L.scores, torch.float32, (nb, nb)),
+        "flags": view(L.flags, torch.int32, (Hh,)),
     }
+
+
+def csr_rows(views, h, which="csr"):
+    """The selection lists of head h as a list of numpy arrays: which = "csr" (key blocks
+    of each query block) or "csc" (query blocks of each key block), for its nb blocks."""
+    nb = int(views["zone_block"][h, -1])
+    cnt = views[f"{which}_count" if which == "csc" else "sel_count"][h, :nb].cpu().numpy()
+    ptr = views[f"{which}_ptr"][h, :nb + 1].cpu().numpy()
+    flat = views["csr_col" if which == "csr" else "csc_row"][h, :int(ptr[nb])].cpu().numpy()
+    return [flat[ptr[i]:ptr[i] + cnt[i]] for i in range(nb)]
 
 
 @dataclass
@@ -315,6 +358,9 @@ class PrismAttention:
         self.lse = None
 
     def plan(self, q, k, v, a2v=None, stream=None):
+        # a new plan invalidates the forward state of the previous one
+        self.o = None
+        self.lse = None
         plan(self.cfg, q, k, v, a2v, self.ws, stream)
 
     def forward(self, o=None, lse=None, stream=None):
@@ -330,15 +376,19 @@ class PrismAttention:
 
     def backward(self, dout, dq=None, dk=None, dv=None, stream=None):
         cfg = self.cfg
+        if self.o is None:
+            raise PrismError("backward needs a forward on this workspace since its last plan")
         mk = lambda: torch.empty(cfg.N, cfg.num_heads, cfg.head_dim, dtype=cfg.torch_dtype,
                                  device=self.device)
         dq = mk() if dq is None else dq
         dk = mk() if dk is None else dk
         dv = mk() if dv is None else dv
-        if self.o is None:
-            raise PrismError("backward needs a forward on this workspace first")
         attn_bwd(cfg, self.ws, dout, dq, dk, dv, stream)
         return dq, dk, dv
 
     def views(self):
         return plan_views(self.cfg, self.ws)
+
+    def check(self, stream=None):
+        """Per-head status flags (waits for the stream); all zero on a valid result."""
+        return check_flags(self.cfg, self.ws, stream)

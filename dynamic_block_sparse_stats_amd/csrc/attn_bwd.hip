@@ -27,23 +27,32 @@ constexpr int kDB = 128;
 
 // ============================================================================ prep
 // dO gathered into the permuted row-major layout (float16 for bfloat16 inputs, the operand
-// type of the MFMA passes), delta = rowsum(dO * O) from the float32 output the forward
-// kept; for bfloat16, delta is stored negated (the dP accumulators start from it) and lse
-// as lse * log2(e) (the exp2 argument).
-template <typename T, int D, bool F16>
+// type of the MFMA passes, in rows of DP = 128 with zero padding for a 64-channel head),
+// delta = rowsum(dO * O) from the float32 output the forward kept; for bfloat16, delta is
+// stored negated (the dP accumulators start from it) and lse as lse * log2(e) (the exp2
+// argument).  For bfloat16 it also sets the head's range flags: a dO value outside the
+// float16 range, or a row whose bound |dO_x| (max_y |v_y| + |o_x|) on |dS_xy| =
+// |P_xy (dP_xy - delta_x)| reaches 65504 (P <= 1, |dP_xy| <= |dO_x| |v_y|, |delta_x| <=
+// |dO_x| |o_x|), where the float16 dS the MFMA passes take could overflow.
+template <typename T, int D, bool F16, int DP>
 __global__ void __launch_bounds__(256)
     bwd_prep_kernel(int N, int heads, const int *__restrict__ perm, const T *__restrict__ dout,
                     const float *__restrict__ o32p, const float *__restrict__ lsep,
-                    T *__restrict__ dop, float *__restrict__ delta, float *__restrict__ lse2) {
+                    T *__restrict__ dop, float *__restrict__ delta, float *__restrict__ lse2,
+                    const float *__restrict__ vmax, uint32_t *__restrict__ flags) {
   constexpr int VPC = 16 / (int)sizeof(T);
   constexpr int CH = D / VPC;
   constexpr int RG = 256 / CH;
   constexpr int RPT = kUnit / RG;
+  static_assert(DP == D || (F16 && DP == 2 * D), "padding only for float16 copies");
   // heads vary fastest across the grid: the workgroups resident together gather every
   // head's slice of the same zones' token rows
   const int u = blockIdx.x / heads, h = blockIdx.x % heads, tid = threadIdx.x;
   const int c = tid % CH, rg = tid / CH;
   const size_t tstride = (size_t)heads * D;
+  bool dout_bad = false, ds_bad = false;
+  float vm = 0.f;
+  if constexpr (F16) vm = vmax[h];
 #pragma unroll
   for (int rr = 0; rr < RPT; ++rr) {
     const int row = rg + RG * rr;
@@ -51,8 +60,8 @@ __global__ void __launch_bounds__(256)
     const int token = perm[(size_t)h * N + p];
     const u32x4 a =
         *reinterpret_cast<const u32x4 *>(dout + token * tstride + (size_t)h * D + c * VPC);
-    const float *orow = o32p + ((size_t)h * N + p) * D + c * VPC;
-    float dot = 0.f;
+    const float *orow = o32p + ((size_t)h * N + p) * DP + c * VPC;
+    float dot = 0.f, dd = 0.f, oo = 0.f;
     if constexpr (F16) {
       u32x4 hv;
       const f32x4 o0 = *reinterpret_cast<const f32x4 *>(orow);
@@ -60,13 +69,20 @@ __global__ void __launch_bounds__(256)
       const float ov[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        dot += __uint_as_float(a[e] << 16) * ov[2 * e];
-        dot += __uint_as_float(a[e] & 0xffff0000u) * ov[2 * e + 1];
+        const float lo = __uint_as_float(a[e] << 16), hi = __uint_as_float(a[e] & 0xffff0000u);
+        dot += lo * ov[2 * e];
+        dot += hi * ov[2 * e + 1];
+        dd += lo * lo + hi * hi;
+        oo += ov[2 * e] * ov[2 * e] + ov[2 * e + 1] * ov[2 * e + 1];
+        dout_bad |= (a[e] & 0x7fffu) >= 0x4780u || ((a[e] >> 16) & 0x7fffu) >= 0x4780u;
         hv[e] = (uint32_t)bf16_to_f16_bits((uint16_t)(a[e] & 0xffffu)) |
                 ((uint32_t)bf16_to_f16_bits((uint16_t)(a[e] >> 16)) << 16);
       }
-      __builtin_nontemporal_store(hv,
-                                  reinterpret_cast<u32x4 *>(dop + ((size_t)h * N + p) * D + c * VPC));
+      T *drow = dop + ((size_t)h * N + p) * DP;
+      __builtin_nontemporal_store(hv, reinterpret_cast<u32x4 *>(drow + c * VPC));
+      if constexpr (DP > D)
+        __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u},
+                                    reinterpret_cast<u32x4 *>(drow + (c + CH) * VPC));
     } else {
       const f32x4 o0 = *reinterpret_cast<const f32x4 *>(orow);
 #pragma unroll
@@ -75,6 +91,14 @@ __global__ void __launch_bounds__(256)
     }
 #pragma unroll
     for (int off = 1; off < CH; off <<= 1) dot += __shfl_xor(dot, off, 64);
+    if constexpr (F16) {
+#pragma unroll
+      for (int off = 1; off < CH; off <<= 1) {
+        dd += __shfl_xor(dd, off, 64);
+        oo += __shfl_xor(oo, off, 64);
+      }
+      ds_bad |= sqrtf(dd) * (vm + sqrtf(oo)) >= 65504.f;
+    }
     if (c == 0) {
       if constexpr (F16) {
         delta[(size_t)h * N + p] = -dot;
@@ -84,6 +108,18 @@ __global__ void __launch_bounds__(256)
       }
     }
   }
+  if constexpr (F16) {
+    const bool any_dout = __any(dout_bad), any_ds = __any(ds_bad);
+    if ((tid & 63) == 0 && (any_dout || any_ds))
+      atomicOr(flags + h, (any_dout ? (uint32_t)PRISM_FLAG_DOUT_RANGE : 0u) |
+                              (any_ds ? (uint32_t)PRISM_FLAG_DS_RANGE : 0u));
+  }
+}
+
+// The backward's flags (dO range, dS bound) start clear on every backward.
+__global__ void clear_bwd_flags_kernel(int heads, uint32_t *__restrict__ flags) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h < heads) flags[h] &= ~(uint32_t)(PRISM_FLAG_DOUT_RANGE | PRISM_FLAG_DS_RANGE);
 }
 
 // ============================================================================ dQ (bf16)
@@ -195,8 +231,9 @@ __device__ __forceinline__ void dq_waves(
     const float *__restrict__ lse2, const float *__restrict__ ndelta,
     const int *__restrict__ unit_blk, const int *__restrict__ blk_start,
     const int *__restrict__ blk_size, const int *__restrict__ sel_count,
-    const int *__restrict__ csr_col, const int *__restrict__ perm, float scale,
-    float scale_log2e, uint16_t *__restrict__ dq) {
+    const int *__restrict__ csr_ptr, const int *__restrict__ csr_col, long long cap,
+    const int *__restrict__ perm, float scale, float scale_log2e, int dio,
+    const uint32_t *__restrict__ flags, uint16_t *__restrict__ dq) {
   const int l32 = lane & 31, hh = lane >> 5;
   // copies of this wave: K rows 16w.. (early waves) or V rows 16(w-4).. (late waves)
   const int wq = wave & (QW / 2 - 1);
@@ -213,8 +250,8 @@ __device__ __forceinline__ void dq_waves(
     const int blk = unit_blk[(size_t)h * U + u0];
     const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
     BlockUnits pre;
-    pre.init(csr_col + ((size_t)h * nb_max + blk) * nb_max,
-             sel_count[(size_t)h * nb_max + blk], bs, bz, lane);
+    pre.init(csr_col + (size_t)h * cap + csr_ptr[(size_t)h * (nb_max + 1) + blk],
+             sel_count[(size_t)h * nb_max + blk], bs, bz, lane, blk);
     const int row0 = u0 * kUnit + wave * 32;
     DqState w;
     w.lse2 = 0.f;
@@ -292,7 +329,9 @@ __device__ __forceinline__ void dq_waves(
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the trailing repeat copies
     if (!active) continue;
     const int token = perm[(size_t)h * N + row0 + l32];
-    uint16_t *qrow = dq + ((size_t)token * heads + h) * kDB;
+    uint16_t *qrow = dq + ((size_t)token * heads + h) * dio;
+    // any status flag of the head (operand range, selection overflow, dS bound): NaN
+    const bool poisoned = flags[h] != 0u;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -302,7 +341,8 @@ __device__ __forceinline__ void dq_waves(
                       ((uint32_t)f32_to_bf16(w.acc[dt][4 * v4 + 1] * scale) << 16);
         uint32_t hi = (uint32_t)f32_to_bf16(w.acc[dt][4 * v4 + 2] * scale) |
                       ((uint32_t)f32_to_bf16(w.acc[dt][4 * v4 + 3] * scale) << 16);
-        *reinterpret_cast<u32x2 *>(qrow + d0) = u32x2{lo, hi};
+        if (poisoned) lo = hi = kNaNbf16x2;
+        if (32 * dt < dio) *reinterpret_cast<u32x2 *>(qrow + d0) = u32x2{lo, hi};
       }
   }
 }
@@ -314,21 +354,22 @@ __global__ void __launch_bounds__(QW * 64)
                         const uint16_t *__restrict__ dop, const float *__restrict__ lse2,
                         const float *__restrict__ ndelta, const int *__restrict__ unit_blk,
                         const int *__restrict__ blk_start, const int *__restrict__ blk_size,
-                        const int *__restrict__ sel_count, const int *__restrict__ csr_col,
-                        const int *__restrict__ perm, float scale, float scale_log2e,
-                        uint16_t *__restrict__ dq) {
+                        const int *__restrict__ sel_count, const int *__restrict__ csr_ptr,
+                        const int *__restrict__ csr_col, long long cap,
+                        const int *__restrict__ perm, float scale, float scale_log2e, int dio,
+                        const uint32_t *__restrict__ flags, uint16_t *__restrict__ dq) {
   // the wave index is uniform in the wave; the two roles run the same sequence of barriers
   // and copies
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int ntiles = *tile_count;
   if (wave < QW / 2)
     dq_waves<false>(wave, lane, N, U, nb_max, heads, tiles, ntiles, qp, kp, vp, dop, lse2,
-                    ndelta, unit_blk, blk_start, blk_size, sel_count, csr_col, perm, scale,
-                    scale_log2e, dq);
+                    ndelta, unit_blk, blk_start, blk_size, sel_count, csr_ptr, csr_col, cap,
+                    perm, scale, scale_log2e, dio, flags, dq);
   else
     dq_waves<true>(wave, lane, N, U, nb_max, heads, tiles, ntiles, qp, kp, vp, dop, lse2,
-                   ndelta, unit_blk, blk_start, blk_size, sel_count, csr_col, perm, scale,
-                   scale_log2e, dq);
+                   ndelta, unit_blk, blk_start, blk_size, sel_count, csr_ptr, csr_col, cap,
+                   perm, scale, scale_log2e, dio, flags, dq);
 }
 
 // ============================================================================ float32
@@ -341,15 +382,17 @@ __global__ void __launch_bounds__(256)
                        const float *__restrict__ dop, const float *__restrict__ lsep,
                        const float *__restrict__ delta, const int *__restrict__ unit_blk,
                        const int *__restrict__ blk_start, const int *__restrict__ blk_size,
-                       const int *__restrict__ sel_count, const int *__restrict__ csr_col,
-                       const int *__restrict__ perm, float scale, float *__restrict__ dq) {
+                       const int *__restrict__ sel_count, const int *__restrict__ csr_ptr,
+                       const int *__restrict__ csr_col, long long cap,
+                       const int *__restrict__ perm, float scale,
+                       const uint32_t *__restrict__ flags, float *__restrict__ dq) {
   constexpr int DP = D / 4;
   __shared__ float ks[kUnit][D], vs[kUnit][D];
   const int u0 = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int r = tid >> 2, part = tid & 3;
   const int blk = unit_blk[(size_t)h * U + u0];
   const int ncols = sel_count[(size_t)h * nb_max + blk];
-  const int *cols = csr_col + ((size_t)h * nb_max + blk) * nb_max;
+  const int *cols = csr_col + (size_t)h * cap + csr_ptr[(size_t)h * (nb_max + 1) + blk];
   const int prow = u0 * kUnit + r;
   float qv[DP], dov[DP];
   double acc[DP];
@@ -390,9 +433,11 @@ __global__ void __launch_bounds__(256)
     }
   }
   const int token = perm[(size_t)h * N + prow];
+  const bool poisoned = flags[h] != 0u;
 #pragma unroll
   for (int e = 0; e < DP; ++e)
-    dq[((size_t)token * heads + h) * D + part * DP + e] = (float)(acc[e] * scale);
+    reinterpret_cast<uint32_t *>(dq)[((size_t)token * heads + h) * D + part * DP + e] =
+        poisoned ? kNaNf32 : __float_as_uint((float)(acc[e] * scale));
 }
 
 // dK/dV: one workgroup per 64-key unit, 4 threads per key row, over the transposed lists.
@@ -403,8 +448,10 @@ __global__ void __launch_bounds__(256)
                          const float *__restrict__ dop, const float *__restrict__ lsep,
                          const float *__restrict__ delta, const int *__restrict__ unit_blk,
                          const int *__restrict__ blk_start, const int *__restrict__ blk_size,
-                         const int *__restrict__ csc_count, const int *__restrict__ csc_row,
-                         const int *__restrict__ perm, float scale, float *__restrict__ dk,
+                         const int *__restrict__ csc_count, const int *__restrict__ csc_ptr,
+                         const int *__restrict__ csc_row, long long cap,
+                         const int *__restrict__ perm, float scale,
+                         const uint32_t *__restrict__ flags, float *__restrict__ dk,
                          float *__restrict__ dv) {
   constexpr int DP = D / 4;
   __shared__ float qs[kUnit][D], ds_[kUnit][D];
@@ -412,7 +459,7 @@ __global__ void __launch_bounds__(256)
   const int r = tid >> 2, part = tid & 3;
   const int jblk = unit_blk[(size_t)h * U + u0];
   const int nq = csc_count[(size_t)h * nb_max + jblk];
-  const int *qlist = csc_row + ((size_t)h * nb_max + jblk) * nb_max;
+  const int *qlist = csc_row + (size_t)h * cap + csc_ptr[(size_t)h * (nb_max + 1) + jblk];
   const int krow = u0 * kUnit + r;
   float kv[DP], vv[DP];
   double gk[DP], gv[DP];
@@ -456,10 +503,13 @@ __global__ void __launch_bounds__(256)
     }
   }
   const int token = perm[(size_t)h * N + krow];
+  const bool poisoned = flags[h] != 0u;
 #pragma unroll
   for (int e = 0; e < DP; ++e) {
-    dk[((size_t)token * heads + h) * D + part * DP + e] = (float)(gk[e] * scale);
-    dv[((size_t)token * heads + h) * D + part * DP + e] = (float)gv[e];
+    const size_t at = ((size_t)token * heads + h) * D + part * DP + e;
+    reinterpret_cast<uint32_t *>(dk)[at] =
+        poisoned ? kNaNf32 : __float_as_uint((float)(gk[e] * scale));
+    reinterpret_cast<uint32_t *>(dv)[at] = poisoned ? kNaNf32 : __float_as_uint((float)gv[e]);
   }
 }
 
@@ -471,9 +521,13 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
   const int *bstart = (const int *)(ws + L.pub.block_start);
   const int *bsize = (const int *)(ws + L.pub.block_size);
   const int *cnt = (const int *)(ws + L.pub.sel_count);
+  const int *cptr = (const int *)(ws + L.pub.csr_ptr);
   const int *cols = (const int *)(ws + L.pub.csr_col);
   const int *tcnt = (const int *)(ws + L.pub.csc_count);
+  const int *tptr = (const int *)(ws + L.pub.csc_ptr);
   const int *trows = (const int *)(ws + L.pub.csc_row);
+  uint32_t *flags = (uint32_t *)(ws + L.pub.flags);
+  const float *vmax = (const float *)(ws + L.vmax);
   float *delta = (float *)(ws + L.delta), *lse2 = (float *)(ws + L.lse2);
   const float *lsep = (const float *)(ws + L.lsep), *o32p = (const float *)(ws + L.o32p);
   dim3 ugrid(d.U, d.heads);
@@ -482,8 +536,16 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
     typedef uint16_t T;
     {
       TraceScope tr(PRISM_STAGE_BWD_PREP, s);
-      hipLaunchKernelGGL((bwd_prep_kernel<T, 128, true>), pgrid, dim3(256), 0, s, d.N, d.heads,
-                         perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop), delta, lse2);
+      hipLaunchKernelGGL(clear_bwd_flags_kernel, dim3((d.heads + 255) / 256), dim3(256), 0, s,
+                         d.heads, flags);
+      if (d.D == 64)
+        hipLaunchKernelGGL((bwd_prep_kernel<T, 64, true, 128>), pgrid, dim3(256), 0, s, d.N,
+                           d.heads, perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop), delta,
+                           lse2, vmax, flags);
+      else
+        hipLaunchKernelGGL((bwd_prep_kernel<T, 128, true, 128>), pgrid, dim3(256), 0, s, d.N,
+                           d.heads, perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop), delta,
+                           lse2, vmax, flags);
     }
     const int *counters = (const int *)(ws + L.counters);
     const float sl2e = scale * 1.4426950408889634f;
@@ -493,42 +555,39 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
     const int2 *tiles = (const int2 *)(ws + L.tiles), *btiles = (const int2 *)(ws + L.btiles);
     {
       TraceScope tr(PRISM_STAGE_BWD_DKDV, s);
-      launch_dkdv_bf16(maxt, s, d.N, d.U, d.nb_max, d.heads, tiles, counters, qp, kp, vp, dop,
-                       lse2, delta, unit_blk, bstart, bsize, tcnt, trows, perm, scale, sl2e,
-                       (T *)dk, (T *)dv);
+      (void)launch_dkdv_bf16(maxt, s, d.N, d.U, d.nb_max, d.heads, tiles, counters, qp, kp, vp, dop,
+                       lse2, delta, unit_blk, bstart, bsize, tcnt, tptr, trows, d.cap, perm,
+                       scale, sl2e, d.D, flags, (T *)dk, (T *)dv);
     }
     {
       TraceScope tr(PRISM_STAGE_BWD_DQ, s);
       const int grid = resident_grid((const void *)attn_dq_bf16_kernel, QW * 64, maxt);
       hipLaunchKernelGGL(attn_dq_bf16_kernel, dim3(grid), dim3(QW * 64), 0, s, d.N, d.U,
                          d.nb_max, d.heads, btiles, counters + 1, qp, kp, vp, dop, lse2, delta,
-                         unit_blk, bstart, bsize, cnt, cols, perm, scale, sl2e, (T *)dq);
+                         unit_blk, bstart, bsize, cnt, cptr, cols, d.cap, perm, scale, sl2e,
+                         d.D, flags, (T *)dq);
     }
   } else {
     typedef float T;
     TraceScope tr(PRISM_STAGE_BWD_DKDV, s);
     const T *qp = (const T *)(ws + L.qp), *kp = (const T *)(ws + L.kp),
             *vp = (const T *)(ws + L.vp), *dop = (const T *)(ws + L.dop);
+#define PRISM_BWD_F32(D)                                                                      \
+  hipLaunchKernelGGL((bwd_prep_kernel<T, D, false, D>), pgrid, dim3(256), 0, s, d.N, d.heads,   \
+                     perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop), delta, nullptr,     \
+                     nullptr, flags);                                                          \
+  hipLaunchKernelGGL((attn_dq_f32_kernel<D>), ugrid, dim3(256), 0, s, d.N, d.U, d.nb_max,      \
+                     d.heads, qp, kp, vp, dop, lsep, delta, unit_blk, bstart, bsize, cnt,      \
+                     cptr, cols, d.cap, perm, scale, flags, (T *)dq);                          \
+  hipLaunchKernelGGL((attn_dkdv_f32_kernel<D>), ugrid, dim3(256), 0, s, d.N, d.U, d.nb_max,    \
+                     d.heads, qp, kp, vp, dop, lsep, delta, unit_blk, bstart, bsize, tcnt,     \
+                     tptr, trows, d.cap, perm, scale, flags, (T *)dk, (T *)dv)
     if (d.D == 64) {
-      hipLaunchKernelGGL((bwd_prep_kernel<T, 64, false>), pgrid, dim3(256), 0, s, d.N, d.heads,
-                         perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop), delta, nullptr);
-      hipLaunchKernelGGL((attn_dq_f32_kernel<64>), ugrid, dim3(256), 0, s, d.N, d.U, d.nb_max,
-                         d.heads, qp, kp, vp, dop, lsep, delta, unit_blk, bstart, bsize, cnt,
-                         cols, perm, scale, (T *)dq);
-      hipLaunchKernelGGL((attn_dkdv_f32_kernel<64>), ugrid, dim3(256), 0, s, d.N, d.U,
-                         d.nb_max, d.heads, qp, kp, vp, dop, lsep, delta, unit_blk, bstart,
-                         bsize, tcnt, trows, perm, scale, (T *)dk, (T *)dv);
+      PRISM_BWD_F32(64);
     } else {
-      hipLaunchKernelGGL((bwd_prep_kernel<T, 128, false>), pgrid, dim3(256), 0, s, d.N,
-                         d.heads, perm, (const T *)dout, o32p, lsep, (T *)(ws + L.dop), delta,
-                         nullptr);
-      hipLaunchKernelGGL((attn_dq_f32_kernel<128>), ugrid, dim3(256), 0, s, d.N, d.U, d.nb_max,
-                         d.heads, qp, kp, vp, dop, lsep, delta, unit_blk, bstart, bsize, cnt,
-                         cols, perm, scale, (T *)dq);
-      hipLaunchKernelGGL((attn_dkdv_f32_kernel<128>), ugrid, dim3(256), 0, s, d.N, d.U,
-                         d.nb_max, d.heads, qp, kp, vp, dop, lsep, delta, unit_blk, bstart,
-                         bsize, tcnt, trows, perm, scale, (T *)dk, (T *)dv);
+      PRISM_BWD_F32(128);
     }
+#undef PRISM_BWD_F32
   }
   return hipGetLastError();
 }

@@ -236,9 +236,10 @@ __device__ __forceinline__ void dkdv_waves(
     const uint16_t *__restrict__ dop, const float *__restrict__ lse2,
     const float *__restrict__ ndelta, const int *__restrict__ unit_blk,
     const int *__restrict__ blk_start, const int *__restrict__ blk_size,
-    const int *__restrict__ csc_count,
-    const int *__restrict__ csc_row, const int *__restrict__ perm, float scale,
-    float scale_log2e, uint16_t *__restrict__ dk, uint16_t *__restrict__ dv) {
+    const int *__restrict__ csc_count, const int *__restrict__ csc_ptr,
+    const int *__restrict__ csc_row, long long cap, const int *__restrict__ perm, float scale,
+    float scale_log2e, int dio, const uint32_t *__restrict__ flags, uint16_t *__restrict__ dk,
+    uint16_t *__restrict__ dv) {
   const int l32 = lane & 31, hh = lane >> 5;
   const int pair = wave & 3;
   // copies of this wave: Q rows 16w.. (P waves) or dO rows 16(w-4).. (dS waves); waves 0
@@ -264,7 +265,7 @@ __device__ __forceinline__ void dkdv_waves(
     const bool active = pair * 32 < rows;
     const int jblk = unit_blk[(size_t)h * U + u0];
     const int nq = __builtin_amdgcn_readfirstlane(csc_count[(size_t)h * nb_max + jblk]);
-    const int *qlist = csc_row + ((size_t)h * nb_max + jblk) * nb_max;
+    const int *qlist = csc_row + (size_t)h * cap + csc_ptr[(size_t)h * (nb_max + 1) + jblk];
     const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
     // the pair's 32 keys: K^T (P wave) or V^T (dS wave) as B operand (lane = key, 8 dims
     // per k-step)
@@ -343,7 +344,7 @@ __device__ __forceinline__ void dkdv_waves(
 
     workgroup_barrier();  // every wave is done with the previous tile's stages
     if (nq > 0) {
-      pre.init(qlist, nq, bs, bz, lane);
+      pre.init(qlist, nq, bs, bz, lane, jblk);
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // K or V rows and the cursor window are in
       issue(g_stage0);
       issue(g_stage1);
@@ -358,7 +359,9 @@ __device__ __forceinline__ void dkdv_waves(
     // P wave writes dV (P carried 2^10), the dS wave dK (times the softmax scale)
     if (!active) continue;
     const int token = perm[(size_t)h * N + key0 + l32];
-    uint16_t *orow = (PW ? dv : dk) + ((size_t)token * heads + h) * kDB;
+    uint16_t *orow = (PW ? dv : dk) + ((size_t)token * heads + h) * dio;
+    // any status flag of the head (operand range, selection overflow, dS bound): NaN
+    const bool poisoned = flags[h] != 0u;
     const float mul = PW ? 1.f / kPScale : scale;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -370,7 +373,8 @@ __device__ __forceinline__ void dkdv_waves(
                       ((uint32_t)f32_to_bf16(A[4 * v4 + 1] * mul) << 16);
         uint32_t x1 = (uint32_t)f32_to_bf16(A[4 * v4 + 2] * mul) |
                       ((uint32_t)f32_to_bf16(A[4 * v4 + 3] * mul) << 16);
-        *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{x0, x1};
+        if (poisoned) x0 = x1 = kNaNbf16x2;
+        if (32 * dt < dio) *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{x0, x1};
       }
   }
 }
@@ -382,20 +386,22 @@ __global__ void __launch_bounds__(NW * 64)
                           const uint16_t *__restrict__ dop, const float *__restrict__ lse2,
                           const float *__restrict__ ndelta, const int *__restrict__ unit_blk,
                           const int *__restrict__ blk_start, const int *__restrict__ blk_size,
-                          const int *__restrict__ csc_count, const int *__restrict__ csc_row,
-                          const int *__restrict__ perm, float scale, float scale_log2e,
-                          uint16_t *__restrict__ dk, uint16_t *__restrict__ dv) {
+                          const int *__restrict__ csc_count, const int *__restrict__ csc_ptr,
+                          const int *__restrict__ csc_row, long long cap,
+                          const int *__restrict__ perm, float scale, float scale_log2e, int dio,
+                          const uint32_t *__restrict__ flags, uint16_t *__restrict__ dk,
+                          uint16_t *__restrict__ dv) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int ntiles = *tile_count;
   // the two roles run the same sequence of barriers and copies
   if (wave < 4)
     dkdv_waves<true>(wave, lane, N, U, nb_max, heads, tiles, tile_count, ntiles, qp, kp, vp,
-                     dop, lse2, ndelta, unit_blk, blk_start, blk_size, csc_count, csc_row,
-                     perm, scale, scale_log2e, dk, dv);
+                     dop, lse2, ndelta, unit_blk, blk_start, blk_size, csc_count, csc_ptr,
+                     csc_row, cap, perm, scale, scale_log2e, dio, flags, dk, dv);
   else
     dkdv_waves<false>(wave, lane, N, U, nb_max, heads, tiles, tile_count, ntiles, qp, kp, vp,
-                      dop, lse2, ndelta, unit_blk, blk_start, blk_size, csc_count, csc_row,
-                      perm, scale, scale_log2e, dk, dv);
+                      dop, lse2, ndelta, unit_blk, blk_start, blk_size, csc_count, csc_ptr,
+                      csc_row, cap, perm, scale, scale_log2e, dio, flags, dk, dv);
 }
 
 hipError_t launch_dkdv_bf16(int work_items, hipStream_t s, int N, int U, int nb_max, int heads,
@@ -403,12 +409,13 @@ hipError_t launch_dkdv_bf16(int work_items, hipStream_t s, int N, int U, int nb_
                             const uint16_t *kp, const uint16_t *vp, const uint16_t *dop,
                             const float *lse2, const float *ndelta, const int *unit_blk,
                             const int *bstart, const int *bsize, const int *tcnt,
-                            const int *trows, const int *perm, float scale, float sl2e,
+                            const int *tptr, const int *trows, long long cap, const int *perm,
+                            float scale, float sl2e, int dio, const uint32_t *flags,
                             uint16_t *dk, uint16_t *dv) {
   const int grid = resident_grid((const void *)attn_dkdv_bf16_kernel, NW * 64, work_items);
   hipLaunchKernelGGL(attn_dkdv_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, N, U, nb_max,
                      heads, tiles, counters, qp, kp, vp, dop, lse2, ndelta, unit_blk, bstart,
-                     bsize, tcnt, trows, perm, scale, sl2e, dk, dv);
+                     bsize, tcnt, tptr, trows, cap, perm, scale, sl2e, dio, flags, dk, dv);
   return hipGetLastError();
 }
 

@@ -195,8 +195,9 @@ __device__ __forceinline__ void fwd_waves(
     int ntiles, const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
     const uint16_t *__restrict__ vp, const int *__restrict__ unit_blk,
     const int *__restrict__ blk_start, const int *__restrict__ blk_size,
-    const int *__restrict__ sel_count, const int *__restrict__ csr_col,
-    const int *__restrict__ perm, float scale_log2e, uint16_t *__restrict__ out,
+    const int *__restrict__ sel_count, const int *__restrict__ csr_ptr,
+    const int *__restrict__ csr_col, long long cap, const int *__restrict__ perm,
+    float scale_log2e, int dio, const uint32_t *__restrict__ flags, uint16_t *__restrict__ out,
     float *__restrict__ lse_out, float *__restrict__ o32p, float *__restrict__ lsep) {
   const int l32 = lane & 31, hh = lane >> 5;
   // copies of this wave: K rows 16w.. (early waves) or V rows 16(w-4).. (late waves)
@@ -214,8 +215,8 @@ __device__ __forceinline__ void fwd_waves(
     const int blk = unit_blk[(size_t)h * U + u0];
     const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
     BlockUnits pre;  // the issuing cursor; compute only counts units
-    pre.init(csr_col + ((size_t)h * nb_max + blk) * nb_max,
-             sel_count[(size_t)h * nb_max + blk], bs, bz, lane);
+    pre.init(csr_col + (size_t)h * cap + csr_ptr[(size_t)h * (nb_max + 1) + blk],
+             sel_count[(size_t)h * nb_max + blk], bs, bz, lane, blk);
 
     // this wave's 32 query rows as B operands: Q[row][16kk + 8hh .. +8]
     const int row0 = u0 * kUnit + wave * 32;
@@ -293,10 +294,14 @@ __device__ __forceinline__ void fwd_waves(
     // epilogue
     if (!active) continue;
     const double ltot = w.lsum + __shfl_xor(w.lsum, 32, 64);  // the two half waves' keys
+    // a head whose operands left the float16 range or whose selection overflowed its
+    // lists gets NaN outputs
+    const bool poisoned =
+        (flags[h] & (PRISM_FLAG_QKV_RANGE | PRISM_FLAG_SELECTION_OVERFLOW)) != 0u;
     const float inv = (float)(1.0 / ltot);
     const int prow = row0 + l32;
     const int token = perm[(size_t)h * N + prow];
-    uint16_t *orow = out + ((size_t)token * heads + h) * kD;
+    uint16_t *orow = out + ((size_t)token * heads + h) * dio;
     float *frow = o32p + ((size_t)h * N + prow) * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -307,13 +312,20 @@ __device__ __forceinline__ void fwd_waves(
                     a2 = w.o[dt][4 * v4 + 2] * inv, a3 = w.o[dt][4 * v4 + 3] * inv;
         uint32_t lo = (uint32_t)f32_to_bf16(a0) | ((uint32_t)f32_to_bf16(a1) << 16);
         uint32_t hi = (uint32_t)f32_to_bf16(a2) | ((uint32_t)f32_to_bf16(a3) << 16);
-        *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{lo, hi};
-        *reinterpret_cast<f32x4 *>(frow + d0) = f32x4{a0, a1, a2, a3};
+        u32x4 fb = __builtin_bit_cast(u32x4, f32x4{a0, a1, a2, a3});
+        if (poisoned) {
+          lo = hi = kNaNbf16x2;
+          fb = u32x4{kNaNf32, kNaNf32, kNaNf32, kNaNf32};
+        }
+        // a 64-channel head keeps its padded channels (zero) in the float32 copy only
+        if (32 * dt < dio) *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{lo, hi};
+        *reinterpret_cast<u32x4 *>(frow + d0) = fb;
       }
     const float lse = (float)(((double)w.m - kPShift + log2(ltot)) * 0.69314718055994530942);
+    const uint32_t lbits = poisoned ? kNaNf32 : __float_as_uint(lse);
     if (hh == 0) {
-      lse_out[(size_t)h * N + token] = lse;
-      lsep[(size_t)h * N + prow] = lse;
+      reinterpret_cast<uint32_t *>(lse_out)[(size_t)h * N + token] = lbits;
+      reinterpret_cast<uint32_t *>(lsep)[(size_t)h * N + prow] = lbits;
     }
   }
 }
@@ -326,8 +338,9 @@ __global__ void __launch_bounds__(NW * 64)
                          const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
                          const int *__restrict__ unit_blk, const int *__restrict__ blk_start,
                          const int *__restrict__ blk_size, const int *__restrict__ sel_count,
-                         const int *__restrict__ csr_col, const int *__restrict__ perm,
-                         float scale_log2e, uint16_t *__restrict__ out,
+                         const int *__restrict__ csr_ptr, const int *__restrict__ csr_col,
+                         long long cap, const int *__restrict__ perm, float scale_log2e, int dio,
+                         const uint32_t *__restrict__ flags, uint16_t *__restrict__ out,
                          float *__restrict__ lse_out, float *__restrict__ o32p,
                          float *__restrict__ lsep) {
   // the wave index is uniform in the wave: in a scalar register, every branch on it (and on
@@ -337,12 +350,12 @@ __global__ void __launch_bounds__(NW * 64)
   // the two roles run the same sequence of barriers and copies
   if (wave < NW / 2)
     fwd_waves<false>(wave, lane, N, U, nb_max, heads, tiles, ntiles, qp, kp, vp, unit_blk,
-                     blk_start, blk_size, sel_count, csr_col, perm, scale_log2e, out, lse_out,
-                     o32p, lsep);
+                     blk_start, blk_size, sel_count, csr_ptr, csr_col, cap, perm, scale_log2e,
+                     dio, flags, out, lse_out, o32p, lsep);
   else
     fwd_waves<true>(wave, lane, N, U, nb_max, heads, tiles, ntiles, qp, kp, vp, unit_blk,
-                    blk_start, blk_size, sel_count, csr_col, perm, scale_log2e, out, lse_out,
-                    o32p, lsep);
+                    blk_start, blk_size, sel_count, csr_ptr, csr_col, cap, perm, scale_log2e,
+                    dio, flags, out, lse_out, o32p, lsep);
 }
 
 // ---------------------------------------------------------------------------- float32
@@ -355,16 +368,18 @@ __global__ void __launch_bounds__(256)
                         const float *__restrict__ kp, const float *__restrict__ vp,
                         const int *__restrict__ unit_blk, const int *__restrict__ blk_start,
                         const int *__restrict__ blk_size, const int *__restrict__ sel_count,
-                        const int *__restrict__ csr_col, const int *__restrict__ perm,
-                        float scale, float *__restrict__ out, float *__restrict__ lse_out,
-                        float *__restrict__ o32p, float *__restrict__ lsep) {
+                        const int *__restrict__ csr_ptr, const int *__restrict__ csr_col,
+                        long long cap, const int *__restrict__ perm, float scale,
+                        const uint32_t *__restrict__ flags, float *__restrict__ out,
+                        float *__restrict__ lse_out, float *__restrict__ o32p,
+                        float *__restrict__ lsep) {
   constexpr int DP = D / 4;  // dims per thread
   __shared__ float ks[kUnit][D], vs[kUnit][D];
   const int u0 = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int r = tid >> 2, part = tid & 3;
   const int blk = unit_blk[(size_t)h * U + u0];
   const int ncols = sel_count[(size_t)h * nb_max + blk];
-  const int *cols = csr_col + ((size_t)h * nb_max + blk) * nb_max;
+  const int *cols = csr_col + (size_t)h * cap + csr_ptr[(size_t)h * (nb_max + 1) + blk];
   const int prow = u0 * kUnit + r;
   float qv[DP];
   double ov[DP];
@@ -407,16 +422,18 @@ __global__ void __launch_bounds__(256)
     }
   }
   const int token = perm[(size_t)h * N + prow];
+  // a head whose selection overflowed its lists gets NaN outputs
+  const bool poisoned = (flags[h] & PRISM_FLAG_SELECTION_OVERFLOW) != 0u;
 #pragma unroll
   for (int e = 0; e < DP; ++e) {
-    const float x = (float)(ov[e] / l);
-    out[((size_t)token * heads + h) * D + part * DP + e] = x;
-    o32p[((size_t)h * N + prow) * D + part * DP + e] = x;
+    const uint32_t x = poisoned ? kNaNf32 : __float_as_uint((float)(ov[e] / l));
+    reinterpret_cast<uint32_t *>(out)[((size_t)token * heads + h) * D + part * DP + e] = x;
+    reinterpret_cast<uint32_t *>(o32p)[((size_t)h * N + prow) * D + part * DP + e] = x;
   }
   if (part == 0) {
-    const float ls = (float)(m + log(l));
-    lse_out[(size_t)h * N + token] = ls;
-    lsep[(size_t)h * N + prow] = ls;
+    const uint32_t ls = poisoned ? kNaNf32 : __float_as_uint((float)(m + log(l)));
+    reinterpret_cast<uint32_t *>(lse_out)[(size_t)h * N + token] = ls;
+    reinterpret_cast<uint32_t *>(lsep)[(size_t)h * N + prow] = ls;
   }
 }
 
@@ -426,8 +443,10 @@ hipError_t launch_attn_fwd(const Dims &d, float scale, uint8_t *ws, const Layout
   const int *bstart = (const int *)(ws + L.pub.block_start);
   const int *bsize = (const int *)(ws + L.pub.block_size);
   const int *cnt = (const int *)(ws + L.pub.sel_count);
+  const int *cptr = (const int *)(ws + L.pub.csr_ptr);
   const int *cols = (const int *)(ws + L.pub.csr_col);
   const int *perm = (const int *)(ws + L.pub.perm);
+  const uint32_t *flags = (const uint32_t *)(ws + L.pub.flags);
   float *o32p = (float *)(ws + L.o32p), *lsep = (float *)(ws + L.lsep);
   TraceScope tr(PRISM_STAGE_ATTN_FWD, s);
   if (d.dtype == PRISM_BF16) {
@@ -437,20 +456,20 @@ hipError_t launch_attn_fwd(const Dims &d, float scale, uint8_t *ws, const Layout
     hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, d.N, d.U,
                        d.nb_max, d.heads, (const int2 *)(ws + L.btiles), counters + 1,
                        (const uint16_t *)(ws + L.qp), (const uint16_t *)(ws + L.kp),
-                       (const uint16_t *)(ws + L.vp), unit_blk, bstart, bsize, cnt, cols, perm,
-                       sl2e, (uint16_t *)o, lse, o32p, lsep);
+                       (const uint16_t *)(ws + L.vp), unit_blk, bstart, bsize, cnt, cptr, cols,
+                       d.cap, perm, sl2e, d.D, flags, (uint16_t *)o, lse, o32p, lsep);
   } else {
     dim3 grid(d.U, d.heads);
     if (d.D == 64)
       hipLaunchKernelGGL((attn_fwd_f32_kernel<64>), grid, dim3(256), 0, s, d.N, d.U, d.nb_max,
                          d.heads, (const float *)(ws + L.qp), (const float *)(ws + L.kp),
-                         (const float *)(ws + L.vp), unit_blk, bstart, bsize, cnt, cols, perm,
-                         scale, (float *)o, lse, o32p, lsep);
+                         (const float *)(ws + L.vp), unit_blk, bstart, bsize, cnt, cptr, cols,
+                         d.cap, perm, scale, flags, (float *)o, lse, o32p, lsep);
     else
       hipLaunchKernelGGL((attn_fwd_f32_kernel<128>), grid, dim3(256), 0, s, d.N, d.U, d.nb_max,
                          d.heads, (const float *)(ws + L.qp), (const float *)(ws + L.kp),
-                         (const float *)(ws + L.vp), unit_blk, bstart, bsize, cnt, cols, perm,
-                         scale, (float *)o, lse, o32p, lsep);
+                         (const float *)(ws + L.vp), unit_blk, bstart, bsize, cnt, cptr, cols,
+                         d.cap, perm, scale, flags, (float *)o, lse, o32p, lsep);
   }
   return hipGetLastError();
 }

@@ -177,7 +177,11 @@ hipError_t launch_zone_stats(const Dims &d, const void *v, int dmode, double *zs
                              hipStream_t s) {
   TraceScope tr(PRISM_STAGE_ZONE_STATS, s);
   dim3 grid(d.Z * d.heads);
-  if (d.dtype == PRISM_BF16) {
+  if (d.dtype == PRISM_BF16 && d.D == 64) {
+    hipLaunchKernelGGL((zone_stats_kernel<uint16_t, 64>), grid, dim3(64), 0, s, d.H, d.W,
+                       d.nzh, d.nzw, (const uint16_t *)v, d.tok_stride, d.head_stride, dmode,
+                       zstat, d.Z, d.heads);
+  } else if (d.dtype == PRISM_BF16) {
     hipLaunchKernelGGL((zone_stats_kernel<uint16_t, 128>), grid, dim3(64), 0, s, d.H, d.W,
                        d.nzh, d.nzw, (const uint16_t *)v, d.tok_stride, d.head_stride, dmode,
                        zstat, d.Z, d.heads);
@@ -282,8 +286,15 @@ __global__ void __launch_bounds__(kQuantThreads)
                     int *__restrict__ zshape,
                     int *__restrict__ zblock, double *__restrict__ zdiag,
                     int *__restrict__ blk_start, int *__restrict__ blk_size,
-                    int *__restrict__ unit_blk) {
+                    int *__restrict__ unit_blk, uint32_t *__restrict__ flags,
+                    float *__restrict__ vmax) {
   const int h = blockIdx.x, tid = threadIdx.x;
+  // a new plan starts with clear status flags (the gather and the selection that follow
+  // set them) and no V row norm yet
+  if (tid == 0) {
+    flags[h] = 0u;
+    vmax[h] = 0.f;
+  }
   __shared__ double red[2][kQuantThreads / 64];
   __shared__ int scan[kQuantThreads];
   const double *zs = zstat + (size_t)h * Z * 4;
@@ -354,7 +365,8 @@ hipError_t launch_quantize(const Dims &d, const prism_config *cfg, const double 
                      cfg->map_exponent > 0.f ? (double)cfg->map_exponent : 0.5,
                      cfg->fixed_shape, cfg->density_mode, (int *)(ws + L.pub.zone_shape), (int *)(ws + L.pub.zone_block),
                      (double *)(ws + L.pub.zone_diag), (int *)(ws + L.pub.block_start),
-                     (int *)(ws + L.pub.block_size), (int *)(ws + L.pub.unit_block));
+                     (int *)(ws + L.pub.block_size), (int *)(ws + L.pub.unit_block),
+                     (uint32_t *)(ws + L.pub.flags), (float *)(ws + L.vmax));
   return hipGetLastError();
 }
 
@@ -363,21 +375,25 @@ hipError_t launch_quantize(const Dims &d, const prism_config *cfg, const double 
 // block is contiguous, with one partition shared by Q, K and V): zones in raster order,
 // blocks inside a zone in raster order of block coordinates, tokens inside a block in
 // raster order.  One workgroup per (zone, head) writes perm / inv_perm, copies the zone's
-// 512 rows of Q, K, V into the permuted row-major layout (bfloat16 inputs are stored as
-// float16, the operand type of the attention MFMAs, saturated to the float16 range), and
-// forms the float32 block means of Q and K from the input values (digest obstacles and
-// selection sections).
-template <typename T, int D, bool F16>
+// 512 rows of Q, K, V into the permuted row-major layout and forms the float32 block means
+// of Q and K from the input values (digest obstacles and selection sections).
+// bfloat16 inputs are stored as float16, the operand type of the attention MFMAs, in rows
+// of DP = 128 (a 64-channel head is padded with zeros, which add nothing to any product);
+// values outside the float16 range (or not finite) set PRISM_FLAG_QKV_RANGE for the head,
+// and the largest row norm of V is kept for the backward's dS range bound.
+template <typename T, int D, bool F16, int DP>
 __global__ void __launch_bounds__(256)
     gather_kernel(int H, int W, int nzh, int nzw, int N, int nb_max, const T *q, const T *k,
                   const T *v, size_t tstride, size_t hstride, const int *__restrict__ zshape,
                   const int *__restrict__ zblock, int *__restrict__ perm,
                   int *__restrict__ inv, T *qp, T *kp, T *vp, float *__restrict__ qbar,
-                  float *__restrict__ kbar, int Z, int heads) {
+                  float *__restrict__ kbar, int Z, int heads, uint32_t *__restrict__ flags,
+                  float *__restrict__ vmax) {
   constexpr int VPC = 16 / (int)sizeof(T);  // values per 16-byte chunk
   constexpr int CH = D / VPC;               // chunks per row
   constexpr int RG = 256 / CH;              // rows per pass
   constexpr int RPT = kUnit / RG;           // rows per thread per unit
+  static_assert(DP == D || (F16 && DP == 2 * D), "padding only for float16 copies");
   // heads vary fastest across the grid (as in the zone statistics): the workgroups
   // resident together read every head's slice of the same token rows
   const int m = blockIdx.x / heads, h = blockIdx.x % heads, tid = threadIdx.x;
@@ -411,6 +427,8 @@ __global__ void __launch_bounds__(256)
   T *dst[3] = {qp, kp, vp};
   float *bar[2] = {qbar, kbar};
   float acc[2][VPC];
+  bool out_of_range = false;
+  float vnorm2 = 0.f;  // largest squared V row norm seen by this thread's row group
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -431,28 +449,46 @@ __global__ void __launch_bounds__(256)
       for (int rr = 0; rr < RPT; ++rr) {
         int p = s * kUnit + rg + RG * rr;
         u32x4 out = buf[x][rr];
+        T *drow = dst[x] + ((size_t)h * N + kZoneTok * m + p) * DP;
         if constexpr (F16) {  // the attention kernels read float16 copies
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            out[e] = (uint32_t)bf16_to_f16_bits((uint16_t)(buf[x][rr][e] & 0xffffu)) |
-                     ((uint32_t)bf16_to_f16_bits((uint16_t)(buf[x][rr][e] >> 16)) << 16);
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w = buf[x][rr][e];
+            // |x| > 65504 (the bfloat16 values from 65536 up, and Inf / NaN)
+            out_of_range |= (w & 0x7fffu) >= 0x4780u || ((w >> 16) & 0x7fffu) >= 0x4780u;
+            out[e] = (uint32_t)bf16_to_f16_bits((uint16_t)(w & 0xffffu)) |
+                     ((uint32_t)bf16_to_f16_bits((uint16_t)(w >> 16)) << 16);
+          }
+          if constexpr (DP > D)
+            __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u},
+                                        reinterpret_cast<u32x4 *>(drow + (c + CH) * VPC));
         }
-        __builtin_nontemporal_store(
-            out, reinterpret_cast<u32x4 *>(dst[x] + ((size_t)h * N + kZoneTok * m + p) * D +
-                                           c * VPC));
-        if (x < 2) {
-          if constexpr (sizeof(T) == 2) {
-            const uint32_t *w32 = reinterpret_cast<const uint32_t *>(&buf[x][rr]);
+        __builtin_nontemporal_store(out, reinterpret_cast<u32x4 *>(drow + c * VPC));
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t *w32 = reinterpret_cast<const uint32_t *>(&buf[x][rr]);
+          if (x < 2) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               acc[x][2 * e] += __uint_as_float(w32[e] << 16);
               acc[x][2 * e + 1] += __uint_as_float(w32[e] & 0xffff0000u);
             }
           } else {
-            const float *f = reinterpret_cast<const float *>(&buf[x][rr]);
+            // squared norm of this V row: the CH threads of the row are consecutive lanes
+            float ss = 0.f;
 #pragma unroll
-            for (int e = 0; e < VPC; ++e) acc[x][e] += f[e];
+            for (int e = 0; e < 4; ++e) {
+              const float lo = __uint_as_float(w32[e] << 16);
+              const float hi = __uint_as_float(w32[e] & 0xffff0000u);
+              ss += lo * lo + hi * hi;
+            }
+#pragma unroll
+            for (int off = 1; off < CH; off <<= 1) ss += __shfl_xor(ss, off, 64);
+            vnorm2 = fmaxf(vnorm2, ss);
           }
+        } else if (x < 2) {
+          const float *f = reinterpret_cast<const float *>(&buf[x][rr]);
+#pragma unroll
+          for (int e = 0; e < VPC; ++e) acc[x][e] += f[e];
         }
       }
     // block boundary: reduce the pooled sums of Q and K over the row groups
@@ -476,6 +512,16 @@ __global__ void __launch_bounds__(256)
         for (int e = 0; e < VPC; ++e) acc[x][e] = 0.f;
     }
   }
+  if constexpr (F16) {
+    // one flag update and one maximum per wave (non-negative floats order as their bits)
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) vnorm2 = fmaxf(vnorm2, __shfl_xor(vnorm2, off, 64));
+    const bool any_bad = __any(out_of_range);
+    if ((tid & 63) == 0) {
+      if (any_bad) atomicOr(flags + h, (uint32_t)PRISM_FLAG_QKV_RANGE);
+      atomicMax(reinterpret_cast<unsigned int *>(vmax + h), __float_as_uint(sqrtf(vnorm2)));
+    }
+  }
 }
 
 hipError_t launch_gather(const Dims &d, const void *q, const void *k, const void *v,
@@ -486,28 +532,23 @@ hipError_t launch_gather(const Dims &d, const void *q, const void *k, const void
   const int *zblock = (const int *)(ws + L.pub.zone_block);
   int *perm = (int *)(ws + L.pub.perm), *inv = (int *)(ws + L.pub.inv_perm);
   float *qbar = (float *)(ws + L.pub.qbar), *kbar = (float *)(ws + L.pub.kbar);
-  if (d.dtype == PRISM_BF16) {
-    typedef uint16_t T;
-    hipLaunchKernelGGL((gather_kernel<T, 128, true>), grid, dim3(256), 0, s, d.H, d.W, d.nzh,
-                       d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k, (const T *)v,
-                       d.tok_stride, d.head_stride, zshape, zblock, perm, inv,
-                       (T *)(ws + L.qp), (T *)(ws + L.kp), (T *)(ws + L.vp), qbar, kbar, d.Z,
-                       d.heads);
-  } else if (d.D == 64) {
-    typedef float T;
-    hipLaunchKernelGGL((gather_kernel<T, 64, false>), grid, dim3(256), 0, s, d.H, d.W, d.nzh,
-                       d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k, (const T *)v,
-                       d.tok_stride, d.head_stride, zshape, zblock, perm, inv,
-                       (T *)(ws + L.qp), (T *)(ws + L.kp), (T *)(ws + L.vp), qbar, kbar, d.Z,
-                       d.heads);
-  } else {
-    typedef float T;
-    hipLaunchKernelGGL((gather_kernel<T, 128, false>), grid, dim3(256), 0, s, d.H, d.W, d.nzh,
-                       d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k, (const T *)v,
-                       d.tok_stride, d.head_stride, zshape, zblock, perm, inv,
-                       (T *)(ws + L.qp), (T *)(ws + L.kp), (T *)(ws + L.vp), qbar, kbar, d.Z,
-                       d.heads);
-  }
+  uint32_t *flags = (uint32_t *)(ws + L.pub.flags);
+  float *vmax = (float *)(ws + L.vmax);
+#define PRISM_GATHER(T, D, F16, DP)                                                          \
+  hipLaunchKernelGGL((gather_kernel<T, D, F16, DP>), grid, dim3(256), 0, s, d.H, d.W, d.nzh,  \
+                     d.nzw, d.N, d.nb_max, (const T *)q, (const T *)k, (const T *)v,          \
+                     d.tok_stride, d.head_stride, zshape, zblock, perm, inv,                  \
+                     (T *)(ws + L.qp), (T *)(ws + L.kp), (T *)(ws + L.vp), qbar, kbar, d.Z,    \
+                     d.heads, flags, vmax)
+  if (d.dtype == PRISM_BF16 && d.D == 64)
+    PRISM_GATHER(uint16_t, 64, true, 128);
+  else if (d.dtype == PRISM_BF16)
+    PRISM_GATHER(uint16_t, 128, true, 128);
+  else if (d.D == 64)
+    PRISM_GATHER(float, 64, false, 64);
+  else
+    PRISM_GATHER(float, 128, false, 128);
+#undef PRISM_GATHER
   return hipGetLastError();
 }
 

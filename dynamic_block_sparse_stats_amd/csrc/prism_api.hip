@@ -5,6 +5,7 @@
 
 #include <mutex>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "prism_internal.h"
@@ -60,6 +61,26 @@ TraceScope::~TraceScope() {
     g_event_pool.push_back((hipEvent_t)start);
 }
 
+// ---------------------------------------------------------------------------- call order
+// The backward reads the O and lse that the forward left in the workspace, and both passes
+// read the plan.  The library records, per workspace address, the configuration of the
+// last plan and whether a forward has run on it since; a forward on a workspace with no
+// plan of the same configuration, or a backward with no forward since the last plan, is
+// refused before any launch.
+namespace {
+struct WsState {
+  prism_config cfg;
+  unsigned long long plan_gen, fwd_gen;  // fwd_gen == plan_gen: forward ran on this plan
+};
+std::mutex g_ws_mu;
+std::unordered_map<uintptr_t, WsState> g_ws;
+unsigned long long g_gen = 0;
+
+bool same_config(const prism_config &a, const prism_config &b) {
+  return memcmp(&a, &b, sizeof(prism_config)) == 0;
+}
+}  // namespace
+
 static thread_local std::string g_last_error;
 
 static prism_status fail(prism_status st, const std::string &msg) {
@@ -85,9 +106,8 @@ prism_status check_config(const prism_config *cfg, Dims *d, const char **why) {
     *why = "dtype must be PRISM_F32 or PRISM_BF16";
     return PRISM_ERR_UNSUPPORTED;
   }
-  if (cfg->dtype == PRISM_BF16 ? cfg->head_dim != 128
-                               : (cfg->head_dim != 64 && cfg->head_dim != 128)) {
-    *why = "head_dim must be 128 for bfloat16, 64 or 128 for float32";
+  if (cfg->head_dim != 64 && cfg->head_dim != 128) {
+    *why = "head_dim must be 64 or 128";
     return PRISM_ERR_UNSUPPORTED;
   }
   if (cfg->min_edge_log2 != 0 && cfg->min_edge_log2 != 1) {
@@ -117,6 +137,10 @@ prism_status check_config(const prism_config *cfg, Dims *d, const char **why) {
       return PRISM_ERR_ARG;
     }
   }
+  if (cfg->max_pairs < 0) {
+    *why = "max_pairs must be 0 (Nb_max^2) or a positive pair count";
+    return PRISM_ERR_ARG;
+  }
   if (cfg->num_heads > 4096) {
     *why = "too many heads in one call";
     return PRISM_ERR_UNSUPPORTED;
@@ -134,6 +158,7 @@ prism_status check_config(const prism_config *cfg, Dims *d, const char **why) {
   d->heads = cfg->num_heads;
   d->D = cfg->head_dim;
   d->dtype = cfg->dtype;
+  d->Dp = cfg->dtype == PRISM_BF16 ? 128 : cfg->head_dim;
   d->N = (int)N;
   d->Z = (int)(N / kZoneTok);
   d->U = (int)(N / kUnit);
@@ -142,6 +167,10 @@ prism_status check_config(const prism_config *cfg, Dims *d, const char **why) {
   d->nzh = cfg->H / kZone;
   d->nzw = cfg->W / kZone;
   d->words = (d->nb_max + 31) / 32;
+  {
+    const long long full = (long long)d->nb_max * d->nb_max;
+    d->cap = cfg->max_pairs > 0 && cfg->max_pairs < full ? cfg->max_pairs : full;
+  }
   d->elt = cfg->dtype == PRISM_BF16 ? 2 : 4;
   d->tok_stride = (size_t)cfg->num_heads * cfg->head_dim;
   d->head_stride = (size_t)cfg->head_dim;
@@ -170,11 +199,16 @@ Layout make_layout(const Dims &d) {
   L.pub.inv_perm = take(H * N * sizeof(int));
   L.pub.qbar = take(H * NB * D * sizeof(float));
   L.pub.kbar = take(H * NB * D * sizeof(float));
+  const size_t CAP = (size_t)d.cap;
   L.pub.sel_count = take(H * NB * sizeof(int));
-  L.pub.csr_col = take(H * NB * NB * sizeof(int));
+  L.pub.csr_ptr = take(H * (NB + 1) * sizeof(int));
+  L.pub.csr_col = take(H * CAP * sizeof(int));
   L.pub.csc_count = take(H * NB * sizeof(int));
-  L.pub.csc_row = take(H * NB * NB * sizeof(int));
+  L.pub.csc_ptr = take(H * (NB + 1) * sizeof(int));
+  L.pub.csc_row = take(H * CAP * sizeof(int));
   L.pub.scores = take(NB * NB * sizeof(float));
+  L.pub.flags = take(H * sizeof(uint32_t));
+  L.vmax = take(H * sizeof(float));
   L.sel_bits = take(H * NB * d.words * sizeof(uint32_t));
   L.csc_bits = take(H * NB * d.words * sizeof(uint32_t));
   L.tiles = take(H * U * sizeof(int2));
@@ -183,8 +217,8 @@ Layout make_layout(const Dims &d) {
   L.delta = take(H * N * sizeof(float));
   L.lsep = take(H * N * sizeof(float));
   L.lse2 = take(H * N * sizeof(float));
-  L.o32p = take(H * N * D * sizeof(float));
-  const size_t tensor = H * N * D * d.elt;
+  L.o32p = take(H * N * (size_t)d.Dp * sizeof(float));
+  const size_t tensor = H * N * (size_t)d.Dp * d.elt;
   L.qp = take(tensor);
   L.kp = take(tensor);
   L.vp = take(tensor);
@@ -194,6 +228,7 @@ Layout make_layout(const Dims &d) {
   L.pub.N = d.N;
   L.pub.Z = d.Z;
   L.pub.nb_max = d.nb_max;
+  L.pub.pair_cap = d.cap;
   return L;
 }
 
@@ -289,6 +324,11 @@ prism_status prism_plan(const prism_config *cfg, const void *q, const void *k, c
   if ((st = launched(launch_gather(d, q, k, v, ws, L, s), "gather"))) return st;
   if ((st = launched(launch_tiles(d, ws, L, s), "tiles"))) return st;
   if ((st = launched(launch_scores_select(d, cfg, sc.score, ws, L, s), "selection"))) return st;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  WsState &w = g_ws[(uintptr_t)workspace];
+  memcpy(&w.cfg, cfg, sizeof(prism_config));
+  w.plan_gen = ++g_gen;
+  w.fwd_gen = 0;
   return PRISM_OK;
 }
 
@@ -303,10 +343,17 @@ prism_status prism_attn_fwd(const prism_config *cfg, void *workspace, size_t wor
     return fail(PRISM_ERR_ARG, "workspace must be 256-byte, o 16-byte, lse 4-byte aligned");
   Layout L = make_layout(d);
   if (workspace_bytes < L.total) return fail(PRISM_ERR_WORKSPACE, "workspace too small");
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  auto it = g_ws.find((uintptr_t)workspace);
+  if (it == g_ws.end() || !same_config(it->second.cfg, *cfg))
+    return fail(PRISM_ERR_STATE, "prism_attn_fwd: no prism_plan of this configuration on "
+                                 "this workspace");
   Scales sc = scales_of(cfg, d);
-  return launched(launch_attn_fwd(d, sc.softmax, (uint8_t *)workspace, L, o, lse,
-                                  (hipStream_t)stream),
-                  "attention forward");
+  st = launched(launch_attn_fwd(d, sc.softmax, (uint8_t *)workspace, L, o, lse,
+                                (hipStream_t)stream),
+                "attention forward");
+  if (st == PRISM_OK) it->second.fwd_gen = it->second.plan_gen;
+  return st;
 }
 
 prism_status prism_attn_bwd(const prism_config *cfg, void *workspace, size_t workspace_bytes,
@@ -323,6 +370,16 @@ prism_status prism_attn_bwd(const prism_config *cfg, void *workspace, size_t wor
                                "16-byte aligned");
   Layout L = make_layout(d);
   if (workspace_bytes < L.total) return fail(PRISM_ERR_WORKSPACE, "workspace too small");
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    auto it = g_ws.find((uintptr_t)workspace);
+    if (it == g_ws.end() || !same_config(it->second.cfg, *cfg))
+      return fail(PRISM_ERR_STATE, "prism_attn_bwd: no prism_plan of this configuration on "
+                                   "this workspace");
+    if (it->second.fwd_gen != it->second.plan_gen)
+      return fail(PRISM_ERR_STATE, "prism_attn_bwd: prism_attn_fwd has not run on this "
+                                   "workspace since its last prism_plan");
+  }
   Scales sc = scales_of(cfg, d);
   return launched(launch_attn_bwd(d, sc.softmax, (uint8_t *)workspace, L, dout, dq, dk, dv,
                                   (hipStream_t)stream),
@@ -336,11 +393,44 @@ const char *prism_status_string(int status) {
     case PRISM_ERR_UNSUPPORTED: return "unsupported configuration";
     case PRISM_ERR_WORKSPACE: return "workspace too small";
     case PRISM_ERR_HIP: return "HIP launch failure";
+    case PRISM_ERR_STATE: return "call out of order for this workspace";
+    case PRISM_ERR_RANGE: return "a head's status flags are set";
     default: return "unknown status";
   }
 }
 
 const char *prism_last_error(void) { return g_last_error.c_str(); }
+
+prism_status prism_check_flags(const prism_config *cfg, const void *workspace, uint32_t *flags,
+                               void *stream) {
+  Dims d;
+  const char *why;
+  prism_status st = check_config(cfg, &d, &why);
+  if (st != PRISM_OK) return fail(st, why);
+  if (!workspace) return fail(PRISM_ERR_ARG, "null workspace");
+  const Layout L = make_layout(d);
+  std::vector<uint32_t> host(d.heads);
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = launched(hipMemcpyAsync(host.data(), (const uint8_t *)workspace + L.pub.flags,
+                                    sizeof(uint32_t) * d.heads, hipMemcpyDeviceToHost, s),
+                     "flags copy")))
+    return st;
+  if ((st = launched(hipStreamSynchronize(s), "flags copy"))) return st;
+  uint32_t any = 0;
+  for (int h = 0; h < d.heads; ++h) {
+    any |= host[h];
+    if (flags) flags[h] = host[h];
+  }
+  if (any) {
+    std::string msg = "flags set:";
+    if (any & PRISM_FLAG_QKV_RANGE) msg += " q/k/v outside the float16 range;";
+    if (any & PRISM_FLAG_SELECTION_OVERFLOW) msg += " selection exceeds max_pairs;";
+    if (any & PRISM_FLAG_DOUT_RANGE) msg += " dout outside the float16 range;";
+    if (any & PRISM_FLAG_DS_RANGE) msg += " dS bound reaches the float16 range;";
+    return fail(PRISM_ERR_RANGE, msg);
+  }
+  return PRISM_OK;
+}
 
 prism_status prism_trace_enable(int on) {
   std::lock_guard<std::mutex> lk(g_trace_mu);

@@ -38,9 +38,12 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 struct Dims {
   int T, H, W, heads, D, dtype;
+  int Dp;                // row width of the permuted operand copies: 128 for bfloat16 (a
+                         //   64-channel head is zero-padded), D for float32
   int N, Z, U, nb_max;   // tokens, zones, 64-token units, max blocks per head (= U)
   int nzt, nzh, nzw;     // zones per axis
   int words;             // 32-bit words per selection bitmask row
+  long long cap;         // capacity of one head's CSR (and CSC) lists in block pairs
   size_t elt;            // bytes per token-tensor element
   // element strides of the q, k, v inputs of prism_plan: (token n, head h, channel c) at
   // n * tok_stride + h * head_stride + c (dense [N][heads][D] by default)
@@ -63,6 +66,7 @@ struct Layout {
   size_t delta;             // bwd: float [heads][N] in permuted order: rowsum(dO * O)
                             //   (float32 inputs) or -rowsum(dO * O) (bfloat16)
   size_t lse2;              // bwd (bfloat16): float [heads][N] lse * log2(e)
+  size_t vmax;              // float [heads]: largest row norm of V (the dS range bound)
   size_t total;
 };
 
@@ -101,7 +105,8 @@ hipError_t launch_dkdv_bf16(int work_items, hipStream_t s, int N, int U, int nb_
                             const uint16_t *kp, const uint16_t *vp, const uint16_t *dop,
                             const float *lse2, const float *ndelta, const int *unit_blk,
                             const int *bstart, const int *bsize, const int *tcnt,
-                            const int *trows, const int *perm, float scale, float sl2e,
+                            const int *tptr, const int *trows, long long cap, const int *perm,
+                            float scale, float sl2e, int dio, const uint32_t *flags,
                             uint16_t *dk, uint16_t *dv);
 
 // a2v_norm.hip
@@ -130,8 +135,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // spread a group of four aligned chunks over four different quarters of the banks, which
 // keeps the 8-byte transposed reads below (4 rows x 4 chunks x 2 halves per 32 lanes)
 // free of bank conflicts too.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int rm_swz(int r, int c) { return r * 256 + ((c ^ swz(r)) << 4); }
+// (The address helpers below are __host__ __device__ so that host code can check them.)
+__host__ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__host__ __device__ __forceinline__ int rm_swz(int r, int c) {
+  return r * 256 + ((c ^ swz(r)) << 4);
+}
 
 // The A operand of a 32x32x16 float16 MFMA taken transposed from a row-major float16 tile
 // X[k][d] with ds_read_b64_tr_b16 (in each 16-lane group, lane i receives element i % 4 of
@@ -139,16 +147,19 @@ __device__ __forceinline__ int rm_swz(int r, int c) { return r * 256 + ((c ^ swz
 // X[kb + 8 (e / 4) + 4 (l / 32) + e % 4][db + l % 32]: row l % 32 of the transposed tile
 // and the same key order as a B operand taken from a C tile (register v of a C tile holds
 // row (v / 4) * 8 + 4 (l / 32) + v % 4).  kb is a multiple of 16, db of 32.
-__device__ __forceinline__ f16x8 tr_operand(const uint8_t *tile, int kb, int db, int lane) {
+// Byte offset in the tile of the 8-byte piece lane `lane` addresses in read m (rows 8m ..).
+__host__ __device__ __forceinline__ int tr_offset(int kb, int db, int lane, int m) {
   const int g = lane >> 4, s = lane & 15;
   const int col = db + 16 * (g & 1) + 4 * (s & 3);
+  const int row = kb + 8 * m + 4 * (g >> 1) + (s >> 2);
+  return rm_swz(row, col >> 3) + (col & 7) * 2;
+}
+__device__ __forceinline__ f16x8 tr_operand(const uint8_t *tile, int kb, int db, int lane) {
   f16x8 r;
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const int row = kb + 8 * m + 4 * (g >> 1) + (s >> 2);
     const fp16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-        (__attribute__((address_space(3))) fp16x4_t *)(tile + rm_swz(row, col >> 3) +
-                                                       (col & 7) * 2));
+        (__attribute__((address_space(3))) fp16x4_t *)(tile + tr_offset(kb, db, lane, m)));
     const f16x4 w = __builtin_bit_cast(f16x4, v);
 #pragma unroll
     for (int e = 0; e < 4; ++e) r[4 * m + e] = w[e];
@@ -165,7 +176,7 @@ __device__ __forceinline__ f16x8 tr_operand(const uint8_t *tile, int kb, int db,
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
-__device__ __forceinline__ uint32_t row_base(uint32_t tile, int r) {
+__host__ __device__ __forceinline__ uint32_t row_base(uint32_t tile, int r) {
   return tile + (uint32_t)(r * 256 + (swz(r) << 4));
 }
 __device__ __forceinline__ f16x8 lds_row16(uint32_t addr) {
@@ -175,19 +186,23 @@ __device__ __forceinline__ f16x8 lds_row16(uint32_t addr) {
 struct TrBase {
   uint32_t m0, m1;  // the lane's 8-byte piece of rows 0-7 and 8-15 at kb = 0, db = 0
 };
-__device__ __forceinline__ TrBase tr_base(uint32_t tile, int lane) {
+__host__ __device__ __forceinline__ TrBase tr_base(uint32_t tile, int lane) {
   const int g = lane >> 4, s = lane & 15;
   const int col = 16 * (g & 1) + 4 * (s & 3);
   const int row = 4 * (g >> 1) + (s >> 2);
   const uint32_t t = tile + (uint32_t)((col & 7) * 2);
   return {t + (uint32_t)rm_swz(row, col >> 3), t + (uint32_t)rm_swz(row + 8, col >> 3)};
 }
+// The LDS address of read m of tr_operand(tile, kb, db, lane) from tr_base(tile, lane)
+__host__ __device__ __forceinline__ uint32_t tr_addr(const TrBase &b, int m, int kb, int db) {
+  return ((m ? b.m1 : b.m0) ^ (uint32_t)(2 * db)) + (uint32_t)(256 * kb);
+}
 // tr_operand(tile, kb, db, lane) from tr_base(tile, lane)
 __device__ __forceinline__ f16x8 tr_read(const TrBase &b, int kb, int db) {
   f16x8 r;
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const uint32_t a = ((m ? b.m1 : b.m0) ^ (uint32_t)(2 * db)) + (uint32_t)(256 * kb);
+    const uint32_t a = tr_addr(b, m, kb, db);
     const fp16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
         (__attribute__((address_space(3))) fp16x4_t *)(uintptr_t)a);
     const f16x4 w = __builtin_bit_cast(f16x4, v);
@@ -266,7 +281,7 @@ __device__ __forceinline__ void dma16(const void *base, uint32_t off, void *dst)
 // (c0 ^ 16 i) + 1024 i with c0 = copy_offset(r0, l) that of copy 0: one register and a XOR
 // per copy, the 1024 i going into the instruction's offset field (which moves the LDS
 // destination by the same 1024 i).
-__device__ __forceinline__ uint32_t copy_offset(int r0, int lane) {
+__host__ __device__ __forceinline__ uint32_t copy_offset(int r0, int lane) {
   const int r = r0 + (lane >> 4);
   return (uint32_t)(r * 256 + (((lane & 15) ^ swz(r)) << 4));
 }
@@ -314,11 +329,12 @@ __device__ __forceinline__ void workgroup_barrier() {
 // it never waits behind the direct-to-LDS copies in flight (loads complete in order).  The
 // members other than the window are the same in every lane.
 struct BlockUnits {
-  int base, idx, sub, us, nu, n, lane;
+  int base, idx, sub, us, nu, n, lane, self;
+  bool empty;
   int win_us, win_nu;  // this lane's entry of the window: first unit and unit count
   const int *list, *bstart, *bsize;
   __device__ void fill() {  // lanes past the end repeat the last entry (never used)
-    const int j = list[min(base + lane, n - 1)];
+    const int j = empty ? self : list[min(base + lane, n - 1)];
     win_us = bstart[j] / kUnit;
     win_nu = bsize[j] / kUnit;
   }
@@ -326,10 +342,15 @@ struct BlockUnits {
     us = __builtin_amdgcn_readlane(win_us, idx);
     nu = __builtin_amdgcn_readlane(win_nu, idx);
   }
-  // a list of count >= 1 blocks
-  __device__ void init(const int *l, int count, const int *bs, const int *bz, int lane_id) {
+  // a list of count blocks; an empty one (a query block whose list a full selection
+  // capacity cut to nothing: its head's outputs are NaN) walks the block self_blk instead
+  __device__ void init(const int *l, int count, const int *bs, const int *bz, int lane_id,
+                       int self_blk) {
     list = l;
     n = __builtin_amdgcn_readfirstlane(count);
+    empty = n < 1;
+    self = self_blk;
+    if (empty) n = 1;
     bstart = bs;
     bsize = bz;
     lane = lane_id;
@@ -367,6 +388,11 @@ constexpr float kPScale = 1024.f;
 // Lazy rescaling in the forward: the running max is kept until a new maximum exceeds it
 // by more than kLazy (log2 units); weights then stay below 2^(kPShift + kLazy) = 2^15.
 constexpr float kLazy = 5.f;
+
+// NaN bit patterns for the outputs of a head whose status flags are set (selected and
+// stored as integers: the attention kernels are compiled without NaN semantics)
+constexpr uint32_t kNaNf32 = 0x7fc00000u;
+constexpr uint32_t kNaNbf16x2 = 0x7fc07fc0u;
 
 template <typename T>
 __device__ __forceinline__ T *ws_ptr(uint8_t *ws, size_t off) {

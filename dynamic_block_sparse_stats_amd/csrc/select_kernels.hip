@@ -154,8 +154,7 @@ template <int NT, int WPT>
 __global__ void __launch_bounds__(NT)
     select_kernel(int nb_max, int words, const int *__restrict__ nb_ptr,
                   const float *__restrict__ scores, int top_k, float top_k_frac, float top_p,
-                  uint32_t *__restrict__ bits, int *__restrict__ count,
-                  int *__restrict__ cols) {
+                  uint32_t *__restrict__ bits, int *__restrict__ count) {
   const int nb = *nb_ptr;
   // Top-k as a fraction of this head's blocks (the pages' sparsity form), else a count
   if (top_k_frac > 0.f) top_k = (int)ceil((double)top_k_frac * (double)nb);
@@ -288,21 +287,10 @@ __global__ void __launch_bounds__(NT)
       wbits[r] = b;
     }
     uint32_t *brow = bits + (size_t)i * words;
-    int *crow = cols + (size_t)i * nb_max;
-    int run2 = 0;
 #pragma unroll
     for (int r = 0; r < WPT; ++r) {
       const int w = tid + NT * r;
       if (w < words) brow[w] = wbits[r];
-      int tot;
-      int pos = run2 + block_excl_scan<NT>(__popc(wbits[r]), scanbuf, &tot);
-      run2 += tot;
-      uint32_t b = wbits[r];
-      while (b) {
-        int e = __ffs(b) - 1;
-        b &= b - 1;
-        crow[pos++] = 32 * w + e;
-      }
     }
     if (tid == 0) count[i] = total;
     (void)wcnt;
@@ -335,11 +323,65 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// Expansion of bitmask rows into ascending index lists with their counts.
+// Set bits per bitmask row (the CSC counts): one wave per row.
+__global__ void __launch_bounds__(256)
+    popc_rows_kernel(int words, const int *__restrict__ nb_ptr,
+                     const uint32_t *__restrict__ bits, int *__restrict__ count) {
+  const int nb = *nb_ptr;
+  const int wn = (nb + 31) / 32, lane = threadIdx.x & 63;
+  for (int i = blockIdx.x * 4 + (threadIdx.x >> 6); i < nb; i += gridDim.x * 4) {
+    const uint32_t *brow = bits + (size_t)i * words;
+    int c = 0;
+    for (int w = lane; w < wn; w += 64) c += __popc(brow[w]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
+    if (lane == 0) count[i] = c;
+  }
+}
+
+// Row offsets of a list set: ptr[i] = count[0] + ... + count[i - 1], ptr[nb] the total.
+// The lists of one head hold at most cap entries: past it the counts are cut (every list
+// then ends inside the capacity) and the head is flagged; its outputs will be NaN.  One
+// workgroup; each thread scans a contiguous chunk of rows.
+constexpr int kScanThreads = 1024;
+__global__ void __launch_bounds__(kScanThreads)
+    offsets_kernel(const int *__restrict__ nb_ptr, int *__restrict__ count,
+                   int *__restrict__ ptr, long long cap, uint32_t *__restrict__ flags, int h) {
+  __shared__ long long scan[kScanThreads];
+  const int nb = *nb_ptr, tid = threadIdx.x;
+  const int chunk = (nb + kScanThreads - 1) / kScanThreads;
+  const int i0 = min(nb, tid * chunk), i1 = min(nb, i0 + chunk);
+  long long local = 0;
+  for (int i = i0; i < i1; ++i) local += count[i];
+  scan[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const long long add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  long long at = scan[tid] - local;
+  for (int i = i0; i < i1; ++i) {
+    const long long room = cap - at > 0 ? cap - at : 0;
+    const int c = count[i];
+    ptr[i] = (int)(at < cap ? at : cap);
+    if (c > room) count[i] = (int)room;
+    at += c;
+  }
+  if (tid == kScanThreads - 1) {
+    const long long total = scan[tid];
+    ptr[nb] = (int)(total < cap ? total : cap);
+    if (total > cap) atomicOr(flags + h, (uint32_t)PRISM_FLAG_SELECTION_OVERFLOW);
+  }
+}
+
+// Expansion of bitmask rows into ascending index lists at their row offsets; a list keeps
+// its first count[i] entries (all of them unless the head's capacity cut it).
 template <int NT, int WPT>
 __global__ void __launch_bounds__(NT)
-    expand_kernel(int nb_max, int words, const int *__restrict__ nb_ptr,
-                  const uint32_t *__restrict__ bits, int *__restrict__ count,
+    expand_kernel(int words, const int *__restrict__ nb_ptr, const uint32_t *__restrict__ bits,
+                  const int *__restrict__ count, const int *__restrict__ ptr,
                   int *__restrict__ lists) {
   const int nb = *nb_ptr;
   __shared__ int scanbuf[NT / 64];
@@ -347,7 +389,8 @@ __global__ void __launch_bounds__(NT)
   const int wn = (nb + 31) / 32;
   for (int i = blockIdx.x; i < nb; i += gridDim.x) {
     const uint32_t *brow = bits + (size_t)i * words;
-    int *lrow = lists + (size_t)i * nb_max;
+    int *lrow = lists + ptr[i];
+    const int keep = count[i];
     int run = 0;
 #pragma unroll
     for (int r = 0; r < WPT; ++r) {
@@ -356,13 +399,12 @@ __global__ void __launch_bounds__(NT)
       int tot;
       int pos = run + block_excl_scan<NT>(__popc(b), scanbuf, &tot);
       run += tot;
-      while (b) {
+      while (b && pos < keep) {
         int e = __ffs(b) - 1;
         b &= b - 1;
         lrow[pos++] = 32 * w + e;
       }
     }
-    if (tid == 0) count[i] = run;
     __syncthreads();
   }
 }
@@ -372,6 +414,7 @@ hipError_t launch_scores_select(const Dims &d, const prism_config *cfg, float sc
                                 uint8_t *ws, const Layout &L, hipStream_t s) {
   const int *zblock = (const int *)(ws + L.pub.zone_block);
   float *scores = (float *)(ws + L.pub.scores);
+  uint32_t *flags = (uint32_t *)(ws + L.pub.flags);
   const int gemm_grid = 1024, sel_grid = 2048;
   const bool small = d.words <= 256 * 2;  // nb_max <= 16384
   for (int h = 0; h < d.heads; ++h) {
@@ -381,32 +424,45 @@ hipError_t launch_scores_select(const Dims &d, const prism_config *cfg, float sc
     uint32_t *bits = (uint32_t *)(ws + L.sel_bits) + (size_t)h * d.nb_max * d.words;
     uint32_t *tbits = (uint32_t *)(ws + L.csc_bits) + (size_t)h * d.nb_max * d.words;
     int *cnt = (int *)(ws + L.pub.sel_count) + (size_t)h * d.nb_max;
-    int *cols = (int *)(ws + L.pub.csr_col) + (size_t)h * d.nb_max * d.nb_max;
+    int *cptr = (int *)(ws + L.pub.csr_ptr) + (size_t)h * (d.nb_max + 1);
+    int *cols = (int *)(ws + L.pub.csr_col) + (size_t)h * d.cap;
     int *tcnt = (int *)(ws + L.pub.csc_count) + (size_t)h * d.nb_max;
-    int *trows = (int *)(ws + L.pub.csc_row) + (size_t)h * d.nb_max * d.nb_max;
+    int *tptr = (int *)(ws + L.pub.csc_ptr) + (size_t)h * (d.nb_max + 1);
+    int *trows = (int *)(ws + L.pub.csc_row) + (size_t)h * d.cap;
     {
       TraceScope tr(PRISM_STAGE_SCORES, s);
       hipLaunchKernelGGL(score_gemm_kernel, dim3(gemm_grid), dim3(256), 0, s, d.D, d.nb_max,
                          nbp, qbar, kbar, score_scale, scores);
     }
     TraceScope tr(PRISM_STAGE_SELECT, s);
-    if (small) {
+    // selection bitmask and counts, then the CSR lists at their offsets; the transposed
+    // bitmask, its counts and the CSC lists the same way
+    if (small)
       hipLaunchKernelGGL((select_kernel<256, 2>), dim3(sel_grid), dim3(256), 0, s, d.nb_max,
                          d.words, nbp, scores, cfg->top_k, cfg->top_k_frac, cfg->top_p, bits,
-                         cnt, cols);
-    } else {
+                         cnt);
+    else
       hipLaunchKernelGGL((select_kernel<1024, 2>), dim3(sel_grid), dim3(1024), 0, s, d.nb_max,
                          d.words, nbp, scores, cfg->top_k, cfg->top_k_frac, cfg->top_p, bits,
-                         cnt, cols);
-    }
+                         cnt);
     hipLaunchKernelGGL(transpose_bits_kernel, dim3(1024), dim3(256), 0, s, d.words, nbp, bits,
                        tbits);
+    hipLaunchKernelGGL(popc_rows_kernel, dim3(1024), dim3(256), 0, s, d.words, nbp, tbits,
+                       tcnt);
+    hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kScanThreads), 0, s, nbp, cnt, cptr, d.cap,
+                       flags, h);
+    hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kScanThreads), 0, s, nbp, tcnt, tptr,
+                       d.cap, flags, h);
     if (small) {
-      hipLaunchKernelGGL((expand_kernel<256, 2>), dim3(sel_grid), dim3(256), 0, s, d.nb_max,
-                         d.words, nbp, tbits, tcnt, trows);
+      hipLaunchKernelGGL((expand_kernel<256, 2>), dim3(sel_grid), dim3(256), 0, s, d.words, nbp,
+                         bits, cnt, cptr, cols);
+      hipLaunchKernelGGL((expand_kernel<256, 2>), dim3(sel_grid), dim3(256), 0, s, d.words, nbp,
+                         tbits, tcnt, tptr, trows);
     } else {
-      hipLaunchKernelGGL((expand_kernel<1024, 2>), dim3(sel_grid), dim3(1024), 0, s, d.nb_max,
-                         d.words, nbp, tbits, tcnt, trows);
+      hipLaunchKernelGGL((expand_kernel<1024, 2>), dim3(sel_grid), dim3(1024), 0, s, d.words,
+                         nbp, bits, cnt, cptr, cols);
+      hipLaunchKernelGGL((expand_kernel<1024, 2>), dim3(sel_grid), dim3(1024), 0, s, d.words,
+                         nbp, tbits, tcnt, tptr, trows);
     }
   }
   return hipGetLastError();

@@ -60,6 +60,7 @@ class Workload:
     blobs: list = field(default_factory=list)
     backward: bool = False
     cid: int = 0
+    tensor_cid: int = -1       # workload whose seeded tensors this one reads (-1: its own)
 
     @property
     def N(self) -> int:
@@ -77,8 +78,11 @@ def _blobs_for(cid: int, T: int, H: int, W: int, rng: np.random.Generator) -> li
         return (float(rng.uniform(0.2, 0.8) * T), float(rng.uniform(0.2, 0.8) * H),
                 float(rng.uniform(0.2, 0.8) * W))
     if cid == 0:
+        # one sounding blob whose motion runs along T only: fixed in H and W, it rises and
+        # fades over the frames around t0 (the tiny grid's one zone row along T sees it
+        # change from frame to frame)
         t0, h0, w0 = T / 2.0, H / 2.0, W / 4.0
-        return [Blob(t0, h0, w0, vt_h=0.0, vt_w=1.0, audio=1.0)]
+        return [Blob(t0, h0, w0, vt_h=0.0, vt_w=0.0, audio=1.0)]
     if cid == 1:
         out = []
         for b in range(3):
@@ -106,7 +110,10 @@ def _blobs_for(cid: int, T: int, H: int, W: int, rng: np.random.Generator) -> li
 
 def workload(cid: int) -> Workload:
     """The five workloads: tiny (fp32), 720p, 1080p, 2K forward, 2K training step."""
-    ss = np.random.SeedSequence(BASE_SEED + cid)
+    # the 2K training step runs on the 2K forward workload's tensors (same blobs, same
+    # seeds): only the pass differs
+    tcid = 3 if cid == 4 else cid
+    ss = np.random.SeedSequence(BASE_SEED + tcid)
     rng = np.random.default_rng(ss.spawn(1)[0])
     if cid == 0:
         T, H, W, heads, D, dt, k, p, mel, amp = 8, 16, 16, 2, 64, "f32", 4, 0.9, 0, 1.0
@@ -122,8 +129,8 @@ def workload(cid: int) -> Workload:
         name, bwd = ("2k-fwd-64x104x128", False) if cid == 3 else ("2k-train-64x104x128", True)
     else:
         raise ValueError(f"unknown workload {cid}")
-    blobs = _blobs_for(cid, T, H, W, rng)
-    return Workload(name, T, H, W, heads, D, dt, k, p, mel, amp, blobs, bwd, cid)
+    blobs = _blobs_for(tcid, T, H, W, rng)
+    return Workload(name, T, H, W, heads, D, dt, k, p, mel, amp, blobs, bwd, cid, tcid)
 
 
 def custom(T: int, H: int, W: int, heads: int, head_dim: int, dtype: str = "bf16",
@@ -148,7 +155,8 @@ def make_inputs(wl: Workload, device="cpu", with_dout: bool | None = None, seed_
     """Draw q, k, v [N, heads, D], a2v [N] (float32) and optionally dout [N, heads, D]."""
     if with_dout is None:
         with_dout = wl.backward
-    ss = np.random.SeedSequence(BASE_SEED + wl.cid + 7919 * seed_offset)
+    tcid = wl.tensor_cid if wl.tensor_cid >= 0 else wl.cid
+    ss = np.random.SeedSequence(BASE_SEED + tcid + 7919 * seed_offset)
     c_bg, c_blob, c_w, c_bulk, c_do = ss.spawn(5)
     T, H, W, D, Hh = wl.T, wl.H, wl.W, wl.head_dim, wl.heads
     N = T * H * W

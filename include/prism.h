@@ -30,7 +30,7 @@
  *   - All pointers are device pointers.  The caller owns every buffer, including the
  *     workspace; the library allocates no device memory.
  *   - Calls are asynchronous on the caller's HIP stream (a hipStream_t passed as void*,
- *     NULL = the null stream) and never synchronise the host.
+ *     NULL = the null stream) and never synchronise the host, except prism_check_flags.
  *   - Arguments are checked before any launch; a rejected call launches nothing and
  *     returns a negative status.  No exception crosses this boundary.
  *   - A call is thread-safe as long as concurrent calls use distinct workspaces.
@@ -50,7 +50,13 @@ typedef enum {
     PRISM_ERR_ARG = -1,          /* null pointer, bad size, inconsistent configuration */
     PRISM_ERR_UNSUPPORTED = -2,  /* grid not a multiple of 8, head_dim / dtype not built */
     PRISM_ERR_WORKSPACE = -3,    /* workspace smaller than prism_workspace_bytes() */
-    PRISM_ERR_HIP = -4           /* a HIP launch failed; see prism_last_error() */
+    PRISM_ERR_HIP = -4,          /* a HIP launch failed; see prism_last_error() */
+    PRISM_ERR_STATE = -5,        /* call out of order for this workspace: a forward with no
+                                    prism_plan of the same configuration on it, or a
+                                    backward with no forward since its last plan */
+    PRISM_ERR_RANGE = -6         /* prism_check_flags: some head's flags are set (inputs
+                                    outside the float16 operand range, or more selected
+                                    block pairs than max_pairs); its outputs are NaN */
 } prism_status;
 
 typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
@@ -82,10 +88,27 @@ typedef struct prism_config {
     int density_mode;     /* information density driving the volume tier: 0 spatial plus
                              temporal terms of rho_raw (the method), 1 spatial term only,
                              2 temporal term only, 3 the normalised A2V intensity a_bar */
+    /* Capacity of the selection lists. */
+    long long max_pairs;  /* selected (query block, key block) pairs one head may hold in
+                             its CSR and CSC lists; 0 = Nb_max^2, which always suffices.
+                             A head that selects more keeps a truncated selection, gets
+                             PRISM_FLAG_SELECTION_OVERFLOW and NaN outputs. */
 } prism_config;
 
+/* Per-head status flags, written on the device by prism_plan (bits 0-1) and prism_attn_bwd
+ * (bits 2-3), read with prism_check_flags.  A flagged head's outputs (o and lse for bits
+ * 0-1; dq, dk, dv for any bit) are NaN, never silently wrong numbers. */
+enum {
+    PRISM_FLAG_QKV_RANGE = 1,          /* a q, k or v value outside +-65504, the float16
+                                          range of the attention operands (or not finite) */
+    PRISM_FLAG_SELECTION_OVERFLOW = 2, /* more selected pairs than max_pairs */
+    PRISM_FLAG_DOUT_RANGE = 4,         /* a dout value outside +-65504 (or not finite) */
+    PRISM_FLAG_DS_RANGE = 8            /* the bound |dout_x| (max_y |v_y| + |o_x|) on dS =
+                                          P (dP - delta) reaches 65504 for some row */
+};
+
 /* Offsets (bytes from the workspace base) and element types of the plan's arrays, for
- * inspection.  Nb_max = N / 64.  Per head h:
+ * inspection.  Nb_max = N / 64; Cap = max_pairs (Nb_max^2 when 0).  Per head h:
  *   zone_stats  double [heads][Z][4]: sigma2_T, sigma2_H, sigma2_W, rho_raw (Z = N / 512)
  *   audio_stats double [Z][4]: zone mean of a, sigma2_T, sigma2_H, sigma2_W
  *   zone_diag   double [heads][Z][4]: rho, tier margin, shape margin, best distance
@@ -98,16 +121,18 @@ typedef struct prism_config {
  *   inv_perm    int32  [heads][N]: token -> permuted position
  *   qbar, kbar  float  [heads][Nb_max][D]: block means of Q and K
  *   sel_count   int32  [heads][Nb_max]: selected key blocks per query block
- *   csr_col     int32  [heads][Nb_max][Nb_max]: row i holds sel_count[i] key blocks,
- *                      ascending (a CSR whose row i starts at i * Nb_max)
- *   csc_count   int32  [heads][Nb_max], csc_row int32 [heads][Nb_max][Nb_max]: the
- *                      transpose (query blocks selecting each key block, ascending)
- *   scores      float  [Nb_max][Nb_max]: block logits of the last head planned */
+ *   csr_ptr     int32  [heads][Nb_max+1]: row i of the CSR starts at csr_ptr[i]
+ *   csr_col     int32  [heads][Cap]: row i holds sel_count[i] key blocks, ascending
+ *   csc_count, csc_ptr, csc_row: the transpose, in the same form (query blocks selecting
+ *                      each key block, ascending)
+ *   scores      float  [Nb_max][Nb_max]: block logits of the last head planned
+ *   flags       uint32 [heads]: PRISM_FLAG_* bits */
 typedef struct prism_layout {
     size_t zone_stats, audio_stats, zone_diag, zone_shape, zone_block, block_start,
-        block_size, unit_block, perm, inv_perm, qbar, kbar, sel_count, csr_col, csc_count,
-        csc_row, scores, total;
+        block_size, unit_block, perm, inv_perm, qbar, kbar, sel_count, csr_ptr, csr_col,
+        csc_count, csc_ptr, csc_row, scores, flags, total;
     int N, Z, nb_max;
+    long long pair_cap;   /* Cap */
 } prism_layout;
 
 /* Bytes of workspace a configuration needs (0 if the configuration is rejected). */
@@ -140,7 +165,9 @@ prism_status prism_plan(const prism_config *cfg, const void *q, const void *k, c
 /* Sparse attention forward over the plan in workspace (step 5): o [N][heads][D] in token
  * order, lse [heads][N] float32 (natural-log sum of exp of the scaled logits).  Also keeps
  * a float32 copy of o and the lse in workspace for prism_attn_bwd.  o must be 16-byte
- * aligned, lse 4-byte, workspace 256-byte (PRISM_ERR_ARG otherwise). */
+ * aligned, lse 4-byte, workspace 256-byte (PRISM_ERR_ARG otherwise).  PRISM_ERR_STATE,
+ * with nothing launched, when no prism_plan with the same configuration has been issued
+ * on this workspace (the library records the last plan of each workspace address). */
 prism_status prism_attn_fwd(const prism_config *cfg, void *workspace, size_t workspace_bytes,
                             void *o, float *lse, void *stream);
 
@@ -158,10 +185,19 @@ prism_status prism_a2v_norm(const void *x, int64_t n_tokens, int channels, int64
 /* Sparse attention backward with the plan held constant (digest, training section): given
  * dout [N][heads][D], writes dq, dk, dv [N][heads][D] (overwritten, token order).  Reads
  * the float32 copy of the output and the lse that prism_attn_fwd left in workspace, so
- * prism_attn_fwd must have run on this workspace since the last prism_plan.  dout, dq, dk,
- * dv must be 16-byte aligned, workspace 256-byte (PRISM_ERR_ARG otherwise). */
+ * prism_attn_fwd must have run on this workspace since the last prism_plan: otherwise the
+ * call returns PRISM_ERR_STATE and launches nothing.  dout, dq, dk, dv must be 16-byte
+ * aligned, workspace 256-byte (PRISM_ERR_ARG otherwise). */
 prism_status prism_attn_bwd(const prism_config *cfg, void *workspace, size_t workspace_bytes,
                             const void *dout, void *dq, void *dk, void *dv, void *stream);
+
+/* Waits for the work queued on stream, then copies the per-head status flags of
+ * workspace into flags[heads] (host memory; may be NULL) and returns PRISM_ERR_RANGE if any
+ * head has a flag set, PRISM_OK otherwise.  This is the one entry point that synchronises
+ * the host; call it after prism_plan or prism_attn_bwd when inputs may leave the float16
+ * range or the selection may exceed max_pairs. */
+prism_status prism_check_flags(const prism_config *cfg, const void *workspace,
+                               uint32_t *flags, void *stream);
 
 /* Per-stage tracing with HIP events (for benchmarks and profiles; off by default).  While
  * enabled, every entry point records a HIP event pair on the caller's stream around the

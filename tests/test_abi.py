@@ -53,6 +53,7 @@ def test_layout_and_workspace(lib):
     (dict(fixed_shape=(0 << 4) | (3 << 2) | 3), -1),     # edge 1 with min_edge_log2 = 1
     (dict(fixed_shape=-1), -1),
     (dict(T=1 << 30, H=1 << 30, W=1 << 30), -2),          # T * H * W beyond 64 bits
+    (dict(max_pairs=-1), -1),
 ])
 def test_rejected_configs(lib, over, code):
     base = dict(T=8, H=16, W=16, num_heads=2, head_dim=128, dtype=P.BF16, min_edge_log2=1,
@@ -152,3 +153,43 @@ def test_a2v_norm_rejects_bad_arguments(lib):
     assert lib.prism_a2v_norm(d, 10, 8, 12, P.BF16, d, None) == -1     # rows not 16-B aligned
     assert lib.prism_a2v_norm(ctypes.c_void_p(8), 10, 8, 8, P.BF16, d, None) == -1
     assert lib.prism_a2v_norm(d, 10, 8, 8, 5, d, None) == -2
+
+
+def test_forward_and_backward_refused_without_plan(lib):
+    """A workspace that no prism_plan has written: the forward and the backward are refused
+    with PRISM_ERR_STATE before any launch (nothing here touches a GPU)."""
+    cfg = P.make_config(8, 16, 16, 2, 128, "bf16")
+    need = lib.prism_workspace_bytes(ctypes.byref(cfg))
+    d, ws = ctypes.c_void_p(4096), ctypes.c_void_p(1 << 20)
+    assert lib.prism_attn_fwd(ctypes.byref(cfg), ws, need, d, d, None) == -5
+    assert b"no prism_plan" in lib.prism_last_error()
+    assert lib.prism_attn_bwd(ctypes.byref(cfg), ws, need, d, d, d, d, None) == -5
+    assert lib.prism_status_string(-5) == b"call out of order for this workspace"
+
+
+def test_pair_capacity_sizes_the_lists(lib):
+    """max_pairs bounds the CSR and CSC lists of each head: the 2K grid with 24 heads needs
+    far less workspace at the named workloads' capacity than at the worst case."""
+    full = P.make_config(64, 104, 128, 24, 128, "bf16", top_k=8, top_p=0.95)
+    capped = P.make_config(64, 104, 128, 24, 128, "bf16", top_k=8, top_p=0.95,
+                           max_pairs=P.default_max_pairs(64 * 104 * 128))
+    a, b = P.plan_layout(full), P.plan_layout(capped)
+    assert a.pair_cap == a.nb_max ** 2 and b.pair_cap == (851968 // 128) ** 2
+    list_bytes = lambda L: 2 * 24 * L.pair_cap * 4
+    assert a.total - b.total == list_bytes(a) - list_bytes(b)
+    assert a.total > 60e9 and b.total < 0.65 * a.total
+    big = P.make_config(8, 16, 16, 2, 128, "bf16", max_pairs=10 ** 12)   # clamped to Nb_max^2
+    assert P.plan_layout(big).pair_cap == 32 ** 2
+
+
+def test_bf16_head_dim_64_accepted(lib):
+    cfg = P.make_config(8, 16, 16, 2, 64, "bf16")
+    L = P.plan_layout(cfg)
+    assert L.total > 0 and P.workspace_bytes(cfg) == L.total
+
+
+def test_check_flags_rejects_bad_arguments(lib):
+    cfg = P.make_config(8, 16, 16, 2, 128, "bf16")
+    assert lib.prism_check_flags(ctypes.byref(cfg), None, None, None) == -1
+    bad = P.make_config(12, 16, 16, 2, 128, "bf16")
+    assert lib.prism_check_flags(ctypes.byref(bad), ctypes.c_void_p(256), None, None) == -2

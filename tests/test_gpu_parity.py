@@ -1,5 +1,6 @@
 """HIP path vs CPU oracle on small grids that span several tiles and ragged tails
 (called through the C ABI; the oracle never sees anything the GPU produced)."""
+import ctypes
 import math
 
 import numpy as np
@@ -9,8 +10,8 @@ import torch
 import dynamic_block_sparse_stats_amd as P
 from dynamic_block_sparse_stats_amd import synth
 import oracle
-from parity import (TOL, check_close, compare_plan, compare_selection, oracle_plan,
-                    rows_of_exact_blocks, run_plan, to_np)
+from parity import (TOL, check_close, check_grads, compare_plan, compare_selection, describe,
+                    oracle_plan, rows_of_exact_blocks, run_plan, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,18 +28,31 @@ def _check_head(wl, cfg, att, inp_cpu, h, o, lse, a2v=True, **over):
     assert not rep.get("downstream_skipped"), rep
     exact, excl, nnz = compare_selection(views, h, op, cfg.top_p, to_np(views["scores"])
                                          if h == cfg.num_heads - 1 else None)
-    oo, ol, mo = oracle.attn_fwd(op, inp_cpu["q"][:, h], inp_cpu["k"][:, h],
-                                 inp_cpu["v"][:, h], with_mag=True)
+    oo, ol = oracle.attn_fwd(op, inp_cpu["q"][:, h], inp_cpu["k"][:, h], inp_cpu["v"][:, h])
     rows = rows_of_exact_blocks(op, exact)
     go = o[:, h].float().cpu().numpy()
     gl = lse[h].cpu().numpy()
-    err_o, r_o = check_close(go[rows], oo[rows], wl.dtype, f"head {h} O", mo[rows])
-    err_l, r_l = check_close(gl[rows], ol[rows], "f32" if wl.dtype == "f32" else "bf16",
-                             f"head {h} lse")
+    err_o, r_o, _ = check_close(go[rows], oo[rows], wl.dtype, f"head {h} O")
+    err_l, r_l, _ = check_close(gl[rows], ol[rows], "f32" if wl.dtype == "f32" else "bf16",
+                                f"head {h} lse")
     print(f"head {h}: nb {op.nb} nnz {nnz} excluded {excl} near-tie zones "
           f"{rep['near_tie_zones']} max|O| {np.abs(oo).max():.2f} max|dO| {err_o:.2e} "
           f"(bound use {r_o:.2f}) max|dlse| {err_l:.2e}", flush=True)
     return op, exact
+
+
+def _grads_vs_oracle(op, inp_cpu, h, dq, dk, dv, what):
+    """Head h's dQ, dK, dV against the oracle's backward (bfloat16 bounds of check_grads)."""
+    g = oracle.attn_bwd(op, inp_cpu["q"][:, h], inp_cpu["k"][:, h], inp_cpu["v"][:, h],
+                        inp_cpu["dout"][:, h], with_mag=True)
+    refs = dict(dq=g[0], dk=g[1], dv=g[2])
+    res = check_grads({n: t[:, h].float().cpu().numpy() for n, t in
+                       (("dq", dq), ("dk", dk), ("dv", dv))},
+                      refs, dict(dq=g[3], dk=g[4], dv=g[5]), "bf16", what)
+    for name, c in res.items():
+        print(f"{what} max|{name}| {np.abs(refs[name]).max():.2f} " + describe(name, c),
+              flush=True)
+    return res
 
 
 @pytest.mark.parametrize("use_a2v", [True, False])
@@ -89,7 +103,7 @@ def test_tiny_fp32_backward():
         g = oracle.attn_bwd(op, inp_cpu["q"][:, h], inp_cpu["k"][:, h], inp_cpu["v"][:, h],
                             inp_cpu["dout"][:, h])
         for name, gpu, ref in (("dq", dq, g[0]), ("dk", dk, g[1]), ("dv", dv, g[2])):
-            err, _ = check_close(gpu[:, h].cpu().numpy(), ref, "f32", f"head {h} {name}")
+            err = check_close(gpu[:, h].cpu().numpy(), ref, "f32", f"head {h} {name}").err
             print(f"head {h} {name}: max abs err {err:.3e}", flush=True)
 
 
@@ -132,14 +146,7 @@ def test_bf16_small_backward(T, H, W, bg, seed, need256):
         op, exact = _check_head(wl, cfg, att, inp_cpu, h, o, lse)
         if not exact.all():
             pytest.skip("selection differs at a near-threshold block; gradient rows excluded")
-        g = oracle.attn_bwd(op, inp_cpu["q"][:, h], inp_cpu["k"][:, h], inp_cpu["v"][:, h],
-                            inp_cpu["dout"][:, h], with_mag=True)
-        for name, gpu, ref, mag in (("dq", dq, g[0], g[3]), ("dk", dk, g[1], g[4]),
-                                    ("dv", dv, g[2], g[5])):
-            err, ratio = check_close(gpu[:, h].float().cpu().numpy(), ref, "bf16",
-                                     f"head {h} {name}", mag)
-            print(f"head {h} {name}: max|ref| {np.abs(ref).max():.2f} max abs err {err:.3e} "
-                  f"(bound use {ratio:.2f})", flush=True)
+        _grads_vs_oracle(op, inp_cpu, h, dq, dk, dv, f"head {h}")
 
 
 def _unit_list_lengths(views, h):
@@ -148,13 +155,11 @@ def _unit_list_lengths(views, h):
     selected."""
     nb = int(views["zone_block"][h, -1])  # the head's block count
     bsz = views["block_size"][h, :nb].cpu().numpy() // 64
-    cnt = views["sel_count"][h, :nb].cpu().numpy()
-    col = views["csr_col"][h, :nb].cpu().numpy()
-    ccnt = views["csc_count"][h, :nb].cpu().numpy()
-    crow = views["csc_row"][h, :nb].cpu().numpy()
-    q_units = [int(bsz[col[i, :cnt[i]]].sum()) for i in range(nb)]
-    k_units = [int(bsz[crow[j, :ccnt[j]]].sum()) for j in range(nb) if ccnt[j] > 0]
-    return q_units, k_units, int((ccnt == 0).sum())
+    col = P.csr_rows(views, h, "csr")
+    crow = P.csr_rows(views, h, "csc")
+    q_units = [int(bsz[c].sum()) for c in col]
+    k_units = [int(bsz[r].sum()) for r in crow if len(r) > 0]
+    return q_units, k_units, sum(len(r) == 0 for r in crow)
 
 
 def test_bf16_short_lists():
@@ -182,14 +187,7 @@ def test_bf16_short_lists():
             if not exact.all():
                 print(f"k={k} head {h}: a near-threshold block differs; gradients not compared")
                 continue
-            g = oracle.attn_bwd(op, inp_cpu["q"][:, h], inp_cpu["k"][:, h],
-                                inp_cpu["v"][:, h], inp_cpu["dout"][:, h], with_mag=True)
-            for name, gpu, ref, mag in (("dq", dq, g[0], g[3]), ("dk", dk, g[1], g[4]),
-                                        ("dv", dv, g[2], g[5])):
-                err, ratio = check_close(gpu[:, h].float().cpu().numpy(), ref, "bf16",
-                                         f"k={k} head {h} {name}", mag)
-                print(f"k={k} head {h} {name}: max abs err {err:.3e} (bound use {ratio:.2f})",
-                      flush=True)
+            _grads_vs_oracle(op, inp_cpu, h, dq, dk, dv, f"k={k} head {h}")
     # the forward and dQ loops are unrolled by four stages, dK/dV by three
     assert fwd_res == {0, 1, 2, 3}, fwd_res
     assert kv_res == {0, 1, 2}, kv_res
@@ -213,7 +211,7 @@ def test_deterministic_rerun():
             nb = int(v["zone_block"][h, -1])
             c = v["sel_count"][h, :nb]
             lists.append(c.clone())
-            lists += [v["csr_col"][h, i, :int(c[i])].clone() for i in range(nb)]
+            lists += [torch.from_numpy(x) for x in P.csr_rows(v, h, "csr")]
         outs.append([o.clone(), lse.clone(), *[x.clone() for x in g], v["perm"].clone(),
                      *lists])
     assert len(outs[0]) == len(outs[1])
@@ -278,14 +276,7 @@ def test_bf16_fixed_shape_backward(shape):
         if not exact.all():
             print(f"head {h}: a near-threshold block differs; gradients not compared")
             continue
-        g = oracle.attn_bwd(op, inp_cpu["q"][:, h], inp_cpu["k"][:, h], inp_cpu["v"][:, h],
-                            inp_cpu["dout"][:, h], with_mag=True)
-        for name, gpu, ref, mag in (("dq", dq, g[0], g[3]), ("dk", dk, g[1], g[4]),
-                                    ("dv", dv, g[2], g[5])):
-            err, ratio = check_close(gpu[:, h].float().cpu().numpy(), ref, "bf16",
-                                     f"{shape} head {h} {name}", mag)
-            print(f"{shape} head {h} {name}: max abs err {err:.3e} (bound use {ratio:.2f})",
-                  flush=True)
+        _grads_vs_oracle(op, inp_cpu, h, dq, dk, dv, f"{shape} head {h}")
         compared += 1
     assert compared > 0
 
@@ -318,7 +309,145 @@ def test_bf16_strided_inputs_match_dense(layout):
         nb = int(vd["zone_block"][h, -1])
         cnt = vd["sel_count"][h, :nb]
         assert torch.equal(va["sel_count"][h, :nb], cnt)
-        keep = torch.arange(nb, device=cnt.device)[None, :] < cnt[:, None]
-        assert torch.equal(va["csr_col"][h, :nb, :nb][keep], vd["csr_col"][h, :nb, :nb][keep])
+        for a, b in zip(P.csr_rows(va, h, "csr"), P.csr_rows(vd, h, "csr")):
+            assert np.array_equal(a, b)
     for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), got, ref):
         assert torch.equal(a, b), name
+
+
+def test_call_order_is_enforced():
+    """A re-plan invalidates the forward state: a backward after it, with no forward, is
+    refused (by the binding and by the C ABI itself), as is a forward whose configuration
+    differs from the plan's; after a forward the backward runs again."""
+    wl = synth.custom(8, 16, 24, 2, 128, "bf16", top_k=4, top_p=0.8, seed=5)
+    _, inp = _inputs(wl, with_dout=True)
+    cfg = P.config_for(wl)
+    att = run_plan(cfg, inp)
+    o, lse = att.forward()
+    ref = att.backward(inp["dout"])
+    att.plan(inp["q"], inp["k"], inp["v"], inp["a2v"])
+    with pytest.raises(P.PrismError, match="forward"):
+        att.backward(inp["dout"])
+    dq, dk, dv = (torch.empty_like(inp["q"]) for _ in range(3))
+    with pytest.raises(P.PrismError, match="out of order"):
+        P.attn_bwd(cfg, att.ws, inp["dout"], dq, dk, dv)
+    other = P.config_for(wl, top_k=2)
+    with pytest.raises(P.PrismError, match="out of order"):
+        P.attn_fwd(other, att.ws, o, lse)
+    att.forward()
+    got = att.backward(inp["dout"])
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)
+
+
+def test_bf16_head_dim_64():
+    """bfloat16 with head_dim 64: the permuted float16 operands are zero-padded to 128
+    channels; plan, forward and backward against the oracle."""
+    wl = synth.custom(8, 16, 24, 2, 64, "bf16", top_k=4, top_p=0.8, seed=5)
+    inp_cpu, inp = _inputs(wl, with_dout=True)
+    cfg = P.config_for(wl)
+    att = run_plan(cfg, inp)
+    o, lse = att.forward()
+    dq, dk, dv = att.backward(inp["dout"])
+    torch.cuda.synchronize()
+    assert att.check() == [0] * wl.heads
+    for h in range(wl.heads):
+        op, exact = _check_head(wl, cfg, att, inp_cpu, h, o, lse)
+        if not exact.all():
+            print(f"head {h}: a near-threshold block differs; gradients not compared")
+            continue
+        _grads_vs_oracle(op, inp_cpu, h, dq, dk, dv, f"D=64 head {h}")
+
+
+def _all_nan(t):
+    return bool(torch.isnan(t.float()).all())
+
+
+def _all_finite(t):
+    return bool(torch.isfinite(t.float()).all())
+
+
+def test_out_of_range_inputs_are_flagged():
+    """bfloat16 q/k/v values beyond the float16 range of the attention operands: the head
+    gets PRISM_FLAG_QKV_RANGE, its outputs are NaN, and prism_check_flags reports it; the
+    other head is unaffected and still matches the oracle."""
+    wl = synth.custom(8, 16, 24, 2, 128, "bf16", top_k=4, top_p=0.8, seed=5)
+    inp_cpu, inp = _inputs(wl, with_dout=True)
+    for name, big in (("q", 7.0e4), ("k", -1.0e5), ("v", 3.0e38)):
+        bad = {n: t.clone() for n, t in inp.items()}
+        bad[name][100, 1, 5] = big          # head 1 only
+        cfg = P.config_for(wl)
+        att = run_plan(cfg, bad)
+        o, lse = att.forward()
+        dq, dk, dv = att.backward(bad["dout"])
+        torch.cuda.synchronize()
+        flags = att.check()
+        assert flags[0] == 0 and flags[1] & P.FLAG_QKV_RANGE, (name, flags)
+        with pytest.raises(P.PrismError, match="float16 range"):
+            P._check(P.lib().prism_check_flags(ctypes.byref(cfg), P._ws(att.ws)[0], None,
+                                               P._stream(None)), "check")
+        for t in (o[:, 1], lse[1], dq[:, 1], dk[:, 1], dv[:, 1]):
+            assert _all_nan(t), name
+        for t in (o[:, 0], lse[0], dq[:, 0], dk[:, 0], dv[:, 0]):
+            assert _all_finite(t), name
+    # head 0 of the last run still matches the oracle
+    _check_head(wl, cfg, att, inp_cpu, 0, o, lse)
+
+
+def test_out_of_range_gradients_are_flagged():
+    """An upstream gradient beyond the float16 range, or one large enough that the bound on
+    the float16 dS reaches it: the backward flags the head and its gradients are NaN; a
+    later backward with a normal gradient clears the flags."""
+    wl = synth.custom(8, 16, 24, 2, 128, "bf16", top_k=4, top_p=0.8, seed=5)
+    _, inp = _inputs(wl, with_dout=True)
+    cfg = P.config_for(wl)
+    att = run_plan(cfg, inp)
+    att.forward()
+    for scale, flag in ((1e5, P.FLAG_DOUT_RANGE), (3e3, P.FLAG_DS_RANGE)):
+        dout = inp["dout"].clone()
+        dout[:, 0] = (dout[:, 0].float() * scale).bfloat16()
+        dq, dk, dv = att.backward(dout)
+        flags = att.check()
+        assert flags[0] & flag and flags[1] == 0, (scale, flags)
+        for t in (dq[:, 0], dk[:, 0], dv[:, 0]):
+            assert _all_nan(t), scale
+        for t in (dq[:, 1], dk[:, 1], dv[:, 1]):
+            assert _all_finite(t), scale
+    dq, dk, dv = att.backward(inp["dout"])
+    assert att.check() == [0, 0]
+    assert _all_finite(dq) and _all_finite(dk) and _all_finite(dv)
+
+
+def test_selection_overflow_is_flagged():
+    """A selection-list capacity (max_pairs) below what the plan selects: the lists stay
+    inside the capacity, the heads are flagged and their outputs are NaN; with room for
+    every pair the same plan is unflagged and its lists are the full ones."""
+    wl = synth.custom(8, 16, 24, 2, 128, "bf16", top_k=4, top_p=0.8, seed=5)
+    _, inp = _inputs(wl, with_dout=True)
+    full = run_plan(P.config_for(wl), inp)
+    full.forward()
+    assert full.check() == [0, 0]
+    nnz = [int(full.views()["csr_ptr"][h, int(full.views()["zone_block"][h, -1])])
+           for h in range(wl.heads)]
+    cap = min(nnz) - 1
+    small = P.config_for(wl, max_pairs=cap)
+    att = run_plan(small, inp)
+    o, lse = att.forward()
+    dq, dk, dv = att.backward(inp["dout"])
+    flags = att.check()
+    assert all(f & P.FLAG_SELECTION_OVERFLOW for f in flags), flags
+    v = att.views()
+    for h in range(wl.heads):
+        nb = int(v["zone_block"][h, -1])
+        assert int(v["csr_ptr"][h, nb]) <= cap and int(v["csc_ptr"][h, nb]) <= cap
+        assert int(v["sel_count"][h, :nb].sum()) <= cap
+    for t in (o, lse, dq, dk, dv):
+        assert _all_nan(t)
+    exact = P.config_for(wl, max_pairs=max(nnz))
+    ok = run_plan(exact, inp)
+    ok.forward()
+    assert ok.check() == [0, 0]
+    for h in range(wl.heads):
+        for a, b in zip(P.csr_rows(ok.views(), h), P.csr_rows(full.views(), h)):
+            assert np.array_equal(a, b)
