@@ -4,10 +4,11 @@ decision margin is below 1e-9 are counted and excluded); selections bit-exact as
 key blocks whose logit lies within 1e-5 of the row's cut logit or whose inclusion by Top-p
 depends on a cumulative mass within 1e-5 of p (counted).  Attention outputs and gradients
 within max-abs 1e-4 (float32) or, for bfloat16, 2e-2 plus one bfloat16 ulp of the
-reference value, on rows whose selection matched.  One documented exception: dQ and dK,
-whose products take dS = P (dP - delta) as a float16 MFMA operand, are held to that bound
-widened by the float16 unit roundoff times the oracle's first-order size of their change
-under a relative perturbation of dS and of the forward's weights; their share of the
+reference value, on rows whose selection matched.  One documented exception: dQ, whose
+product takes dS = P (dP - delta) as a float16 MFMA operand and sums it against keys of
+norm up to a few hundred in rows dominated by a few large logits, is held to that bound
+widened by the float16 unit roundoff times the oracle's first-order size of its change
+under a relative perturbation of dS and of the forward's weights; its share of the
 unwidened bound is returned and printed as well."""
 from __future__ import annotations
 
@@ -28,7 +29,7 @@ def ulp_bf16(x):
 
 U16 = 2.0 ** -11   # unit roundoff of float16 (round to nearest even)
 # results whose bfloat16 bound carries the float16 dS allowance
-OPERAND_TERM = ("dq", "dk")
+OPERAND_TERM = ("dq",)
 
 
 class Closeness(tuple):
@@ -50,7 +51,7 @@ class Closeness(tuple):
 def check_close(got, ref, dtype, what="", mag=None):
     """float32: max-abs <= 1e-4.  bfloat16: |got - ref| <= 2e-2 + one bf16 ulp of ref (the
     stored result cannot be closer to the exact value than its own rounding step, which
-    exceeds 2e-2 once |ref| >= 8).  mag, given only for dQ and dK: the bound is widened by
+    exceeds 2e-2 once |ref| >= 8).  mag, given only for dQ: the bound is widened by
     U16 * mag, where mag is the oracle's first-order size of the result's change when each
     attention weight and each dS moves by a relative amount of at most 1 (the HIP path
     feeds dS to those products as float16; at unit-variance inputs the term is far below
@@ -73,7 +74,7 @@ def check_close(got, ref, dtype, what="", mag=None):
 
 
 def check_grads(grads, refs, mags, dtype, what=""):
-    """dq, dk, dv against the oracle: dV to the stated bound, dQ and dK with the float16
+    """dq, dk, dv against the oracle: dK and dV to the stated bound, dQ with the float16
     dS allowance.  grads, refs, mags: dicts by name.  Returns {name: Closeness}."""
     out = {}
     for name in ("dq", "dk", "dv"):
