@@ -70,6 +70,7 @@ class PrismError(RuntimeError):
 _lib = None
 EXPORTS = ["prism_workspace_bytes", "prism_plan_layout", "prism_plan_view", "prism_plan",
            "prism_attn_fwd", "prism_attn_bwd", "prism_a2v_norm", "prism_check_flags",
+           "prism_forward_static",
            "prism_status_string", "prism_last_error", "prism_trace_enable", "prism_trace_read",
            "prism_stage_name"]
 STAGES = ["audio_stats", "zone_stats", "quantize", "gather", "tiles", "scores", "select",
@@ -101,6 +102,9 @@ def lib():
         L.prism_a2v_norm.argtypes = [vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
                                      ctypes.c_int, vp, vp]
         L.prism_a2v_norm.restype = ctypes.c_int
+        L.prism_forward_static.argtypes = [cfgp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64,
+                                           vp, vp, vp, vp]
+        L.prism_forward_static.restype = ctypes.c_int
         L.prism_check_flags.argtypes = [cfgp, vp, vp, vp]
         L.prism_check_flags.restype = ctypes.c_int
         L.prism_status_string.argtypes = [ctypes.c_int]
@@ -265,6 +269,22 @@ def a2v_norm(x, out=None, stream=None):
     _check(lib().prism_a2v_norm(_ptr(x), n, x.shape[1], x.stride(0), dt, _ptr(out),
                                 _stream(stream)), "prism_a2v_norm")
     return out
+
+
+def forward_static(cfg, q, k, v, a2v, o, lse, stream=None):
+    """prism_forward_static: plan and forward with the library's static scratch as the
+    workspace (no device allocation; small configurations only)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _tok(cfg, t, name, strided=True)
+    if not (q.stride() == k.stride() == v.stride()):
+        raise ValueError("q, k, v must share their strides")
+    _tok(cfg, o, "o")
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (cfg.num_heads, cfg.N)
+            or not lse.is_contiguous() or not lse.is_cuda):
+        raise ValueError("lse: expected a contiguous float32 [heads, N] GPU tensor")
+    _check(lib().prism_forward_static(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v),
+                                      q.stride(0), q.stride(1), _ptr(a2v), _ptr(o), _ptr(lse),
+                                      _stream(stream)), "prism_forward_static")
 
 
 def check_flags(cfg, ws, stream=None):

@@ -81,6 +81,19 @@ bool same_config(const prism_config &a, const prism_config &b) {
 }
 }  // namespace
 
+// ---------------------------------------------------------------------------- static scratch
+// The workspace of prism_forward_static: a device array of fixed size that the library
+// owns, for callers that cannot allocate.  Each GPU the library runs on holds its own copy
+// until the process ends.  Host code never passes the array's name to a kernel or a copy
+// (on the host it is only a stand-in for the symbol): the device address of this GPU's
+// copy comes from hipGetSymbolAddress, taken once per device on its first call.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+namespace {
+std::mutex g_scratch_mu;
+std::unordered_map<int, void *> g_scratch_ptr;  // device -> address of its scratch copy
+}  // namespace
+
 static thread_local std::string g_last_error;
 
 static prism_status fail(prism_status st, const std::string &msg) {
@@ -384,6 +397,43 @@ prism_status prism_attn_bwd(const prism_config *cfg, void *workspace, size_t wor
   return launched(launch_attn_bwd(d, sc.softmax, (uint8_t *)workspace, L, dout, dq, dk, dv,
                                   (hipStream_t)stream),
                   "attention backward");
+}
+
+prism_status prism_forward_static(const prism_config *cfg, const void *q, const void *k,
+                                  const void *v, int64_t tok_stride, int64_t head_stride,
+                                  const float *a2v_norm, void *o, float *lse, void *stream) {
+  Dims d;
+  const char *why;
+  prism_status st = check_config(cfg, &d, &why);
+  if (st != PRISM_OK) return fail(st, why);
+  if (!q || !k || !v || !o || !lse) return fail(PRISM_ERR_ARG, "null tensor");
+  const size_t need = make_layout(d).total;
+  if (need > kScratchBytes)
+    return fail(PRISM_ERR_WORKSPACE,
+                "prism_forward_static: this configuration needs " + std::to_string(need) +
+                    " bytes of workspace, more than the " + std::to_string(kScratchBytes) +
+                    "-byte static scratch (use prism_plan and prism_attn_fwd with a "
+                    "workspace)");
+  int dev = 0;
+  if ((st = launched(hipGetDevice(&dev), "prism_forward_static"))) return st;
+  void *ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch_ptr.find(dev);
+    if (it == g_scratch_ptr.end()) {
+      if ((st = launched(hipGetSymbolAddress(&ws, HIP_SYMBOL(scratch)), "scratch address")))
+        return st;
+      g_scratch_ptr[dev] = ws;
+    } else {
+      ws = it->second;
+    }
+  }
+  // the plan fills every array the forward reads (flags and maxima are cleared by the
+  // plan itself), so nothing of the previous call's contents needs clearing
+  if ((st = prism_plan(cfg, q, k, v, tok_stride, head_stride, a2v_norm, ws, kScratchBytes,
+                       stream)))
+    return st;
+  return prism_attn_fwd(cfg, ws, kScratchBytes, o, lse, stream);
 }
 
 const char *prism_status_string(int status) {

@@ -191,6 +191,19 @@ prism_status prism_a2v_norm(const void *x, int64_t n_tokens, int channels, int64
 prism_status prism_attn_bwd(const prism_config *cfg, void *workspace, size_t workspace_bytes,
                             const void *dout, void *dq, void *dk, void *dv, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): prism_plan followed by prism_attn_fwd,
+ * with the workspace taken from a static scratch array of 128 MiB that the library holds
+ * on each GPU it runs on until the process ends.  Arguments as in prism_plan (q, k, v,
+ * strides, a2v_norm) and prism_attn_fwd (o, lse); allocates nothing (no hipMalloc, no
+ * allocating library call).  Configurations whose workspace (prism_workspace_bytes)
+ * exceeds 128 MiB are refused with PRISM_ERR_WORKSPACE before any launch.  Every call on
+ * one GPU shares that GPU's scratch and leaves its plan there: calls that overlap on one
+ * GPU (from several threads or streams) race; a prism_attn_bwd cannot follow. */
+prism_status prism_forward_static(const prism_config *cfg, const void *q, const void *k,
+                                  const void *v, int64_t tok_stride, int64_t head_stride,
+                                  const float *a2v_norm, void *o, float *lse, void *stream);
+
 /* Waits for the work queued on stream, then copies the per-head status flags of
  * workspace into flags[heads] (host memory; may be NULL) and returns PRISM_ERR_RANGE if any
  * head has a flag set, PRISM_OK otherwise.  This is the one entry point that synchronises

@@ -193,3 +193,15 @@ def test_check_flags_rejects_bad_arguments(lib):
     assert lib.prism_check_flags(ctypes.byref(cfg), None, None, None) == -1
     bad = P.make_config(12, 16, 16, 2, 128, "bf16")
     assert lib.prism_check_flags(ctypes.byref(bad), ctypes.c_void_p(256), None, None) == -2
+
+
+def test_static_forward_refuses_what_exceeds_its_scratch(lib):
+    """prism_forward_static checks the workspace its configuration needs against its static
+    scratch before touching the GPU: the 720p workload (24 heads) is refused."""
+    cfg = P.make_config(24, 48, 80, 24, 128, "bf16", top_k=8, top_p=0.9)
+    assert lib.prism_workspace_bytes(ctypes.byref(cfg)) > 128 << 20
+    d = ctypes.c_void_p(4096)
+    assert lib.prism_forward_static(ctypes.byref(cfg), d, d, d, 0, 0, None, d, d, None) == -3
+    assert b"static scratch" in lib.prism_last_error()
+    assert lib.prism_forward_static(ctypes.byref(cfg), None, d, d, 0, 0, None, d, d,
+                                    None) == -1
