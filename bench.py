@@ -36,6 +36,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # hash of the kernel sources they were taken with: a kernel changed since reports null.
 KERNEL_SOURCES = {"attn_fwd": "attn_fwd.hip", "bwd_dkdv": "attn_bwd_dkdv.hip",
                   "bwd_dq": "attn_bwd.hip"}
+TRAFFIC_SOURCE = "profiles/attention_2k_train_pmc_traffic.md"
 MEASURED_TRAFFIC = {
     ("attn_fwd", "2k-train-64x104x128"): ("192c0ff358424f69", 30.777e12),
     ("bwd_dkdv", "2k-train-64x104x128"): ("20352c6fcd989e62", 49.600e12),
@@ -463,6 +464,7 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(dom, wl.name),
+                "traffic_source": TRAFFIC_SOURCE,
                 "launch_ms": round(per_launch_ms, 3)}
     if roofline["traffic"] is not None:
         roofline["traffic_note"] = ("HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "

@@ -12,8 +12,8 @@
 //   dK/dV -- one workgroup per key tile (pairs of waves over 32 keys, K or V rows held in
 //            registers), streaming the 64-token query units of every query block that
 //            selected the key block (the transposed selection lists);
-//   dQ    -- one workgroup per query block (32 queries per wave, Q and dO in registers),
-//            streaming the selected key units as in the forward pass.
+//   dQ    -- one workgroup per query tile of 256 rows (32 queries per wave, Q and dO in
+//            registers), streaming the selected key units as in the forward pass.
 // Both MFMA passes recompute P from the stored lse and run on the float16 MFMA: the
 // permuted copies are float16, the transposed operands (K^T, Q^T, dO^T) are read from
 // the row-major LDS tiles with transposing LDS reads, P is fed scaled by 2^10 (as in the
@@ -123,8 +123,9 @@ __global__ void clear_bwd_flags_kernel(int heads, uint32_t *__restrict__ flags) 
 }
 
 // ============================================================================ dQ (bf16)
-// One workgroup of eight waves (two per SIMD) per query block (32 queries per wave, Q and
-// dO rows held as B operands), streaming the selected key units through a four-stage LDS
+// One workgroup of eight waves (two per SIMD) per query tile of 256 rows (32 queries per
+// wave, Q and dO rows held as B operands; a wave computes only the units its own block
+// selected), streaming the key units of the tile's union list through a four-stage LDS
 // ring of direct global->LDS copies, two units ahead of the one being computed: per stage
 // K and V row-major [64][128] float16 (32 KB); waves 0-3 copy 16 K rows each, waves 4-7
 // 16 V rows, four one-kilobyte copies per wave and unit.  Per unit a wave forms S^T and
@@ -230,8 +231,8 @@ __device__ __forceinline__ void dq_waves(
     const uint16_t *__restrict__ vp, const uint16_t *__restrict__ dop,
     const float *__restrict__ lse2, const float *__restrict__ ndelta,
     const int *__restrict__ unit_blk, const int *__restrict__ blk_start,
-    const int *__restrict__ blk_size, const int *__restrict__ sel_count,
-    const int *__restrict__ csr_ptr, const int *__restrict__ csr_col, long long cap,
+    const int *__restrict__ blk_size, int Z, const int *__restrict__ qt_count,
+    const int *__restrict__ qt_ptr, const int *__restrict__ qt_list, long long cap,
     const int *__restrict__ perm, float scale, float scale_log2e, int dio,
     const uint32_t *__restrict__ flags, uint16_t *__restrict__ dq) {
   const int l32 = lane & 31, hh = lane >> 5;
@@ -245,18 +246,19 @@ __device__ __forceinline__ void dq_waves(
     const int2 tl = tiles[t];
     const int h = __builtin_amdgcn_readfirstlane(tl.x);
     const int ty = __builtin_amdgcn_readfirstlane(tl.y);
-    const int u0 = ty & 0xffff, rows = (ty >> 16) * kUnit;
-    const bool active = wave * 32 < rows;
+    // 256 query rows: one block of 256, two of 128 or four of 64 tokens; the tile's list is
+    // the union of its blocks' lists, each entry with the mask of the blocks that selected it
+    const int u0 = ty & 0xffff, lb = (ty >> 16) & 3;
+    const int g = (32 * wave) >> (6 + lb);  // this wave's block within the tile
+    const int qslot = u0 >> 2;
     const int blk = unit_blk[(size_t)h * U + u0];
     const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
-    BlockUnits pre;
-    pre.init(csr_col + (size_t)h * cap + csr_ptr[(size_t)h * (nb_max + 1) + blk],
-             sel_count[(size_t)h * nb_max + blk], bs, bz, lane, blk);
+    BlockUnits<true> pre;
+    pre.init(qt_list + (size_t)h * cap + qt_ptr[(size_t)h * (2 * Z + 1) + qslot],
+             qt_count[(size_t)h * 2 * Z + qslot], bs, bz, lane, blk);
     const int row0 = u0 * kUnit + wave * 32;
     DqState w;
-    w.lse2 = 0.f;
-    w.ndlt = 0.f;
-    if (active) {
+    {
       const uint16_t *qr = qp + ((size_t)h * N + row0 + l32) * kDB + 8 * hh;
       const uint16_t *dr = dop + ((size_t)h * N + row0 + l32) * kDB + 8 * hh;
 #pragma unroll
@@ -269,47 +271,60 @@ __device__ __forceinline__ void dq_waves(
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) w.acc[dt] = f32x16{};
-    // the late wave's dQ product of the first step multiplies by zero (no previous unit)
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int g = 0; g < 2; ++g) w.db[a][g] = f16x8{};
+      for (int q = 0; q < 2; ++q) w.db[a][q] = f16x8{};
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // rows and cursor window in before any copy
 
     const uint8_t *hbase = csrc + (size_t)h * N * kDB * 2;
     int issued = 0;
     bool pending = true;
+    int smask[kQStages];  // the entry mask of the unit in each stage
     // kQCpw copies per step; past the end of the list they repeat the last unit into a
     // stage no step reads any more (drained before the next tile)
-    auto issue = [&](DqStage &st) {
+    auto issue = [&](auto stage_tag) {
+      constexpr int X = decltype(stage_tag)::value;
       const uint8_t *src = hbase + (size_t)pre.unit() * kUnit * kDB * 2;
-      copy_rows16(src, c0, reinterpret_cast<uint8_t *>(&st) + cdst);
+      copy_rows16(src, c0, reinterpret_cast<uint8_t *>(&dq_stage<X>()) + cdst);
+      smask[X] = pre.mask;
       if (pending) {
         ++issued;
         pending = pre.next();
       }
     };
     // step u (stage S = u mod 4): wait for unit u (u + 1 stays in flight), refill the stage
-    // of unit u - 2 with unit u + 2, compute.  One step past the last unit finishes the
-    // late wave's dQ product.  Returns whether unit u existed.
+    // of unit u - 2 with unit u + 2, compute the units this wave's block selected.  One step
+    // past the last unit finishes the late wave's dQ product.  Returns whether unit u
+    // existed.
     auto step = [&](auto stage_tag, int u) {
       constexpr int S = decltype(stage_tag)::value;
       dq_wait_one_behind();
       // issued counts the units up to u + 1 at least, or all of them
       const bool unit_u = u < issued;
+      const bool on = unit_u && ((smask[S] >> g) & 1);
       const uint32_t st = dq_stage_addr<S>();
       if constexpr (LATE) {
         // the late wave issues its copies after its dQ product, so that right after the
         // barrier the early waves' copies and score products go first
+        // (the product of a unit this wave skipped, or of none at u = 0, takes zero dS: a
+        // conditional product here would make the compiler spill)
         const uint32_t prev = dq_stage_addr<(S + kQStages - 1) % kQStages>();
-        if (active) dq_update(w, u == 0 ? st : prev, lane);
-        issue(dq_stage<(S + 2) % kQStages>());
+        dq_update(w, u == 0 ? st : prev, lane);
+        issue(std::integral_constant<int, (S + 2) % kQStages>{});
         if (!unit_u) return false;
-        if (active) dq_scores(w, st, lane, scale_log2e);
+        if (on) {
+          dq_scores(w, st, lane, scale_log2e);
+        } else {
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) w.db[a][q] = f16x8{};
+        }
       } else {
-        issue(dq_stage<(S + 2) % kQStages>());
+        issue(std::integral_constant<int, (S + 2) % kQStages>{});
         if (!unit_u) return false;
-        if (active) {
+        if (on) {
           dq_scores(w, st, lane, scale_log2e);
           dq_update(w, st, lane);
         }
@@ -318,8 +333,8 @@ __device__ __forceinline__ void dq_waves(
     };
 
     workgroup_barrier();  // every wave is done with the previous tile's stages
-    issue(g_dq0);
-    issue(g_dq1);
+    issue(std::integral_constant<int, 0>{});
+    issue(std::integral_constant<int, 1>{});
     for (int i = 0;; i += kQStages) {
       if (!step(std::integral_constant<int, 0>{}, i)) break;
       if (!step(std::integral_constant<int, 1>{}, i + 1)) break;
@@ -327,7 +342,6 @@ __device__ __forceinline__ void dq_waves(
       if (!step(std::integral_constant<int, 3>{}, i + 3)) break;
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the trailing repeat copies
-    if (!active) continue;
     const int token = perm[(size_t)h * N + row0 + l32];
     uint16_t *qrow = dq + ((size_t)token * heads + h) * dio;
     // any status flag of the head (operand range, selection overflow, dS bound): NaN
@@ -354,21 +368,22 @@ __global__ void __launch_bounds__(QW * 64)
                         const uint16_t *__restrict__ dop, const float *__restrict__ lse2,
                         const float *__restrict__ ndelta, const int *__restrict__ unit_blk,
                         const int *__restrict__ blk_start, const int *__restrict__ blk_size,
-                        const int *__restrict__ sel_count, const int *__restrict__ csr_ptr,
-                        const int *__restrict__ csr_col, long long cap,
-                        const int *__restrict__ perm, float scale, float scale_log2e, int dio,
-                        const uint32_t *__restrict__ flags, uint16_t *__restrict__ dq) {
+                        int Z, const int *__restrict__ qt_count,
+                        const int *__restrict__ qt_ptr, const int *__restrict__ qt_list,
+                        long long cap, const int *__restrict__ perm, float scale,
+                        float scale_log2e, int dio, const uint32_t *__restrict__ flags,
+                        uint16_t *__restrict__ dq) {
   // the wave index is uniform in the wave; the two roles run the same sequence of barriers
   // and copies
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int ntiles = *tile_count;
   if (wave < QW / 2)
     dq_waves<false>(wave, lane, N, U, nb_max, heads, tiles, ntiles, qp, kp, vp, dop, lse2,
-                    ndelta, unit_blk, blk_start, blk_size, sel_count, csr_ptr, csr_col, cap,
+                    ndelta, unit_blk, blk_start, blk_size, Z, qt_count, qt_ptr, qt_list, cap,
                     perm, scale, scale_log2e, dio, flags, dq);
   else
     dq_waves<true>(wave, lane, N, U, nb_max, heads, tiles, ntiles, qp, kp, vp, dop, lse2,
-                   ndelta, unit_blk, blk_start, blk_size, sel_count, csr_ptr, csr_col, cap,
+                   ndelta, unit_blk, blk_start, blk_size, Z, qt_count, qt_ptr, qt_list, cap,
                    perm, scale, scale_log2e, dio, flags, dq);
 }
 
@@ -555,17 +570,18 @@ hipError_t launch_attn_bwd(const Dims &d, float scale, uint8_t *ws, const Layout
     const int2 *tiles = (const int2 *)(ws + L.tiles), *btiles = (const int2 *)(ws + L.btiles);
     {
       TraceScope tr(PRISM_STAGE_BWD_DKDV, s);
-      (void)launch_dkdv_bf16(maxt, s, d.N, d.U, d.nb_max, d.heads, tiles, counters, qp, kp, vp, dop,
-                       lse2, delta, unit_blk, bstart, bsize, tcnt, tptr, trows, d.cap, perm,
-                       scale, sl2e, d.D, flags, (T *)dk, (T *)dv);
+      (void)launch_dkdv_bf16(maxt, s, d.N, d.U, d.nb_max, d.heads, tiles, counters, qp, kp,
+                             vp, dop, lse2, delta, unit_blk, bstart, bsize, tcnt, tptr, trows,
+                             d.cap, perm, scale, sl2e, d.D, flags, (T *)dk, (T *)dv);
     }
     {
       TraceScope tr(PRISM_STAGE_BWD_DQ, s);
       const int grid = resident_grid((const void *)attn_dq_bf16_kernel, QW * 64, maxt);
       hipLaunchKernelGGL(attn_dq_bf16_kernel, dim3(grid), dim3(QW * 64), 0, s, d.N, d.U,
                          d.nb_max, d.heads, btiles, counters + 1, qp, kp, vp, dop, lse2, delta,
-                         unit_blk, bstart, bsize, cnt, cptr, cols, d.cap, perm, scale, sl2e,
-                         d.D, flags, (T *)dq);
+                         unit_blk, bstart, bsize, d.Z, (const int *)(ws + L.qt_count),
+                         (const int *)(ws + L.qt_ptr), (const int *)(ws + L.qt_list), d.cap,
+                         perm, scale, sl2e, d.D, flags, (T *)dq);
     }
   } else {
     typedef float T;

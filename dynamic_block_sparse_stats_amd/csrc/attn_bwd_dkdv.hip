@@ -290,7 +290,7 @@ __device__ __forceinline__ void dkdv_waves(
     const size_t hb = (size_t)h * N;
     int issued = 0;
     bool pending = true;
-    BlockUnits pre;
+    BlockUnits<false> pre;
     // every step issues this wave's copies: past the end of the list they repeat the last
     // unit (finite data) into a stage no step reads any more, or reads only for a result
     // it discards (drained before the next tile)

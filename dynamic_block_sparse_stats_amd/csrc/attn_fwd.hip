@@ -6,15 +6,16 @@
 //
 // bfloat16 path, head_dim 128, gfx950 MFMA v_mfma_f32_32x32x16_f16 (the planner stores
 // the permuted Q, K, V as float16: exact for bfloat16 values inside the float16 range):
-//   * a workgroup (8 waves, two per SIMD) owns one query block: 256, 128 or 64 rows, 32
-//     per wave (waves past the block's rows only help stage K/V); each wave keeps its 32
-//     query rows in registers as the B operand; one workgroup per CU, persistent over the
-//     list of blocks;
-//   * the key units of the block's selected key blocks stream through a four-stage LDS
-//     ring (128 KB) filled by direct global->LDS copies, two units ahead of the one being
-//     computed (the fourth stage is still being read by the late waves, below): K and V as
-//     [64 keys][128] float16, XOR-swizzled by 16-byte chunk; K rows are read directly, V^T
-//     with transposing LDS reads (ds_read_b64_tr_b16);
+//   * a workgroup (8 waves, two per SIMD) owns one query tile of 256 rows: one block of
+//     256, two of 128 or four of 64 tokens, 32 rows per wave; each wave keeps its 32 query
+//     rows in registers as the B operand; one workgroup per CU, persistent over the tiles;
+//   * the key units of the union of the tile's blocks' selections stream through a
+//     four-stage LDS ring (128 KB) filled by direct global->LDS copies, two units ahead of
+//     the one being computed (the fourth stage is still being read by the late waves,
+//     below): K and V as [64 keys][128] float16, XOR-swizzled by 16-byte chunk; K rows are
+//     read directly, V^T with transposing LDS reads (ds_read_b64_tr_b16); each wave
+//     computes only the units its own block selected (an entry's mask bit), so with blocks
+//     of 64 or 128 tokens every wave still has work;
 //   * the two waves of a SIMD run half a unit apart (the late one finishes the previous
 //     unit's PV product and forms its scores, then issues its copies, while the early one
 //     issues its copies and forms its scores), each wave raises its issue priority while it
@@ -195,8 +196,8 @@ __device__ __forceinline__ void fwd_waves(
     int ntiles, const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
     const uint16_t *__restrict__ vp, const int *__restrict__ unit_blk,
     const int *__restrict__ blk_start, const int *__restrict__ blk_size,
-    const int *__restrict__ sel_count, const int *__restrict__ csr_ptr,
-    const int *__restrict__ csr_col, long long cap, const int *__restrict__ perm,
+    int Z, const int *__restrict__ qt_count, const int *__restrict__ qt_ptr,
+    const int *__restrict__ qt_list, long long cap, const int *__restrict__ perm,
     float scale_log2e, int dio, const uint32_t *__restrict__ flags, uint16_t *__restrict__ out,
     float *__restrict__ lse_out, float *__restrict__ o32p, float *__restrict__ lsep) {
   const int l32 = lane & 31, hh = lane >> 5;
@@ -210,18 +211,21 @@ __device__ __forceinline__ void fwd_waves(
     const int2 tl = tiles[t];
     const int h = __builtin_amdgcn_readfirstlane(tl.x);
     const int ty = __builtin_amdgcn_readfirstlane(tl.y);
-    const int u0 = ty & 0xffff, rows = (ty >> 16) * kUnit;
-    const bool active = wave * 32 < rows;
+    // 256 query rows: one block of 256, two of 128 or four of 64 tokens; the tile's list is
+    // the union of its blocks' lists, each entry with the mask of the blocks that selected it
+    const int u0 = ty & 0xffff, lb = (ty >> 16) & 3;
+    const int g = (32 * wave) >> (6 + lb);  // this wave's block within the tile
+    const int qslot = u0 >> 2;
     const int blk = unit_blk[(size_t)h * U + u0];
     const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
-    BlockUnits pre;  // the issuing cursor; compute only counts units
-    pre.init(csr_col + (size_t)h * cap + csr_ptr[(size_t)h * (nb_max + 1) + blk],
-             sel_count[(size_t)h * nb_max + blk], bs, bz, lane, blk);
+    BlockUnits<true> pre;  // the issuing cursor
+    pre.init(qt_list + (size_t)h * cap + qt_ptr[(size_t)h * (2 * Z + 1) + qslot],
+             qt_count[(size_t)h * 2 * Z + qslot], bs, bz, lane, blk);
 
     // this wave's 32 query rows as B operands: Q[row][16kk + 8hh .. +8]
     const int row0 = u0 * kUnit + wave * 32;
     FwdState w;
-    if (active) {
+    {
       const uint16_t *qrow = qp + ((size_t)h * N + row0 + l32) * kD + 8 * hh;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
@@ -239,51 +243,62 @@ __device__ __forceinline__ void fwd_waves(
     const uint8_t *hbase = csrc + (size_t)h * N * kD * 2;
     int issued = 0;
     bool pending = true;  // pre points at a unit not yet issued
+    int smask[kStages];   // the entry mask of the unit in each stage
     // every step issues kCpw copies: past the end of the list they repeat the last unit
     // into a stage no step reads any more (drained before the next tile)
-    auto issue = [&](FwdStage &st) {
+    auto issue = [&](auto stage_tag) {
+      constexpr int X = decltype(stage_tag)::value;
       const uint8_t *src = hbase + (size_t)pre.unit() * kUnit * kD * 2;
-      copy_rows16(src, c0, reinterpret_cast<uint8_t *>(&st) + cdst);
+      copy_rows16(src, c0, reinterpret_cast<uint8_t *>(&fwd_stage<X>()) + cdst);
+      smask[X] = pre.mask;
       if (pending) {
         ++issued;
         pending = pre.next();
       }
     };
     // step u (stage S = u mod 4): wait for unit u (unit u + 1 stays in flight), refill the
-    // stage of unit u - 2 (no wave reads it any more) with unit u + 2, compute.  One step
-    // past the last unit finishes the late wave's PV product; the late wave's product in
-    // the first step multiplies unit 0's V by zero weights (adds nothing).  Returns whether
-    // unit u existed.
+    // stage of unit u - 2 (no wave reads it any more) with unit u + 2, compute the units
+    // this wave's block selected.  One step past the last unit finishes the late wave's PV
+    // product.  Returns whether unit u existed.
     auto step = [&](auto stage_tag, int u) {
       constexpr int S = decltype(stage_tag)::value;
       wait_unit_one_behind();
       // issued counts the units up to u + 1 at least, or all of them
       const bool unit_u = u < issued;
+      const bool on = unit_u && ((smask[S] >> g) & 1);
       const uint32_t st = fwd_stage_addr<S>();
       if constexpr (LATE) {
         // the late wave issues its copies at the end of its step, so that right after the
         // barrier the early waves' copies and score products go first
+        // (the product of a unit this wave skipped, or of none at u = 0, takes zero
+        // weights: a conditional product here would make the compiler spill)
         const uint32_t prev = fwd_stage_addr<(S + kStages - 1) % kStages>();
-        if (active) fwd_values(w, (u == 0 ? st : prev) + 16384, lane);
-        if (unit_u && active) fwd_scores(w, st, lane, scale_log2e);
-        issue(fwd_stage<(S + 2) % kStages>());
+        fwd_values(w, (u == 0 ? st : prev) + 16384, lane);
+        if (on) {
+          fwd_scores(w, st, lane, scale_log2e);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) w.pb[q] = f16x8{};
+        }
+        issue(std::integral_constant<int, (S + 2) % kStages>{});
         if (!unit_u) return false;
       } else {
-        issue(fwd_stage<(S + 2) % kStages>());
+        issue(std::integral_constant<int, (S + 2) % kStages>{});
         if (!unit_u) return false;
-        if (active) {
+        if (on) {
           fwd_scores(w, st, lane, scale_log2e);
           fwd_values(w, st + 16384, lane);
         }
       }
       return true;
     };
+
 #pragma unroll
-    for (int g = 0; g < 4; ++g) w.pb[g] = f16x8{};
+    for (int q = 0; q < 4; ++q) w.pb[q] = f16x8{};
 
     workgroup_barrier();  // every wave is done with the previous tile's stages
-    issue(g_fwd0);
-    issue(g_fwd1);
+    issue(std::integral_constant<int, 0>{});
+    issue(std::integral_constant<int, 1>{});
     for (int i = 0;; i += kStages) {
       if (!step(std::integral_constant<int, 0>{}, i)) break;
       if (!step(std::integral_constant<int, 1>{}, i + 1)) break;
@@ -292,7 +307,6 @@ __device__ __forceinline__ void fwd_waves(
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the trailing repeat copies
     // epilogue
-    if (!active) continue;
     const double ltot = w.lsum + __shfl_xor(w.lsum, 32, 64);  // the two half waves' keys
     // a head whose operands left the float16 range or whose selection overflowed its
     // lists gets NaN outputs
@@ -337,9 +351,10 @@ __global__ void __launch_bounds__(NW * 64)
                          const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
                          const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
                          const int *__restrict__ unit_blk, const int *__restrict__ blk_start,
-                         const int *__restrict__ blk_size, const int *__restrict__ sel_count,
-                         const int *__restrict__ csr_ptr, const int *__restrict__ csr_col,
-                         long long cap, const int *__restrict__ perm, float scale_log2e, int dio,
+                         const int *__restrict__ blk_size, int Z,
+                         const int *__restrict__ qt_count, const int *__restrict__ qt_ptr,
+                         const int *__restrict__ qt_list, long long cap,
+                         const int *__restrict__ perm, float scale_log2e, int dio,
                          const uint32_t *__restrict__ flags, uint16_t *__restrict__ out,
                          float *__restrict__ lse_out, float *__restrict__ o32p,
                          float *__restrict__ lsep) {
@@ -350,12 +365,12 @@ __global__ void __launch_bounds__(NW * 64)
   // the two roles run the same sequence of barriers and copies
   if (wave < NW / 2)
     fwd_waves<false>(wave, lane, N, U, nb_max, heads, tiles, ntiles, qp, kp, vp, unit_blk,
-                     blk_start, blk_size, sel_count, csr_ptr, csr_col, cap, perm, scale_log2e,
-                     dio, flags, out, lse_out, o32p, lsep);
+                     blk_start, blk_size, Z, qt_count, qt_ptr, qt_list, cap, perm,
+                     scale_log2e, dio, flags, out, lse_out, o32p, lsep);
   else
     fwd_waves<true>(wave, lane, N, U, nb_max, heads, tiles, ntiles, qp, kp, vp, unit_blk,
-                    blk_start, blk_size, sel_count, csr_ptr, csr_col, cap, perm, scale_log2e,
-                    dio, flags, out, lse_out, o32p, lsep);
+                    blk_start, blk_size, Z, qt_count, qt_ptr, qt_list, cap, perm,
+                    scale_log2e, dio, flags, out, lse_out, o32p, lsep);
 }
 
 // ---------------------------------------------------------------------------- float32
@@ -456,8 +471,10 @@ hipError_t launch_attn_fwd(const Dims &d, float scale, uint8_t *ws, const Layout
     hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, d.N, d.U,
                        d.nb_max, d.heads, (const int2 *)(ws + L.btiles), counters + 1,
                        (const uint16_t *)(ws + L.qp), (const uint16_t *)(ws + L.kp),
-                       (const uint16_t *)(ws + L.vp), unit_blk, bstart, bsize, cnt, cptr, cols,
-                       d.cap, perm, sl2e, d.D, flags, (uint16_t *)o, lse, o32p, lsep);
+                       (const uint16_t *)(ws + L.vp), unit_blk, bstart, bsize, d.Z,
+                       (const int *)(ws + L.qt_count), (const int *)(ws + L.qt_ptr),
+                       (const int *)(ws + L.qt_list), d.cap, perm, sl2e, d.D, flags,
+                       (uint16_t *)o, lse, o32p, lsep);
   } else {
     dim3 grid(d.U, d.heads);
     if (d.D == 64)

@@ -553,71 +553,65 @@ hipError_t launch_gather(const Dims &d, const void *q, const void *k, const void
 }
 
 // ============================================================================ tile lists
-// Attention work items.  Key tiles (dK/dV, `tiles`): 128 keys inside blocks of 128 or 256
-// tokens, 64 keys for 64-token blocks (the 64-token atomic unit of the digest's training
-// section; 128- and 256-token blocks are 2 and 4 units); entry (head, first unit | kTile64
-// flag).  Block tiles (forward, dQ, `btiles`): one query block each; entry (head, first unit
-// | units << 16).  The same partition serves queries and keys because Q, K and V share it.
-// The order of a list changes no result, only which tiles run together.
-//
-// Block tiles are in (head, zone, position) order: the persistent kernels take tiles t,
-// t + grid, ..., so the workgroups resident at any moment work on tiles of one head.  Key
-// tiles put the 256-token blocks first (four tiles per zone, so the two halves of a block
-// sit at positions 2p and 2p + 1), then the zones of smaller blocks, whose shorter tiles
-// then even out the end of the walk; counters[2] holds the number of tiles of the first
-// part.  The dK/dV kernel gives the two halves of a block (same query units, same cost) to
-// two workgroups of one XCD.
+// Attention work items (the digest's training section: 64-token atomic units; blocks of 128
+// and 256 tokens are 2 and 4 units).
+//   * Query tiles (forward, dQ; `btiles`): 256 rows each, two per zone whatever its block
+//     volume: one block of 256, two of 128 or four of 64 tokens.  Each of the workgroup's
+//     eight waves owns 32 rows, so every wave has rows; a wave works on the key units of the
+//     tile's union list that its own block selected.  Entry (head, first unit |
+//     (log2 B - 6) << 16).
+//   * Key tiles (dK/dV; `tiles`): 128 keys inside blocks of 128 or 256 tokens (two per
+//     256-token block), 64 keys for a 64-token block; entry (head, first unit | kTile64 for
+//     64 keys).
+// The order of a list changes no result, only which tiles run together.  Query tiles are in
+// (head, zone, position) order: the persistent kernels take tiles t, t + grid, ..., so the
+// workgroups resident at any moment work on tiles of one head.  Key tiles put the zones of
+// 256-token blocks first (the two halves of a block at positions 2p and 2p + 1), then the
+// zones of smaller blocks, whose shorter tiles even out the end of the walk; counters[2]
+// holds the number of tiles of the first part.  The dK/dV kernel gives the two halves of a
+// block (same query units, same cost) to two workgroups of one XCD.
 constexpr int kTileThreads = 1024;
 
 __global__ void __launch_bounds__(kTileThreads)
     tiles_kernel(int heads, int Z, const int *__restrict__ zshape, int2 *tiles, int2 *btiles,
                  int *counters) {
-  __shared__ int pscan[kTileThreads], rscan[kTileThreads], bscan[kTileThreads];
+  __shared__ int pscan[kTileThreads], rscan[kTileThreads];
   const int tid = threadIdx.x, n = heads * Z;
   const int chunk = (n + kTileThreads - 1) / kTileThreads;
   const int i0 = min(n, tid * chunk), i1 = min(n, i0 + chunk);
-  // units per block: log2 of the block volume is the sum of the log2 edges (6, 7 or 8)
-  auto bunits = [&](int idx) {
+  // log2 of the block volume minus 6: 0, 1 or 2 for blocks of 64, 128 or 256 tokens
+  auto lb_of = [&](int idx) {
     const int code = zshape[idx];
-    return 1 << (((code >> 4) & 3) + ((code >> 2) & 3) + (code & 3) - 6);
+    return ((code >> 4) & 3) + ((code >> 2) & 3) + (code & 3) - 6;
   };
-  // key tiles of a zone: four of 128 keys (128- and 256-token blocks) or eight of 64
-  auto ntile = [&](int idx) { return bunits(idx) >= 2 ? 4 : 8; };
-  int plocal = 0, rlocal = 0, blocal = 0;
+  int plocal = 0, rlocal = 0;
   for (int i = i0; i < i1; ++i) {
-    if (bunits(i) == 4)
+    const int lb = lb_of(i);
+    if (lb == 2)
       plocal += 4;
     else
-      rlocal += ntile(i);
-    blocal += 8 / bunits(i);
+      rlocal += lb == 1 ? 4 : 8;
   }
   pscan[tid] = plocal;
   rscan[tid] = rlocal;
-  bscan[tid] = blocal;
   __syncthreads();
   for (int off = 1; off < kTileThreads; off <<= 1) {
     const int padd = tid >= off ? pscan[tid - off] : 0;
     const int radd = tid >= off ? rscan[tid - off] : 0;
-    const int badd = tid >= off ? bscan[tid - off] : 0;
     __syncthreads();
     pscan[tid] += padd;
     rscan[tid] += radd;
-    bscan[tid] += badd;
     __syncthreads();
   }
   const int npaired = pscan[kTileThreads - 1];
-  int pat = pscan[tid] - plocal, rat = npaired + rscan[tid] - rlocal, bat = bscan[tid] - blocal;
+  int pat = pscan[tid] - plocal, rat = npaired + rscan[tid] - rlocal;
   for (int i = i0; i < i1; ++i) {
-    const int h = i / Z, m = i % Z, nu = bunits(i);
-    for (int b = 0; b < 8 / nu; ++b) btiles[bat + b] = make_int2(h, (8 * m + b * nu) | (nu << 16));
-    bat += 8 / nu;
-  }
-  for (int i = i0; i < i1; ++i) {
-    const int h = i / Z, m = i % Z, nu = bunits(i);
-    if (nu == 4) {
+    const int h = i / Z, m = i % Z, lb = lb_of(i);
+    for (int b = 0; b < 2; ++b) btiles[2 * i + b] = make_int2(h, (8 * m + 4 * b) | (lb << 16));
+    if (lb == 2) {
       for (int s = 0; s < 4; ++s) tiles[pat + s] = make_int2(h, 8 * m + 2 * s);
       pat += 4;
-    } else if (nu == 2) {
+    } else if (lb == 1) {
       for (int s = 0; s < 4; ++s) tiles[rat + s] = make_int2(h, 8 * m + 2 * s);
       rat += 4;
     } else {
@@ -627,7 +621,7 @@ __global__ void __launch_bounds__(kTileThreads)
   }
   if (tid == kTileThreads - 1) {
     counters[0] = npaired + rscan[tid];
-    counters[1] = bscan[tid];
+    counters[1] = 2 * n;
     counters[2] = npaired;
   }
 }

@@ -225,17 +225,26 @@ Layout make_layout(const Dims &d) {
   L.sel_bits = take(H * NB * d.words * sizeof(uint32_t));
   L.csc_bits = take(H * NB * d.words * sizeof(uint32_t));
   L.tiles = take(H * U * sizeof(int2));
-  L.btiles = take(H * U * sizeof(int2));
+  L.btiles = take(H * 2 * Z * sizeof(int2));
+  L.qt_count = take(H * 2 * Z * sizeof(int));
+  L.qt_ptr = take(H * (2 * Z + 1) * sizeof(int));
+  L.qt_list = take(H * CAP * sizeof(int));
   L.counters = take(16 * sizeof(int));
   L.delta = take(H * N * sizeof(float));
   L.lsep = take(H * N * sizeof(float));
   L.lse2 = take(H * N * sizeof(float));
-  L.o32p = take(H * N * (size_t)d.Dp * sizeof(float));
+  // the large per-token arrays start on 2 MiB boundaries: their placement relative to the
+  // memory channels then does not depend on the sizes of the arrays before them
+  auto take_big = [&](size_t bytes) {
+    off = (off + ((size_t)1 << 21) - 1) & ~(((size_t)1 << 21) - 1);
+    return take(bytes);
+  };
+  L.o32p = take_big(H * N * (size_t)d.Dp * sizeof(float));
   const size_t tensor = H * N * (size_t)d.Dp * d.elt;
-  L.qp = take(tensor);
-  L.kp = take(tensor);
-  L.vp = take(tensor);
-  L.dop = take(tensor);
+  L.qp = take_big(tensor);
+  L.kp = take_big(tensor);
+  L.vp = take_big(tensor);
+  L.dop = take_big(tensor);
   L.total = off;
   L.pub.total = off;
   L.pub.N = d.N;

@@ -14,7 +14,7 @@ constexpr int kZone = 8;       // macro-zone edge along T, H, W
 constexpr int kZoneTok = 512;  // tokens per zone
 constexpr int kUnit = 64;      // tokens per atomic compute unit of the attention kernels
 constexpr int kMaxUnits = 65535;  // units per head (block indices fit 16 bits)
-constexpr int kTile64 = 1 << 30;  // tile flag: 64 rows (a 64-token block) instead of 128
+constexpr int kTile64 = 1 << 30;  // key tile flag: 64 keys (a 64-token block) instead of 128
 
 // Per-stage tracing: while enabled, records a HIP event pair on the stream around the
 // launches of a stage (prism_api.hip).
@@ -57,9 +57,16 @@ struct Layout {
                             //   bfloat16 inputs, float32 for float32 inputs)
   size_t sel_bits;          // uint32 [heads][nb_max][words]
   size_t csc_bits;          // uint32 [heads][nb_max][words]
-  size_t tiles;             // int2 [heads*U]: (head, first unit | kTile64) per query/key tile
-  size_t btiles;            // int2 [heads*U]: (head, first unit | units << 16) per block
-  size_t counters;          // int32 [16]: [0] = tile count, [1] = block tile count
+  size_t tiles;             // int2 [heads*U]: key tiles, (head, first unit | kTile64)
+  size_t btiles;            // int2 [heads*2Z]: query tiles of 256 rows, (head, first unit |
+                            //   (log2 B - 6) << 16), two per zone
+  size_t counters;          // int32 [16]: [0] = key tiles, [1] = query tiles, [2] = key tiles
+                            //   of 256-token blocks (listed first)
+  // Query tile lists: per query tile, the union of the selection lists of its blocks (one
+  // block of 256, two of 128 or four of 64 tokens).  Entries are j | mask << 16: key block j
+  // and the bit g set when the tile's block g selects it.  Per head: counts, offsets (as the
+  // CSR) and the entries within the pair capacity.
+  size_t qt_count, qt_ptr, qt_list;  // int32 [heads][2Z], [heads][2Z+1], [heads][cap]
   size_t dop;               // bwd: gathered dout, row-major [heads][N][D] (as qp)
   size_t o32p;              // fwd: float [heads][N][D] output in permuted order
   size_t lsep;              // fwd: float [heads][N] lse in permuted order
@@ -324,26 +331,37 @@ __device__ __forceinline__ void workgroup_barrier() {
 }
 
 // The 64-token units of a list of blocks, in list order (a block of B tokens is B/64
-// consecutive units).  The list is read 64 entries at a time, one per lane, and the
-// current block is broadcast from its lane: the walk itself issues no memory operation, so
-// it never waits behind the direct-to-LDS copies in flight (loads complete in order).  The
-// members other than the window are the same in every lane.
+// consecutive units).  With MASKS (the query tiles' lists) entries are j | mask << 16: block
+// j and the mask of the tile's blocks that selected it; without (the transposed lists)
+// entries are plain block indices.  The list is read 64 entries at a time, one per lane, and
+// the current entry is broadcast from its lane: the walk itself issues no memory operation,
+// so it never waits behind the direct-to-LDS copies in flight (loads complete in order).
+// The members other than the window are the same in every lane.
+template <bool MASKS>
 struct BlockUnits {
-  int base, idx, sub, us, nu, n, lane, self;
+  int base, idx, sub, us, nu, n, lane, self, mask;
   bool empty;
-  int win_us, win_nu;  // this lane's entry of the window: first unit and unit count
+  int win_us, win_nu, win_mask;  // this lane's entry of the window
   const int *list, *bstart, *bsize;
   __device__ void fill() {  // lanes past the end repeat the last entry (never used)
-    const int j = empty ? self : list[min(base + lane, n - 1)];
+    int j;
+    if constexpr (MASKS) {
+      const int e = empty ? (self | (0xf << 16)) : list[min(base + lane, n - 1)];
+      j = e & 0xffff;
+      win_mask = (e >> 16) & 0xf;
+    } else {
+      j = empty ? self : list[min(base + lane, n - 1)];
+    }
     win_us = bstart[j] / kUnit;
     win_nu = bsize[j] / kUnit;
   }
   __device__ void load() {
     us = __builtin_amdgcn_readlane(win_us, idx);
     nu = __builtin_amdgcn_readlane(win_nu, idx);
+    if constexpr (MASKS) mask = __builtin_amdgcn_readlane(win_mask, idx);
   }
-  // a list of count blocks; an empty one (a query block whose list a full selection
-  // capacity cut to nothing: its head's outputs are NaN) walks the block self_blk instead
+  // a list of count entries; an empty one (a list a full selection capacity cut to
+  // nothing: its head's outputs are NaN) walks the block self_blk instead
   __device__ void init(const int *l, int count, const int *bs, const int *bz, int lane_id,
                        int self_blk) {
     list = l;
@@ -355,6 +373,7 @@ struct BlockUnits {
     bsize = bz;
     lane = lane_id;
     base = idx = sub = 0;
+    mask = 0xf;
     fill();
     load();
   }

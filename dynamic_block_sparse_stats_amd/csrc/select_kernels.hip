@@ -7,8 +7,11 @@
 // (2) one workgroup per query block finds the selection threshold on the row by bisection
 // over the order-preserving integer image of the float32 logits, with both the count and
 // the softmax mass of the candidate prefix reduced in a fixed order (deterministic), then
-// writes a bitmask row and the ascending column list; (3) the bitmask is transposed with
-// wave ballots and expanded into the ascending per-key-block query lists used by dK/dV.
+// writes a bitmask row and its count; (3) the bitmask is transposed with wave ballots; (4)
+// each bitmask is expanded into ascending lists at row offsets from an on-device scan,
+// within the head's list capacity: the CSR (key blocks per query block), the CSC (query
+// blocks per key block, walked by dK/dV) and the query tiles' union lists (walked by the
+// forward and dQ).
 #include "prism_internal.h"
 
 namespace prism {
@@ -345,10 +348,10 @@ __global__ void __launch_bounds__(256)
 // workgroup; each thread scans a contiguous chunk of rows.
 constexpr int kScanThreads = 1024;
 __global__ void __launch_bounds__(kScanThreads)
-    offsets_kernel(const int *__restrict__ nb_ptr, int *__restrict__ count,
+    offsets_kernel(const int *__restrict__ nb_ptr, int n_fixed, int *__restrict__ count,
                    int *__restrict__ ptr, long long cap, uint32_t *__restrict__ flags, int h) {
   __shared__ long long scan[kScanThreads];
-  const int nb = *nb_ptr, tid = threadIdx.x;
+  const int nb = nb_ptr ? *nb_ptr : n_fixed, tid = threadIdx.x;
   const int chunk = (nb + kScanThreads - 1) / kScanThreads;
   const int i0 = min(nb, tid * chunk), i1 = min(nb, i0 + chunk);
   long long local = 0;
@@ -409,6 +412,83 @@ __global__ void __launch_bounds__(NT)
   }
 }
 
+// ============================================================================ tile lists
+// The union lists of the query tiles (see the tile lists in plan_kernels.hip).  Query tile
+// i of zone m (slot 2m + i) covers the G = 256 / B blocks zone_block[m] + i G .. + G - 1 and
+// takes the union of their selection rows.  Entry: key block j | mask << 16, bit g of mask
+// set when the tile's block g selects j.
+__device__ __forceinline__ void group_of(int slot, const int *zshape, const int *zblock,
+                                         int *first, int *g) {
+  const int m = slot >> 1, s = slot & 1;
+  const int code = zshape[m];
+  const int S = ((code >> 4) & 3) + ((code >> 2) & 3) + (code & 3);
+  *g = 1 << (8 - S);
+  *first = zblock[m] + s * *g;
+}
+
+// Entries per tile: one wave per tile.
+__global__ void __launch_bounds__(256)
+    group_count_kernel(int Z, const int *__restrict__ zshape, const int *__restrict__ zblock,
+                       const uint32_t *__restrict__ bits, int words, int *__restrict__ count) {
+  const int nslots = 2 * Z, lane = threadIdx.x & 63;
+  const int wn = (zblock[Z] + 31) / 32;
+  for (int slot = blockIdx.x * 4 + (threadIdx.x >> 6); slot < nslots; slot += gridDim.x * 4) {
+    int first, g;
+    group_of(slot, zshape, zblock, &first, &g);
+    int c = 0;
+    for (int w = lane; w < wn; w += 64) {
+      uint32_t u = 0;
+      for (int b = 0; b < g; ++b) u |= bits[(size_t)(first + b) * words + w];
+      c += __popc(u);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
+    if (lane == 0) count[slot] = c;
+  }
+}
+
+// The entries at the tile offsets (at most count[slot] of them, count having been cut to the
+// capacity where it overflowed): one workgroup per tile.
+template <int NT, int WPT>
+__global__ void __launch_bounds__(NT)
+    group_expand_kernel(int Z, const int *__restrict__ zshape, const int *__restrict__ zblock,
+                        const uint32_t *__restrict__ bits, int words,
+                        const int *__restrict__ count, const int *__restrict__ ptr,
+                        int *__restrict__ lists) {
+  __shared__ int scanbuf[NT / 64];
+  const int nslots = 2 * Z, tid = threadIdx.x;
+  const int wn = (zblock[Z] + 31) / 32;
+  for (int slot = blockIdx.x; slot < nslots; slot += gridDim.x) {
+    int first, g;
+    group_of(slot, zshape, zblock, &first, &g);
+    int *lrow = lists + ptr[slot];
+    const int keep = count[slot];
+    int run = 0;
+#pragma unroll
+    for (int r = 0; r < WPT; ++r) {
+      const int w = tid + NT * r;
+      uint32_t rw[4] = {0u, 0u, 0u, 0u};
+      uint32_t u = 0;
+      if (w < wn)
+        for (int b = 0; b < g; ++b) {
+          rw[b] = bits[(size_t)(first + b) * words + w];
+          u |= rw[b];
+        }
+      int tot;
+      int pos = run + block_excl_scan<NT>(__popc(u), scanbuf, &tot);
+      run += tot;
+      while (u && pos < keep) {
+        const int e = __ffs(u) - 1;
+        u &= u - 1;
+        int mask = 0;
+        for (int b = 0; b < g; ++b) mask |= (int)((rw[b] >> e) & 1u) << b;
+        lrow[pos++] = (32 * w + e) | (mask << 16);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // ============================================================================ launcher
 hipError_t launch_scores_select(const Dims &d, const prism_config *cfg, float score_scale,
                                 uint8_t *ws, const Layout &L, hipStream_t s) {
@@ -449,9 +529,9 @@ hipError_t launch_scores_select(const Dims &d, const prism_config *cfg, float sc
                        tbits);
     hipLaunchKernelGGL(popc_rows_kernel, dim3(1024), dim3(256), 0, s, d.words, nbp, tbits,
                        tcnt);
-    hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kScanThreads), 0, s, nbp, cnt, cptr, d.cap,
-                       flags, h);
-    hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kScanThreads), 0, s, nbp, tcnt, tptr,
+    hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kScanThreads), 0, s, nbp, 0, cnt, cptr,
+                       d.cap, flags, h);
+    hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kScanThreads), 0, s, nbp, 0, tcnt, tptr,
                        d.cap, flags, h);
     if (small) {
       hipLaunchKernelGGL((expand_kernel<256, 2>), dim3(sel_grid), dim3(256), 0, s, d.words, nbp,
@@ -464,6 +544,23 @@ hipError_t launch_scores_select(const Dims &d, const prism_config *cfg, float sc
       hipLaunchKernelGGL((expand_kernel<1024, 2>), dim3(sel_grid), dim3(1024), 0, s, d.words,
                          nbp, tbits, tcnt, tptr, trows);
     }
+    // the query tiles' union lists, from the same bitmask
+    const int *zsh = (const int *)(ws + L.pub.zone_shape) + (size_t)h * d.Z;
+    const int *zb = zblock + (size_t)h * (d.Z + 1);
+    int *qtc = (int *)(ws + L.qt_count) + (size_t)h * 2 * d.Z;
+    int *qtp = (int *)(ws + L.qt_ptr) + (size_t)h * (2 * d.Z + 1);
+    int *qtl = (int *)(ws + L.qt_list) + (size_t)h * d.cap;
+    const int cgrid = (2 * d.Z + 3) / 4 < 1024 ? (2 * d.Z + 3) / 4 : 1024;
+    hipLaunchKernelGGL(group_count_kernel, dim3(cgrid), dim3(256), 0, s, d.Z, zsh, zb, bits,
+                       d.words, qtc);
+    hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kScanThreads), 0, s, nullptr, 2 * d.Z,
+                       qtc, qtp, d.cap, flags, h);
+    if (small)
+      hipLaunchKernelGGL((group_expand_kernel<256, 2>), dim3(sel_grid), dim3(256), 0, s, d.Z,
+                         zsh, zb, bits, d.words, qtc, qtp, qtl);
+    else
+      hipLaunchKernelGGL((group_expand_kernel<1024, 2>), dim3(sel_grid), dim3(1024), 0, s, d.Z,
+                         zsh, zb, bits, d.words, qtc, qtp, qtl);
   }
   return hipGetLastError();
 }

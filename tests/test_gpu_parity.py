@@ -150,22 +150,32 @@ def test_bf16_small_backward(T, H, W, bg, seed, need256):
 
 
 def _unit_list_lengths(views, h):
-    """Per query block, the units of its selected key blocks; per key block selected by at
-    least one query block, the units of those query blocks; and the key blocks nobody
+    """The unit counts the attention kernels walk: per query tile (256 rows: one block of
+    256, two of 128 or four of 64 tokens; the forward and dQ walk the union of the tile's
+    blocks' selections), the units of the union; per key block selected by at least one
+    query block, the units of those query blocks (dK/dV); and the key blocks nobody
     selected."""
     nb = int(views["zone_block"][h, -1])  # the head's block count
     bsz = views["block_size"][h, :nb].cpu().numpy() // 64
+    zb = views["zone_block"][h].cpu().numpy()
     col = P.csr_rows(views, h, "csr")
     crow = P.csr_rows(views, h, "csc")
-    q_units = [int(bsz[c].sum()) for c in col]
+    q_units = []
+    for m in range(len(zb) - 1):
+        g = 4 // int(bsz[zb[m]])     # blocks per query tile
+        for i in range(2):
+            first = zb[m] + i * g
+            union = set().union(*(col[first + b].tolist() for b in range(g)))
+            q_units.append(int(bsz[sorted(union)].sum()))
     k_units = [int(bsz[r].sum()) for r in crow if len(r) > 0]
     return q_units, k_units, sum(len(r) == 0 for r in crow)
 
 
 def test_bf16_short_lists():
     """Pure Top-k with k = 1, 2, 3 (Top-p off): selection lists of a few units, so the
-    unrolled unit loops of the three attention kernels end at every stage position, and
-    key blocks that no query block selected get zero dK and dV."""
+    unrolled unit loops of the three attention kernels end at every stage position (the
+    forward and dQ walk the query tiles' union lists), and key blocks that no query block
+    selected get zero dK and dV."""
     fwd_res, kv_res, unselected = set(), set(), 0
     for k in (1, 2, 3):
         wl = synth.custom(8, 16, 24, 2, 128, "bf16", top_k=k, top_p=0.0, bg_amp=1.0, seed=5)
@@ -181,7 +191,7 @@ def test_bf16_short_lists():
             fwd_res |= {u % 4 for u in q_units}
             kv_res |= {u % 3 for u in k_units}
             unselected += unsel
-            print(f"k={k} head {h}: query lists {sorted(set(q_units))} units, key lists "
+            print(f"k={k} head {h}: query tile lists {sorted(set(q_units))} units, key lists "
                   f"{sorted(set(k_units))} units, unselected key blocks {unsel}", flush=True)
             op, exact = _check_head(wl, cfg, att, inp_cpu, h, o, lse)
             if not exact.all():
