@@ -351,10 +351,13 @@ def test_call_order_is_enforced():
         assert torch.equal(a, b)
 
 
-def test_bf16_head_dim_64():
+@pytest.mark.parametrize("T,H,W,bg", [(8, 16, 24, 1.0), (16, 32, 32, 0.15)],
+                         ids=["mixed-blocks", "near-uniform"])
+def test_bf16_head_dim_64(T, H, W, bg):
     """bfloat16 with head_dim 64: the permuted float16 operands are zero-padded to 128
-    channels; plan, forward and backward against the oracle."""
-    wl = synth.custom(8, 16, 24, 2, 64, "bf16", top_k=4, top_p=0.8, seed=5)
+    channels; plan, forward and backward against the oracle (small blocks of a varied
+    field, and the 256-token blocks of a near-uniform one)."""
+    wl = synth.custom(T, H, W, 2, 64, "bf16", top_k=4, top_p=0.8, bg_amp=bg, seed=5)
     inp_cpu, inp = _inputs(wl, with_dout=True)
     cfg = P.config_for(wl)
     att = run_plan(cfg, inp)
