@@ -38,9 +38,9 @@ KERNEL_SOURCES = {"attn_fwd": "attn_fwd.hip", "bwd_dkdv": "attn_bwd_dkdv.hip",
                   "bwd_dq": "attn_bwd.hip"}
 TRAFFIC_SOURCE = "profiles/attention_2k_train_pmc_traffic.md"
 MEASURED_TRAFFIC = {
-    ("attn_fwd", "2k-train-64x104x128"): ("192c0ff358424f69", 30.777e12),
-    ("bwd_dkdv", "2k-train-64x104x128"): ("20352c6fcd989e62", 49.600e12),
-    ("bwd_dq", "2k-train-64x104x128"): ("4b95a96e12497379", 30.768e12),
+    ("attn_fwd", "2k-train-64x104x128"): ("0ddb8f39722364af", 30.825e12),
+    ("bwd_dkdv", "2k-train-64x104x128"): ("1a0ceb2f3222c720", 48.587e12),
+    ("bwd_dq", "2k-train-64x104x128"): ("75457d8b12b584a7", 30.844e12),
 }
 
 
