@@ -15,9 +15,10 @@ constexpr int kDB = 128;
 
 // ============================================================================ dK / dV (bf16)
 // One workgroup of eight waves (two per SIMD) per 128-key tile (a 256-key block is two
-// tiles), in four pairs; pair w owns keys 32w .. 32w + 31 of the tile (a 64-key block
-// leaves pairs 2-3 idle in the arithmetic; they still help stage the units).  Over the
-// 64-token query units of every query block that selected the key block:
+// tiles), in four pairs; pair w owns keys 32w .. 32w + 31 of the tile.  (The 64-key tiles of
+// 64-token blocks run in a second launch in which pair w owns keys 32 (w % 2) .. + 31 and
+// one half of each unit's query rows, below.)  Over the 64-token query units of every query
+// block that selected the key block:
 //   * the P wave (w < 4) holds K as B operand, forms S = Q K^T and P = exp(S - lse),
 //     hands P to its partner through LDS (float32) and accumulates dV^T += dO^T P;
 //   * the dS wave (w >= 4) holds V as B operand, forms dP = dO V^T and accumulates
@@ -225,10 +226,123 @@ __device__ __forceinline__ void d_ds(DState &w, int pair, int lane) {
     for (int g = 0; g < 2; ++g) w.db[a][g] = db[a][g];
 }
 
+// ---- 64-key tiles (a launch of their own): the four pairs split the tile into 32 keys x
+// one half of each unit's queries.  Pair p owns keys 32 (p % 2) .. + 31 and query half
+// a = p / 2 (rows 32a .. 32a + 31 of every unit), so every wave has work; the two pairs of a
+// key half add their accumulators at the end of the tile.  A wave keeps one half's values in
+// the [0] entries of its state.
+
+// acc (C layout, lane = key l32) += the 32 query rows of the row-major float16 tile at LDS
+// address t (the half's first row) times the wave's B operand; the next group's operands
+// are read while one runs
+__device__ __forceinline__ void half_product(f32x16 &acc, uint32_t t, const f16x8 (&b)[8],
+                                             int l32, int hh) {
+  const uint32_t r = row_base(t, l32) ^ (uint32_t)(hh << 4);
+  f16x8 x[2][2];  // [buffer][e]
+  auto load = [&](int buf, int grp) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) x[buf][e] = lds_row16(r ^ (uint32_t)((2 * grp + e) << 5));
+  };
+  load(0, 0);
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) {
+    if (grp < 3) load((grp + 1) & 1, grp + 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) acc = mfma_f16(x[grp & 1][e], b[2 * grp + e], acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+// acc[dt] += T^T[d][k] X[k][j] over the 32 rows k of one half (two 16-row slices) of the
+// tile whose transposed-read base is tb (taken at the half's first row); first holds the
+// first slice's operands
+__device__ __forceinline__ void half_tr_update(f32x16 (&acc)[4], const TrBase &tb,
+                                               const f16x8 (&x)[2], const f16x8 (&first)[4]) {
+  f16x8 second[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) second[dt] = tr_read(tb, 16, 32 * dt);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma_f16(first[dt], x[0], acc[dt]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma_f16(second[dt], x[1], acc[dt]);
+}
+// P wave of a 64-key tile, before the barrier: S and P for half a, published
+__device__ __forceinline__ void ps_first(PState &w, uint32_t st, int pair, int a, int lane,
+                                         float scale_log2e) {
+  const int l32 = lane & 31, hh = lane >> 5;
+  f32x4 lv[4];
+#pragma unroll
+  for (int v4 = 0; v4 < 4; ++v4)
+    lv[v4] = lds_f32x4(st + kVecs + 4u * (32 * a + 8 * v4 + 4 * hh));
+  f32x16 sacc = f32x16{};
+  half_product(sacc, st + 8192u * (uint32_t)a, w.breg, l32, hh);
+  f16x8 x[2];
+#pragma unroll
+  for (int v4 = 0; v4 < 4; ++v4) {
+    f32x4 p4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = 4 * v4 + e;
+      p4[e] = __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2e, -lv[v4][e]));
+      x[v >> 3][v & 7] = (_Float16)(p4[e] * kPScale);
+    }
+    g_pex[pair][a][v4][lane] = p4;
+  }
+  w.x[0][0] = x[0];
+  w.x[0][1] = x[1];
+}
+// P wave of a 64-key tile, after the barrier: dV^T += dO^T (P * 2^10) over half a
+__device__ __forceinline__ void ps_second(PState &w, uint32_t st, int a, int lane) {
+  const TrBase tb = tr_base(st + kDOTile + 8192u * (uint32_t)a, lane);
+  f16x8 first[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) first[dt] = tr_read(tb, 0, 32 * dt);
+  half_tr_update(w.acc, tb, w.x[0], first);
+}
+// dS wave of a 64-key tile: dP for half a, started at -delta
+__device__ __forceinline__ void ds_dp(DState &w, uint32_t st, int a, int lane) {
+  const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int v4 = 0; v4 < 4; ++v4) {
+    const f32x4 d4 = lds_f32x4(st + kVecs + 4u * (kUnit + 32 * a + 8 * v4 + 4 * hh));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w.dp[0][4 * v4 + e] = d4[e];
+  }
+  half_product(w.dp[0], st + kDOTile + 8192u * (uint32_t)a, w.breg, l32, hh);
+}
+// dS wave of a 64-key tile: the transposed-read base of half a of the Q tile at st and the
+// first slice's operands of the dK product (read before dP)
+__device__ __forceinline__ TrBase ds_dk_first(uint32_t st, int a, int lane,
+                                              f16x8 (&first)[4]) {
+  const TrBase tb = tr_base(st + 8192u * (uint32_t)a, lane);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) first[dt] = tr_read(tb, 0, 32 * dt);
+  return tb;
+}
+// dS wave of a 64-key tile, after the barrier: dS = P (dP - delta) for half a
+__device__ __forceinline__ void ds_ds(DState &w, int pair, int a, int lane) {
+  f32x4 pv[4];
+#pragma unroll
+  for (int v4 = 0; v4 < 4; ++v4) pv[v4] = g_pex[pair][a][v4][lane];
+  __builtin_amdgcn_sched_barrier(0);
+  f16x8 db[2];
+#pragma unroll
+  for (int v4 = 0; v4 < 4; ++v4)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = 4 * v4 + e;
+      db[v >> 3][v & 7] = (_Float16)(pv[v4][e] * w.dp[0][v]);
+    }
+  w.db[0][0] = db[0];
+  w.db[0][1] = db[1];
+}
+
 // P published: the P waves' LDS writes are complete before the barrier
 __device__ __forceinline__ void publish_sync() { wait_and_barrier<kLgkm0>(); }
 
-template <bool PW>
+template <bool PW, bool SPLIT>
 __device__ __forceinline__ void dkdv_waves(
     int wave, int lane, int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
     const int *__restrict__ tile_count, int ntiles, const uint16_t *__restrict__ qp,
@@ -253,23 +367,31 @@ __device__ __forceinline__ void dkdv_waves(
   // the two halves of a 256-token key block (tiles 2p and 2p + 1 of the first npaired) go
   // to slots j and j + 8 of a group of 16, i.e. to workgroups b and b + 8, which sit on the
   // same XCD (workgroups are dealt to the eight XCDs in turn)
-  const int npaired = __builtin_amdgcn_readfirstlane(tile_count[2]) & ~15;
+  // (the 64-key tiles follow the others in the list)
+  const int npaired = SPLIT ? 0 : __builtin_amdgcn_readfirstlane(tile_count[2]) & ~15;
+  const int tbase = SPLIT ? __builtin_amdgcn_readfirstlane(tile_count[0]) : 0;
   for (int slot = blockIdx.x; slot < ntiles; slot += gridDim.x) {
-    const int j = slot & 15;
-    const int t = slot < npaired ? (slot & ~15) + 2 * (j & 7) + (j >> 3) : slot;
+    int t;
+    if constexpr (SPLIT) {
+      t = tbase + slot;
+    } else {
+      const int j = slot & 15;
+      t = slot < npaired ? (slot & ~15) + 2 * (j & 7) + (j >> 3) : slot;
+    }
     const int2 tl = tiles[t];
     const int h = __builtin_amdgcn_readfirstlane(tl.x);
     const int ty = __builtin_amdgcn_readfirstlane(tl.y);
     // 128-key tiles (two per 256-key block), 64-key tiles for 64-key blocks
     const int u0 = ty & (kTile64 - 1), rows = (ty & kTile64) ? kUnit : 2 * kUnit;
-    const bool active = pair * 32 < rows;
+    const bool active = SPLIT || pair * 32 < rows;
+    const int half = SPLIT ? pair >> 1 : 0;  // 64-key tiles: this pair's query half
     const int jblk = unit_blk[(size_t)h * U + u0];
     const int nq = __builtin_amdgcn_readfirstlane(csc_count[(size_t)h * nb_max + jblk]);
     const int *qlist = csc_row + (size_t)h * cap + csc_ptr[(size_t)h * (nb_max + 1) + jblk];
     const int *bs = blk_start + (size_t)h * nb_max, *bz = blk_size + (size_t)h * nb_max;
     // the pair's 32 keys: K^T (P wave) or V^T (dS wave) as B operand (lane = key, 8 dims
     // per k-step)
-    const int key0 = u0 * kUnit + pair * 32;
+    const int key0 = u0 * kUnit + (SPLIT ? pair & 1 : pair) * 32;
     std::conditional_t<PW, PState, DState> w;
     if (active) {
       const uint16_t *br = (PW ? kp : vp) + ((size_t)h * N + key0 + l32) * kDB + 8 * hh;
@@ -320,7 +442,25 @@ __device__ __forceinline__ void dkdv_waves(
       wait_one_behind();
       const bool unit_u = u < issued;
       const uint32_t st = stage_addr<S>();
-      if constexpr (PW) {
+      if constexpr (PW && SPLIT) {
+        if (!unit_u) return false;
+        ps_first(w, st, pair, half, lane, scale_log2e);
+        publish_sync();
+        issue(stage<(S + 2) % kStages>());
+        ps_second(w, st, half, lane);
+      } else if constexpr (SPLIT) {
+        {
+          const uint32_t prev = stage_addr<(S + kStages - 1) % kStages>();
+          f16x8 first[4];
+          const TrBase tb = ds_dk_first(u == 0 ? st : prev, half, lane, first);
+          ds_dp(w, st, half, lane);
+          half_tr_update(w.acc, tb, w.db[0], first);
+        }
+        if (!unit_u) return false;
+        publish_sync();
+        issue(stage<(S + 2) % kStages>());
+        ds_ds(w, pair, half, lane);
+      } else if constexpr (PW) {
         if (!unit_u) return false;
         if (active) p_first(w, st, pair, lane, scale_log2e);
         publish_sync();
@@ -355,6 +495,33 @@ __device__ __forceinline__ void dkdv_waves(
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the trailing repeat copies
     }
+    if constexpr (SPLIT) {
+      // the pairs of query half 1 hand their accumulators to those of half 0 (same keys)
+      // through the stage tiles, which no wave reads or fills any more (every wave's copies
+      // have landed before the first barrier)
+      workgroup_barrier();
+      const int region = (wave & 1) + (PW ? 0 : 2);
+      f32x4 *red = reinterpret_cast<f32x4 *>(region < 2 ? g_stage0.tile[region & 1]
+                                                        : g_stage1.tile[region & 1]);
+      if (half) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4)
+            red[(dt * 4 + v4) * 64 + lane] = f32x4{w.acc[dt][4 * v4], w.acc[dt][4 * v4 + 1],
+                                                   w.acc[dt][4 * v4 + 2], w.acc[dt][4 * v4 + 3]};
+      }
+      wait_and_barrier<kLgkm0>();
+      if (half) continue;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const f32x4 o = red[(dt * 4 + v4) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w.acc[dt][4 * v4 + e] += o[e];
+        }
+    }
     // epilogue: C layout lane = key l32, register v -> d = 32dt + (v/4)*8 + 4hh + v%4; the
     // P wave writes dV (P carried 2^10), the dS wave dK (times the softmax scale)
     if (!active) continue;
@@ -379,31 +546,59 @@ __device__ __forceinline__ void dkdv_waves(
   }
 }
 
-__global__ void __launch_bounds__(NW * 64)
-    attn_dkdv_bf16_kernel(int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
-                          const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
-                          const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
-                          const uint16_t *__restrict__ dop, const float *__restrict__ lse2,
-                          const float *__restrict__ ndelta, const int *__restrict__ unit_blk,
-                          const int *__restrict__ blk_start, const int *__restrict__ blk_size,
-                          const int *__restrict__ csc_count, const int *__restrict__ csc_ptr,
-                          const int *__restrict__ csc_row, long long cap,
-                          const int *__restrict__ perm, float scale, float scale_log2e, int dio,
-                          const uint32_t *__restrict__ flags, uint16_t *__restrict__ dk,
-                          uint16_t *__restrict__ dv) {
+// The kernel of the 128-key tiles (SPLIT false) and that of the 64-key tiles (SPLIT true);
+// the two roles run the same sequence of barriers and copies
+template <bool SPLIT>
+__device__ __forceinline__ void dkdv_body(
+    int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,
+    const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,
+    const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,
+    const uint16_t *__restrict__ dop, const float *__restrict__ lse2,
+    const float *__restrict__ ndelta, const int *__restrict__ unit_blk,
+    const int *__restrict__ blk_start, const int *__restrict__ blk_size,
+    const int *__restrict__ csc_count, const int *__restrict__ csc_ptr,
+    const int *__restrict__ csc_row, long long cap, const int *__restrict__ perm, float scale,
+    float scale_log2e, int dio, const uint32_t *__restrict__ flags, uint16_t *__restrict__ dk,
+    uint16_t *__restrict__ dv) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int ntiles = *tile_count;
-  // the two roles run the same sequence of barriers and copies
+  const int ntiles = SPLIT ? tile_count[3] : *tile_count;
   if (wave < 4)
-    dkdv_waves<true>(wave, lane, N, U, nb_max, heads, tiles, tile_count, ntiles, qp, kp, vp,
-                     dop, lse2, ndelta, unit_blk, blk_start, blk_size, csc_count, csc_ptr,
-                     csc_row, cap, perm, scale, scale_log2e, dio, flags, dk, dv);
+    dkdv_waves<true, SPLIT>(wave, lane, N, U, nb_max, heads, tiles, tile_count, ntiles, qp,
+                            kp, vp, dop, lse2, ndelta, unit_blk, blk_start, blk_size,
+                            csc_count, csc_ptr, csc_row, cap, perm, scale, scale_log2e, dio,
+                            flags, dk, dv);
   else
-    dkdv_waves<false>(wave, lane, N, U, nb_max, heads, tiles, tile_count, ntiles, qp, kp, vp,
-                      dop, lse2, ndelta, unit_blk, blk_start, blk_size, csc_count, csc_ptr,
-                      csc_row, cap, perm, scale, scale_log2e, dio, flags, dk, dv);
+    dkdv_waves<false, SPLIT>(wave, lane, N, U, nb_max, heads, tiles, tile_count, ntiles, qp,
+                             kp, vp, dop, lse2, ndelta, unit_blk, blk_start, blk_size,
+                             csc_count, csc_ptr, csc_row, cap, perm, scale, scale_log2e, dio,
+                             flags, dk, dv);
 }
 
+#define PRISM_DKDV_PARAMS                                                                    \
+  int N, int U, int nb_max, int heads, const int2 *__restrict__ tiles,                       \
+      const int *__restrict__ tile_count, const uint16_t *__restrict__ qp,                   \
+      const uint16_t *__restrict__ kp, const uint16_t *__restrict__ vp,                      \
+      const uint16_t *__restrict__ dop, const float *__restrict__ lse2,                      \
+      const float *__restrict__ ndelta, const int *__restrict__ unit_blk,                    \
+      const int *__restrict__ blk_start, const int *__restrict__ blk_size,                   \
+      const int *__restrict__ csc_count, const int *__restrict__ csc_ptr,                    \
+      const int *__restrict__ csc_row, long long cap, const int *__restrict__ perm,          \
+      float scale, float scale_log2e, int dio, const uint32_t *__restrict__ flags,           \
+      uint16_t *__restrict__ dk, uint16_t *__restrict__ dv
+#define PRISM_DKDV_ARGS                                                                      \
+  N, U, nb_max, heads, tiles, tile_count, qp, kp, vp, dop, lse2, ndelta, unit_blk,           \
+      blk_start, blk_size, csc_count, csc_ptr, csc_row, cap, perm, scale, scale_log2e, dio,  \
+      flags, dk, dv
+
+__global__ void __launch_bounds__(NW * 64) attn_dkdv_bf16_kernel(PRISM_DKDV_PARAMS) {
+  dkdv_body<false>(PRISM_DKDV_ARGS);
+}
+__global__ void __launch_bounds__(NW * 64) attn_dkdv64_bf16_kernel(PRISM_DKDV_PARAMS) {
+  dkdv_body<true>(PRISM_DKDV_ARGS);
+}
+
+// The 128-key tiles, then the 64-key tiles (each launch persistent over its part of the
+// list; the second exits at once when there are none)
 hipError_t launch_dkdv_bf16(int work_items, hipStream_t s, int N, int U, int nb_max, int heads,
                             const int2 *tiles, const int *counters, const uint16_t *qp,
                             const uint16_t *kp, const uint16_t *vp, const uint16_t *dop,
@@ -416,7 +611,14 @@ hipError_t launch_dkdv_bf16(int work_items, hipStream_t s, int N, int U, int nb_
   hipLaunchKernelGGL(attn_dkdv_bf16_kernel, dim3(grid), dim3(NW * 64), 0, s, N, U, nb_max,
                      heads, tiles, counters, qp, kp, vp, dop, lse2, ndelta, unit_blk, bstart,
                      bsize, tcnt, tptr, trows, cap, perm, scale, sl2e, dio, flags, dk, dv);
+  const int grid64 = resident_grid((const void *)attn_dkdv64_bf16_kernel, NW * 64, work_items);
+  hipLaunchKernelGGL(attn_dkdv64_bf16_kernel, dim3(grid64), dim3(NW * 64), 0, s, N, U, nb_max,
+                     heads, tiles, counters, qp, kp, vp, dop, lse2, ndelta, unit_blk, bstart,
+                     bsize, tcnt, tptr, trows, cap, perm, scale, sl2e, dio, flags, dk, dv);
   return hipGetLastError();
 }
+
+#undef PRISM_DKDV_PARAMS
+#undef PRISM_DKDV_ARGS
 
 }  // namespace prism

@@ -567,15 +567,17 @@ hipError_t launch_gather(const Dims &d, const void *q, const void *k, const void
 // (head, zone, position) order: the persistent kernels take tiles t, t + grid, ..., so the
 // workgroups resident at any moment work on tiles of one head.  Key tiles put the zones of
 // 256-token blocks first (the two halves of a block at positions 2p and 2p + 1), then the
-// zones of smaller blocks, whose shorter tiles even out the end of the walk; counters[2]
-// holds the number of tiles of the first part.  The dK/dV kernel gives the two halves of a
-// block (same query units, same cost) to two workgroups of one XCD.
+// zones of 128-token blocks, whose shorter tiles even out the end of the walk, then the
+// 64-key tiles of 64-token blocks, which dK/dV runs as a launch of its own; counters[0] holds
+// the number of tiles before those, counters[2] that of the first part and counters[3] the
+// number of 64-key tiles.  The dK/dV kernel gives the two halves of a block (same query
+// units, same cost) to two workgroups of one XCD.
 constexpr int kTileThreads = 1024;
 
 __global__ void __launch_bounds__(kTileThreads)
     tiles_kernel(int heads, int Z, const int *__restrict__ zshape, int2 *tiles, int2 *btiles,
                  int *counters) {
-  __shared__ int pscan[kTileThreads], rscan[kTileThreads];
+  __shared__ int pscan[kTileThreads], rscan[kTileThreads], sscan[kTileThreads];
   const int tid = threadIdx.x, n = heads * Z;
   const int chunk = (n + kTileThreads - 1) / kTileThreads;
   const int i0 = min(n, tid * chunk), i1 = min(n, i0 + chunk);
@@ -584,27 +586,34 @@ __global__ void __launch_bounds__(kTileThreads)
     const int code = zshape[idx];
     return ((code >> 4) & 3) + ((code >> 2) & 3) + (code & 3) - 6;
   };
-  int plocal = 0, rlocal = 0;
+  int plocal = 0, rlocal = 0, slocal = 0;
   for (int i = i0; i < i1; ++i) {
     const int lb = lb_of(i);
     if (lb == 2)
       plocal += 4;
+    else if (lb == 1)
+      rlocal += 4;
     else
-      rlocal += lb == 1 ? 4 : 8;
+      slocal += 8;
   }
   pscan[tid] = plocal;
   rscan[tid] = rlocal;
+  sscan[tid] = slocal;
   __syncthreads();
   for (int off = 1; off < kTileThreads; off <<= 1) {
     const int padd = tid >= off ? pscan[tid - off] : 0;
     const int radd = tid >= off ? rscan[tid - off] : 0;
+    const int sadd = tid >= off ? sscan[tid - off] : 0;
     __syncthreads();
     pscan[tid] += padd;
     rscan[tid] += radd;
+    sscan[tid] += sadd;
     __syncthreads();
   }
   const int npaired = pscan[kTileThreads - 1];
-  int pat = pscan[tid] - plocal, rat = npaired + rscan[tid] - rlocal;
+  const int nmain = npaired + rscan[kTileThreads - 1];
+  int pat = pscan[tid] - plocal, rat = npaired + rscan[tid] - rlocal,
+      sat = nmain + sscan[tid] - slocal;
   for (int i = i0; i < i1; ++i) {
     const int h = i / Z, m = i % Z, lb = lb_of(i);
     for (int b = 0; b < 2; ++b) btiles[2 * i + b] = make_int2(h, (8 * m + 4 * b) | (lb << 16));
@@ -615,14 +624,15 @@ __global__ void __launch_bounds__(kTileThreads)
       for (int s = 0; s < 4; ++s) tiles[rat + s] = make_int2(h, 8 * m + 2 * s);
       rat += 4;
     } else {
-      for (int s = 0; s < 8; ++s) tiles[rat + s] = make_int2(h, (8 * m + s) | kTile64);
-      rat += 8;
+      for (int s = 0; s < 8; ++s) tiles[sat + s] = make_int2(h, (8 * m + s) | kTile64);
+      sat += 8;
     }
   }
   if (tid == kTileThreads - 1) {
-    counters[0] = npaired + rscan[tid];
+    counters[0] = nmain;
     counters[1] = 2 * n;
     counters[2] = npaired;
+    counters[3] = sscan[tid];
   }
 }
 

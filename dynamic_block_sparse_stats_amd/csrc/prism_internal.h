@@ -60,8 +60,9 @@ struct Layout {
   size_t tiles;             // int2 [heads*U]: key tiles, (head, first unit | kTile64)
   size_t btiles;            // int2 [heads*2Z]: query tiles of 256 rows, (head, first unit |
                             //   (log2 B - 6) << 16), two per zone
-  size_t counters;          // int32 [16]: [0] = key tiles, [1] = query tiles, [2] = key tiles
-                            //   of 256-token blocks (listed first)
+  size_t counters;          // int32 [16]: [0] = key tiles of 128 keys, [1] = query tiles,
+                            //   [2] = key tiles of 256-token blocks (listed first), [3] =
+                            //   64-key tiles (listed last, from [0] on)
   // Query tile lists: per query tile, the union of the selection lists of its blocks (one
   // block of 256, two of 128 or four of 64 tokens).  Entries are j | mask << 16: key block j
   // and the bit g set when the tile's block g selects it.  Per head: counts, offsets (as the
