@@ -373,7 +373,11 @@ __device__ __forceinline__ void dkdv_waves(
   for (int slot = blockIdx.x; slot < ntiles; slot += gridDim.x) {
     int t;
     if constexpr (SPLIT) {
-      t = tbase + slot;
+      // the eight tiles of a zone (neighbouring key blocks, similar query lists) go to
+      // workgroups of one XCD: in each full group of 64, tile 8z + s to slot 8s + z
+      const int within = slot & 63;
+      t = tbase + (slot < (ntiles & ~63) ? (slot & ~63) + 8 * (within & 7) + (within >> 3)
+                                          : slot);
     } else {
       const int j = slot & 15;
       t = slot < npaired ? (slot & ~15) + 2 * (j & 7) + (j >> 3) : slot;
