@@ -269,9 +269,10 @@ def test_bf16_settings(name, over):
 @pytest.mark.parametrize("shape", [(4, 4, 4), (4, 4, 8), (4, 8, 8)],
                          ids=["64", "128", "256"])
 def test_bf16_fixed_shape_backward(shape):
-    """Every zone cut into one block shape: 64-token blocks (64-key dK/dV tiles with half the
-    wave pairs idle, 64-row forward/dQ tiles), 128-token blocks (one key tile per block),
-    256-token blocks (two key tiles per block, placed on one XCD)."""
+    """Every zone cut into one block shape: 64-token blocks (the 64-key dK/dV launch, where
+    the wave pairs split keys and query halves: 96 tiles, one full group of 64 placed by zone
+    on the XCDs and a tail of 32; forward/dQ query tiles of four blocks), 128-token blocks
+    (one key tile per block), 256-token blocks (two key tiles per block, placed on one XCD)."""
     wl = synth.custom(8, 16, 24, 2, 128, "bf16", top_k=3, top_p=0.5, seed=5)
     over = dict(fixed_shape=P.shape_code(*shape))
     inp_cpu, inp = _inputs(wl, with_dout=True)
