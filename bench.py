@@ -30,17 +30,18 @@ T_START = time.perf_counter()  # the run's wall-clock budget counts from here
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
-# HBM bytes per launch of the attention kernels on the 2K training workload, from two
-# rocprofv3 counter passes over one step (FETCH_SIZE x 2 x 1024 + WRITE_SIZE x 1024 bytes;
-# the scales come from a 1 GiB device copy measured in the same runs), together with the
-# hash of the kernel sources they were taken with: a kernel changed since reports null.
+# HBM bytes per stage of the attention kernels on the 2K training workload (dK/dV: its two
+# launches, 128-key and 64-key tiles, together), from two rocprofv3 counter passes over one
+# step (FETCH_SIZE x 2 x 1024 + WRITE_SIZE x 1024 bytes; the scales come from a 1 GiB device
+# copy measured in the same runs), together with the hash of the kernel sources they were
+# taken with: a kernel changed since reports null.
 KERNEL_SOURCES = {"attn_fwd": "attn_fwd.hip", "bwd_dkdv": "attn_bwd_dkdv.hip",
                   "bwd_dq": "attn_bwd.hip"}
 TRAFFIC_SOURCE = "profiles/attention_2k_train_pmc_traffic.md"
 MEASURED_TRAFFIC = {
-    ("attn_fwd", "2k-train-64x104x128"): ("0ddb8f39722364af", 30.825e12),
-    ("bwd_dkdv", "2k-train-64x104x128"): ("1a0ceb2f3222c720", 48.587e12),
-    ("bwd_dq", "2k-train-64x104x128"): ("75457d8b12b584a7", 30.844e12),
+    ("attn_fwd", "2k-train-64x104x128"): ("0ddb8f39722364af", 30.828e12),
+    ("bwd_dkdv", "2k-train-64x104x128"): ("b5746f3c63fc0e76", 45.658e12),
+    ("bwd_dq", "2k-train-64x104x128"): ("75457d8b12b584a7", 30.842e12),
 }
 
 
