@@ -76,8 +76,16 @@ std::mutex g_ws_mu;
 std::unordered_map<uintptr_t, WsState> g_ws;
 unsigned long long g_gen = 0;
 
+// Field by field: the struct has padding (before eps) whose bytes a caller need not set.
+// Floating fields compare by value (check_config has refused non-finite ones).
 bool same_config(const prism_config &a, const prism_config &b) {
-  return memcmp(&a, &b, sizeof(prism_config)) == 0;
+  return a.T == b.T && a.H == b.H && a.W == b.W && a.num_heads == b.num_heads &&
+         a.head_dim == b.head_dim && a.dtype == b.dtype && a.min_edge_log2 == b.min_edge_log2 &&
+         a.top_k == b.top_k && a.top_p == b.top_p && a.tau128 == b.tau128 &&
+         a.tau256 == b.tau256 && a.eps == b.eps && a.score_scale == b.score_scale &&
+         a.softmax_scale == b.softmax_scale && a.top_k_frac == b.top_k_frac &&
+         a.fixed_shape == b.fixed_shape && a.map_exponent == b.map_exponent &&
+         a.density_mode == b.density_mode && a.max_pairs == b.max_pairs;
 }
 }  // namespace
 
@@ -332,6 +340,12 @@ prism_status prism_plan(const prism_config *cfg, const void *q, const void *k, c
   if (workspace_bytes < L.total) return fail(PRISM_ERR_WORKSPACE, "workspace too small");
   hipStream_t s = (hipStream_t)stream;
   uint8_t *ws = (uint8_t *)workspace;
+  {
+    // the launches below overwrite the previous plan: until they have all been issued the
+    // workspace holds no valid plan (a failed launch leaves it without one)
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    g_ws.erase((uintptr_t)workspace);
+  }
   Scales sc = scales_of(cfg, d);
   double *zstat = (double *)(ws + L.pub.zone_stats);
   double *astat = (double *)(ws + L.pub.audio_stats);

@@ -64,7 +64,7 @@ typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
 typedef struct prism_config {
     int T, H, W;          /* video latent grid; each a positive multiple of 8 (zone edge) */
     int num_heads;        /* heads handled by one call, each with its own plan */
-    int head_dim;         /* D: 64 or 128 (float32), 128 (bfloat16) */
+    int head_dim;         /* D: 64 or 128, both dtypes */
     int dtype;            /* prism_dtype of every token tensor */
     int min_edge_log2;    /* 1: edges {2,4,8}, 16 candidate shapes (the pages' pool);
                              0: edges {1,2,4,8}, 19 shapes */
@@ -78,8 +78,8 @@ typedef struct prism_config {
     /* Operating-point and ablation settings (digest, selection section and the sparsity,
      * shape, density and mapping ablations).  All-zero values keep the method as above. */
     float top_k_frac;     /* > 0: Top-k = ceil(top_k_frac * Nb) key blocks for each head
-                             (Nb = that head's block count), replacing top_k; the pages'
-                             "Top-k at 95% sparsity" is 0.05.  Range [0, 1] */
+                             (Nb = that head's block count), replacing top_k; Top-k at the
+                             pages' 95% sparsity is 0.05.  Range [0, 1] */
     int fixed_shape;      /* > 0: every zone takes this packed shape (lT*16 + lH*4 + lW;
                              each log2 edge in [min_edge_log2, 3], volume 64, 128 or 256)
                              instead of the adaptive one: the fixed-shape baseline */

@@ -329,7 +329,8 @@ def test_bf16_strided_inputs_match_dense(layout):
 def test_call_order_is_enforced():
     """A re-plan invalidates the forward state: a backward after it, with no forward, is
     refused (by the binding and by the C ABI itself), as is a forward whose configuration
-    differs from the plan's; after a forward the backward runs again."""
+    differs from the plan's (the padding bytes of the struct do not count); after a forward
+    the backward runs again and gives the same gradients."""
     wl = synth.custom(8, 16, 24, 2, 128, "bf16", top_k=4, top_p=0.8, seed=5)
     _, inp = _inputs(wl, with_dout=True)
     cfg = P.config_for(wl)
@@ -345,10 +346,17 @@ def test_call_order_is_enforced():
     other = P.config_for(wl, top_k=2)
     with pytest.raises(P.PrismError, match="out of order"):
         P.attn_fwd(other, att.ws, o, lse)
-    att.forward()
-    got = att.backward(inp["dout"])
+    # the same configuration with other bytes in the struct's padding (before eps) is the
+    # same configuration
+    pad0 = P.PrismConfig.tau256.offset + 4
+    assert P.PrismConfig.eps.offset - pad0 == 4
+    raw = bytearray(ctypes.string_at(ctypes.addressof(att.cfg), ctypes.sizeof(att.cfg)))
+    raw[pad0:pad0 + 4] = b"\xab\xcd\xef\x01"
+    padded = P.PrismConfig.from_buffer_copy(bytes(raw))
+    P.attn_fwd(padded, att.ws, o, lse)
+    P.attn_bwd(att.cfg, att.ws, inp["dout"], dq, dk, dv)
     torch.cuda.synchronize()
-    for a, b in zip(got, ref):
+    for a, b in zip((dq, dk, dv), ref):
         assert torch.equal(a, b)
 
 
