@@ -22,15 +22,23 @@ def _head_inputs(inp, h):
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("cid,policy", [(1, None), (2, None), (4, None), (4, "pages")],
-                         ids=["720p", "1080p", "2k", "2k-pages-operating-point"])
-def test_fullsize(cid, policy):
+@pytest.mark.parametrize("cid,policy,fixed", [(1, None, None), (2, None, None), (4, None, None),
+                                              (4, "pages", None), (4, "pages", (4, 4, 4))],
+                         ids=["720p", "1080p", "2k", "2k-pages-operating-point",
+                              "2k-pages-all-64-token-blocks"])
+def test_fullsize(cid, policy, fixed):
+    """With every block of 64 tokens (13,312 blocks per head) the forward and dQ walk query
+    tiles of four blocks and dK/dV runs only its 64-key launch; there the oracle's plan is
+    recomputed for the first and last head only (about half a minute each)."""
     wl = synth.workload(cid)
-    print(f"\n== {wl.name} {policy or ''}: generating inputs", flush=True)
+    print(f"\n== {wl.name} {policy or ''} {fixed or ''}: generating inputs", flush=True)
     inp = synth.make_inputs(wl, device="cuda", with_dout=False)
     over = dict(P.POLICIES[policy]) if policy else {}
+    if fixed:
+        over["fixed_shape"] = P.shape_code(*fixed)
     cfg = P.config_for(wl, **over)
-    sel = dict(top_k=cfg.top_k, top_p=cfg.top_p, top_k_frac=cfg.top_k_frac)
+    sel = dict(top_k=cfg.top_k, top_p=cfg.top_p, top_k_frac=cfg.top_k_frac,
+               fixed_shape=cfg.fixed_shape)
     att = P.PrismAttention(cfg)
     att.plan(inp["q"], inp["k"], inp["v"], inp["a2v"])
     o, lse = att.forward()
@@ -43,7 +51,7 @@ def test_fullsize(cid, policy):
     heads = [0, wl.heads - 1]
     samples = {}
     views = att.views()
-    for h in range(wl.heads):
+    for h in (heads if fixed else range(wl.heads)):
         hi = _head_inputs(inp, h)
         op = oracle.plan_head(wl.T, wl.H, wl.W, hi["q"], hi["k"], hi["v"], a2v,
                               min_edge_log2=wl.min_edge_log2, **sel)
