@@ -338,8 +338,8 @@ def cpu_baseline(wl, cfg, inp, budget_s, views=None, outputs=None):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; the head-sharded multi-GPU "
-                          "layout is a design note only", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the benchmark runs on one GPU; the head-sharded "
+                          "multi-GPU layout is a design note only", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
     import dynamic_block_sparse_stats_amd as P
